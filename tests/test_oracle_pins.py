@@ -1,0 +1,327 @@
+"""Pins of the float64 oracle against facts that do not come from the oracle itself:
+hand-derived rationals, torch's scaled_dot_product_attention, closed forms,
+invariants and a pure-Python brute force."""
+from __future__ import annotations
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+from hypothesis import given, settings, strategies as st
+
+from oracle import SCORE_ATTN, SCORE_VL1, OracleCache
+from tests.brute import BruteCache
+from workloads import get_workload, initial_cache, step_inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _frac(s: str) -> float:
+    if s.startswith("ln "):
+        return math.log(float(Fraction(s[3:])))
+    return float(Fraction(s))
+
+
+# ---------------------------------------------------------------- golden fixture
+
+def _hand_cache(fx, score):
+    c = fx["cache"]
+    keys = np.array([[math.log(a), math.log(b)] for a, b in zip(c["a"], c["b"])])
+    vals = np.array(c["v"], dtype=np.float64)
+    return OracleCache([keys[None]], [vals[None]], [c["positions"]], [c["t"]], fx["budget"],
+                       fx["n_q_heads"], fx["sink"], fx["recent"], scale=fx["scale"], score=score)
+
+
+@pytest.mark.parametrize("score", [SCORE_ATTN, SCORE_VL1])
+def test_hand_worked_example(score):
+    with open(os.path.join(GOLDEN, "hand_worked_step.json")) as f:
+        fx = json.load(f)
+    oc = _hand_cache(fx, score)
+    q = np.array(fx["q"], dtype=np.float64)[None]
+    for i, st_ in enumerate(fx["steps"]):
+        if score == SCORE_VL1 and "vl1_scores" not in st_:
+            break
+        kn = np.array([[[math.log(st_["new_a"]), math.log(st_["new_b"])]]])
+        vn = np.array([[st_["v_new"]]], dtype=np.float64)
+        dec = oc.decide(q, kn, vn)
+        want_out = np.array([[_frac(x) for x in row] for row in st_["out"]])
+        np.testing.assert_allclose(dec.out[0], want_out, rtol=0, atol=1e-14)
+        want_alpha_new = [_frac(row[-1]) for row in st_["alpha"]]
+        np.testing.assert_allclose(dec.alpha_new[0], want_alpha_new, rtol=0, atol=1e-15)
+        np.testing.assert_allclose(dec.lse[0], [_frac(x) for x in st_["lse"]], rtol=0, atol=1e-14)
+        key = "attn" if score == SCORE_ATTN else "vl1"
+        np.testing.assert_allclose(dec.scores[0][0], [_frac(x) for x in st_[key + "_scores"]], rtol=0, atol=1e-14)
+        assert dec.eligible[0][0].tolist() == st_["eligible"]
+        assert int(dec.evict[0, 0]) == st_[key + "_evict"]
+        oc.commit(dec.slot, kn, vn)
+        if "positions_after" in st_:
+            assert oc.pos[0][0].tolist() == st_["positions_after"]
+
+
+# ---------------------------------------------------------------- textbook attention
+
+def _sdpa_reference(keys, vals, q, scale):
+    """torch float64 SDPA with GQA: keys/vals [Hkv][n][d], q [Hq][d] -> [Hq][d]."""
+    kq = torch.from_numpy(np.asarray(keys, dtype=np.float64))[None]
+    vq = torch.from_numpy(np.asarray(vals, dtype=np.float64))[None]
+    qq = torch.from_numpy(np.asarray(q, dtype=np.float64))[None, :, None, :]
+    o = torch.nn.functional.scaled_dot_product_attention(qq, kq, vq, scale=scale, enable_gqa=True)
+    return o[0, :, 0, :].numpy()
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(4, 4, 8), (8, 2, 16), (6, 3, 8), (7, 1, 4)])
+def test_attention_matches_torch_sdpa_without_eviction(hq, hkv, d):
+    rng = np.random.default_rng(10 + hq + d)
+    n0, steps, budget = 5, 12, 64
+    k0 = rng.standard_normal((hkv, n0, d)).astype(np.float32)
+    v0 = rng.standard_normal((hkv, n0, d)).astype(np.float32)
+    oc = OracleCache([k0], [v0], [np.arange(n0)], [n0], budget, hq, sink=2, recent=3)
+    allk, allv = [k0.astype(np.float64)], [v0.astype(np.float64)]
+    for _ in range(steps):
+        q = rng.standard_normal((1, hq, d)).astype(np.float32)
+        kn = rng.standard_normal((1, hkv, d)).astype(np.float32)
+        vn = rng.standard_normal((1, hkv, d)).astype(np.float32)
+        allk.append(kn[0][:, None].astype(np.float64))
+        allv.append(vn[0][:, None].astype(np.float64))
+        dec = oc.step(q, kn, vn)
+        K = np.concatenate(allk, axis=1)
+        V = np.concatenate(allv, axis=1)
+        ref = _sdpa_reference(K, V, q[0], 1.0 / math.sqrt(d))
+        np.testing.assert_allclose(dec.out[0], ref, rtol=0, atol=1e-12)
+        assert (dec.evict == -1).all()
+        # lse against torch.logsumexp of the per-head logits
+        kk = torch.from_numpy(K).repeat_interleave(hq // hkv, dim=0)
+        s = torch.einsum("hnd,hd->hn", kk, torch.from_numpy(q[0].astype(np.float64))) / math.sqrt(d)
+        np.testing.assert_allclose(dec.lse[0], torch.logsumexp(s, dim=1).numpy(), rtol=0, atol=1e-12)
+
+
+def test_sdpa_pin_rejects_interleaved_grouping():
+    """The GQA pin distinguishes h -> h // G from h -> h % Hkv: feeding the oracle
+    queries permuted the interleaved way changes the outputs beyond tolerance."""
+    hq, hkv, d = 8, 2, 8
+    rng = np.random.default_rng(5)
+    k0 = rng.standard_normal((hkv, 6, d)).astype(np.float32)
+    v0 = rng.standard_normal((hkv, 6, d)).astype(np.float32)
+    q = rng.standard_normal((1, hq, d)).astype(np.float32)
+    kn = rng.standard_normal((1, hkv, d)).astype(np.float32)
+    vn = rng.standard_normal((1, hkv, d)).astype(np.float32)
+    perm = np.array([(h % hkv) * (hq // hkv) + h // hkv for h in range(hq)])
+    oc = OracleCache([k0], [v0], [np.arange(6)], [6], 64, hq, 1, 1)
+    wrong = oc.decide(q[:, perm], kn, vn).out[0][np.argsort(perm)]
+    K = np.concatenate([k0, kn[0][:, None]], axis=1)
+    V = np.concatenate([v0, vn[0][:, None]], axis=1)
+    ref = _sdpa_reference(K, V, q[0], 1.0 / math.sqrt(d))
+    assert np.abs(wrong - ref).max() > 1e-3
+
+
+# ---------------------------------------------------------------- closed forms
+
+@pytest.mark.parametrize("score", [SCORE_ATTN, SCORE_VL1])
+def test_uniform_keys_closed_form(score):
+    """Identical keys: every weight is 1/(n+1), the output is the mean of the
+    values, ATTN scores are G/(n+1), and the tie goes to the lowest eligible slot."""
+    hq, hkv, d, n, sink, recent = 6, 2, 8, 10, 2, 3
+    rng = np.random.default_rng(1)
+    key = rng.standard_normal(d).astype(np.float32)
+    k0 = np.broadcast_to(key, (hkv, n, d)).copy()
+    v0 = np.sign(rng.standard_normal((hkv, n, d))).astype(np.float32)  # |v|_1 = d for every slot
+    oc = OracleCache([k0], [v0], [np.arange(n)], [n], n, hq, sink, recent, score=score)
+    q = rng.standard_normal((1, hq, d)).astype(np.float32)
+    kn = key[None, None].repeat(hkv, 1)
+    vn = np.ones((1, hkv, d), np.float32)
+    dec = oc.decide(q, kn, vn)
+    G = hq // hkv
+    for g in range(hkv):
+        want = np.concatenate([v0[g], vn[0, g][None]]).astype(np.float64).mean(axis=0)
+        for j in range(G):
+            np.testing.assert_allclose(dec.out[0, g * G + j], want, rtol=0, atol=1e-14)
+        mult = d if score == SCORE_VL1 else 1
+        np.testing.assert_allclose(dec.scores[0][g], np.full(n, G * mult / (n + 1)), rtol=1e-14)
+        assert dec.evict[0, g] == sink  # all eligible scores tie: lowest eligible slot
+    np.testing.assert_allclose(dec.alpha_new[0], 1.0 / (n + 1), rtol=1e-14)
+
+
+def test_weights_of_each_head_sum_to_one():
+    w = get_workload("tiny_f32")
+    ks, vs, ps, ts = initial_cache(w)
+    oc = OracleCache(ks, vs, ps, ts, w.budget_lo, w.n_q_heads, w.sink, w.recent)
+    for s in range(3):
+        q, kn, vn = step_inputs(w, s)
+        dec = oc.step(q, kn, vn)
+        G = w.group
+        for g in range(w.n_kv_heads):
+            total = dec.scores[0][g].sum() + dec.alpha_new[0, g * G:(g + 1) * G].sum()
+            assert abs(total - G) < 1e-12
+
+
+def test_g1_integer_logits_argmin_is_logit_argmin():
+    """G = 1, integer-valued q and keys, scale 1: the softmax is monotone in the
+    logit, so the evicted slot is the first eligible slot of smallest logit
+    (computed here on the exact integer logits)."""
+    rng = np.random.default_rng(7)
+    d, n, sink, recent = 4, 24, 2, 4
+    for trial in range(20):
+        k0 = rng.integers(-3, 4, size=(1, n, d)).astype(np.float32)
+        q = rng.integers(-2, 3, size=(1, 1, d)).astype(np.float32)
+        kn = rng.integers(-3, 4, size=(1, 1, d)).astype(np.float32)
+        vn = np.zeros((1, 1, d), np.float32)
+        oc = OracleCache([k0], [np.zeros_like(k0)], [np.arange(n)], [n], n, 1, sink, recent, scale=1.0)
+        dec = oc.decide(q, kn, vn)
+        logits = (k0[0].astype(np.int64) @ q[0, 0].astype(np.int64))
+        cand = np.arange(sink, n - recent)
+        want = cand[np.argmin(logits[cand])]
+        assert dec.evict[0, 0] == want, trial
+
+
+def test_streaming_closed_form_when_logits_rise_with_position():
+    """Constant query and keys whose logit grows with position: the oldest
+    eligible token always has the smallest weight, so after every step the cache
+    holds the sink positions plus the newest budget - sink positions."""
+    d, hq, hkv, budget, sink, recent = 4, 4, 2, 16, 2, 3
+    q = np.zeros((1, hq, d), np.float32)
+    q[..., 0] = 1.0
+
+    def key(p):
+        k = np.zeros(d, np.float32)
+        k[0] = 0.25 * p
+        return k
+
+    k0 = np.stack([key(p) for p in range(budget)])[None].repeat(hkv, 0)
+    v0 = np.ones((hkv, budget, d), np.float32)
+    oc = OracleCache([k0], [v0], [np.arange(budget)], [budget], budget, hq, sink, recent, scale=1.0)
+    prev_slot = None
+    for t in range(budget, budget + 40):
+        kn = key(t)[None, None].repeat(hkv, 1)
+        dec = oc.step(q, kn, np.ones((1, hkv, d), np.float32))
+        want = set(range(sink)) | set(range(t + 1 - (budget - sink), t + 1))
+        for g in range(hkv):
+            assert set(oc.pos[0][g].tolist()) == want
+        # victims cycle through the middle slots in order
+        e = int(dec.evict[0, 0])
+        if prev_slot is not None:
+            assert e == (sink + (prev_slot - sink + 1) % (budget - sink))
+        prev_slot = e
+
+
+def test_vl1_equals_l1_norm_of_removed_contribution():
+    """VL1 importance of slot i equals sum over the group's heads of
+    |o_h - o_h without token i|_1 at fixed weights (no renormalisation)."""
+    rng = np.random.default_rng(3)
+    hq, hkv, d, n = 6, 2, 5, 9
+    k0 = rng.standard_normal((hkv, n, d)).astype(np.float32)
+    v0 = rng.standard_normal((hkv, n, d)).astype(np.float32)
+    q = rng.standard_normal((1, hq, d)).astype(np.float32)
+    kn = rng.standard_normal((1, hkv, d)).astype(np.float32)
+    vn = rng.standard_normal((1, hkv, d)).astype(np.float32)
+    oc = OracleCache([k0], [v0], [np.arange(n)], [n], n, hq, 1, 1, score=SCORE_VL1)
+    dec = oc.decide(q, kn, vn)
+    G = hq // hkv
+    scale = 1.0 / math.sqrt(d)
+    for g in range(hkv):
+        keys = [list(map(float, r)) for r in k0[g]] + [list(map(float, kn[0, g]))]
+        vals = [list(map(float, r)) for r in v0[g]] + [list(map(float, vn[0, g]))]
+        for i in range(n):
+            total = 0.0
+            for j in range(G):
+                qh = list(map(float, q[0, g * G + j]))
+                lg = [scale * sum(a * b for a, b in zip(qh, kk)) for kk in keys]
+                m = max(lg)
+                w = [math.exp(x - m) for x in lg]
+                z = sum(w)
+                w = [x / z for x in w]
+                full = [sum(w[r] * vals[r][c] for r in range(n + 1)) for c in range(d)]
+                minus = [sum(w[r] * vals[r][c] for r in range(n + 1) if r != i) for c in range(d)]
+                total += sum(abs(a - b) for a, b in zip(full, minus))
+            assert abs(dec.scores[0][g][i] - total) < 1e-12
+
+
+# ---------------------------------------------------------------- brute force
+
+@settings(max_examples=40, deadline=None)
+@given(
+    hkv=st.integers(1, 2),
+    G=st.sampled_from([1, 2, 3, 4, 7]),
+    d=st.sampled_from([2, 4, 8]),
+    budget=st.integers(6, 14),
+    sink=st.integers(0, 2),
+    recent=st.integers(0, 3),
+    prefill=st.integers(1, 14),
+    vl1=st.booleans(),
+    seed=st.integers(0, 10_000),
+)
+def test_oracle_matches_brute_force(hkv, G, d, budget, sink, recent, prefill, vl1, seed):
+    if budget <= sink + recent:
+        budget = sink + recent + 1
+    prefill = min(prefill, budget)
+    rng = np.random.default_rng(seed)
+    B, hq = 2, hkv * G
+    ks = [rng.standard_normal((hkv, prefill, d)).astype(np.float32) for _ in range(B)]
+    vs = [rng.standard_normal((hkv, prefill, d)).astype(np.float32) for _ in range(B)]
+    pos = [np.arange(prefill)] * B
+    ts = [prefill] * B
+    scale = 1.0 / math.sqrt(d)
+    oc = OracleCache(ks, vs, pos, ts, budget, hq, sink, recent, score=SCORE_VL1 if vl1 else SCORE_ATTN)
+    br = BruteCache(ks, vs, pos, ts, [budget] * B, hq, sink, recent, scale, vl1=vl1)
+    for _ in range(2 * budget):
+        q = rng.standard_normal((B, hq, d)).astype(np.float32)
+        kn = rng.standard_normal((B, hkv, d)).astype(np.float32)
+        vn = rng.standard_normal((B, hkv, d)).astype(np.float32)
+        dec = oc.decide(q, kn, vn)
+        out_b, slot_b, ev_b = br.step(q, kn, vn)
+        np.testing.assert_allclose(dec.out, np.array(out_b), rtol=0, atol=1e-12)
+        exact = dec.gap > 1e-12
+        assert (np.array(ev_b)[exact] == dec.evict[exact]).all()
+        oc.commit(np.array(slot_b), kn, vn)  # follow the brute force inside near-ties
+        for b in range(B):
+            for g in range(hkv):
+                assert oc.pos[b][g, : oc.n[b]].tolist() == br.positions(b, g)
+
+
+# ---------------------------------------------------------------- invariants over many steps
+
+def test_occupancy_and_protection_over_the_tiny_workload():
+    w = get_workload("tiny_f32")
+    ks, vs, ps, ts = initial_cache(w)
+    oc = OracleCache(ks, vs, ps, ts, w.budget_lo, w.n_q_heads, w.sink, w.recent)
+    sink_k = oc.k[0][:, : w.sink].copy()
+    for s in range(64):
+        q, kn, vn = step_inputs(w, s)
+        t = oc.t[0]
+        dec = oc.step(q, kn, vn)
+        assert oc.n[0] == w.budget_lo
+        for g in range(w.n_kv_heads):
+            p = oc.pos[0][g]
+            assert (p >= 0).all() and len(set(p.tolist())) == w.budget_lo
+            e = int(dec.evict[0, g])
+            assert w.sink <= e and p[e] == t
+            assert set(range(t + 1 - w.recent, t + 1)) <= set(p.tolist())  # recent window kept
+            assert np.array_equal(oc.k[0][g, e], kn[0, g])
+        assert np.array_equal(oc.k[0][:, : w.sink], sink_k)
+
+
+def test_append_path_until_full():
+    rng = np.random.default_rng(11)
+    hkv, hq, d, budget = 2, 4, 4, 8
+    k0 = rng.standard_normal((hkv, 3, d)).astype(np.float32)
+    oc = OracleCache([k0], [k0.copy()], [np.arange(3)], [3], budget, hq, 1, 2)
+    evs = []
+    for _ in range(8):
+        q = rng.standard_normal((1, hq, d)).astype(np.float32)
+        kn = rng.standard_normal((1, hkv, d)).astype(np.float32)
+        dec = oc.step(q, kn, kn)
+        evs.append(int(dec.evict[0, 0]))
+    assert evs[:5] == [-1] * 5 and all(e >= 1 for e in evs[5:])
+    assert oc.n[0] == budget
+
+
+def test_rejects_budget_not_above_windows_and_protected_commit():
+    k = np.zeros((1, 4, 2), np.float32)
+    with pytest.raises(ValueError):
+        OracleCache([k], [k], [np.arange(4)], [4], 4, 1, sink=2, recent=2)
+    oc = OracleCache([k], [k], [np.arange(4)], [4], 4, 1, sink=1, recent=1)
+    with pytest.raises(ValueError):
+        oc.commit(np.array([[0]]), np.zeros((1, 1, 2)), np.zeros((1, 1, 2)))
