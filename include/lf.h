@@ -1,0 +1,159 @@
+/*
+ * lf.h - C ABI of the LongFlow-style fused decode step for AMD MI355X (gfx950).
+ *
+ * One call of lf_decode_step runs, for every sequence b and KV head g of a
+ * static fixed-budget KV cache, in one kernel launch:
+ *   (a) GQA decode attention of the query heads of group g over the cached
+ *       slots plus the incoming token,
+ *   (b) the history-free importance of every cached slot: the softmax weight
+ *       that this step's attention gives it, summed over the group's query
+ *       heads (LF_SCORE_ATTN), or that sum times the L1 norm of the slot's
+ *       value vector (LF_SCORE_VL1, the LongFlowScore equation of the LongFlow
+ *       summary on gist.science, section 2.B),
+ *   (c) the argmin over the slots outside the sink and recent windows,
+ *   (d) the in-place overwrite of that slot with the incoming K/V,
+ * so the cache never holds more than its budget.  The fusion of attention,
+ * importance and eviction into a single operator over a statically
+ * pre-allocated cache is the design of the LongFlow summary, section 2.C, and
+ * of the LongFlow blog post (denisavetisyan.com), section on fused kernels.
+ *
+ * Conventions shared by every entry point:
+ *  - Device buffers are caller-owned and passed as plain device pointers
+ *    (for example torch tensors' data_ptr()).  The library allocates only the
+ *    small host-side lf_cache handle; it never allocates device memory.
+ *  - `stream` is a hipStream_t passed as void*; NULL is the default stream.
+ *  - Errors are returned as lf_status, never thrown across the ABI; the text of
+ *    the last error of the calling thread is available from lf_last_error().
+ *  - Layouts are dense row-major.  Element type is lf_config.dtype everywhere
+ *    (q, k_new, v_new, out, k_cache, v_cache).
+ *  - Query head h belongs to KV head h / G with G = n_q_heads / n_kv_heads
+ *    (contiguous groups).
+ */
+#ifndef LF_H_
+#define LF_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LF_ABI_VERSION 1
+
+typedef enum lf_status {
+  LF_OK = 0,
+  LF_ERR_ARG = 1,         /* invalid argument (null pointer, shape, window, size) */
+  LF_ERR_UNSUPPORTED = 2, /* well-formed but not built: head_dim, group size, dtype */
+  LF_ERR_STATE = 3,       /* handle is not a live lf_cache */
+  LF_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} lf_status;
+
+typedef enum lf_dtype { LF_F32 = 0, LF_BF16 = 1 } lf_dtype;
+
+typedef enum lf_score {
+  LF_SCORE_ATTN = 0, /* I_i = sum over the group's query heads of alpha_{h,i} */
+  LF_SCORE_VL1 = 1   /* I_i = (sum_h alpha_{h,i}) * sum_l |v_i[l]|            */
+} lf_score;
+
+typedef struct lf_config {
+  int32_t batch;         /* B >= 1                                                */
+  int32_t n_q_heads;     /* Hq, a multiple of n_kv_heads                          */
+  int32_t n_kv_heads;    /* Hkv >= 1; G = Hq / Hkv must be in [1, 8]              */
+  int32_t head_dim;      /* d: 64 or 128                                          */
+  int32_t max_budget;    /* slot stride of k_cache/v_cache; every budget <= this, */
+                         /* at most 65536                                         */
+  int32_t sink;          /* slots [0, sink) hold positions 0..sink-1, never evicted */
+  int32_t recent;        /* the `recent` newest cached tokens are never evicted   */
+  int32_t dtype;         /* lf_dtype                                              */
+  int32_t score;         /* lf_score                                              */
+  float softmax_scale;   /* logit scale; <= 0 selects 1/sqrt(head_dim)            */
+  int32_t chunk_slots;   /* split-KV chunk length in slots; 0 = automatic         */
+  int32_t reserved;      /* must be 0                                             */
+} lf_config;
+
+typedef struct lf_cache lf_cache; /* opaque host handle */
+
+/* lf_init_cache flag: keep the device state as it is (resume from a saved copy
+ * of k_cache, v_cache and state); only the host handle is rebuilt. */
+#define LF_INIT_ATTACH 1
+
+/*
+ * lf_state_bytes - size of the device `state` buffer lf_init_cache needs.
+ *   cfg      host, validated as in lf_init_cache.
+ *   budgets  host int32[B], per-sequence budget (1 <= budget <= max_budget and
+ *            budget > sink + recent), or NULL for max_budget everywhere.
+ *   bytes    host, receives the size.
+ * Pure host computation; no HIP call.  Errors: LF_ERR_ARG, LF_ERR_UNSUPPORTED.
+ */
+lf_status lf_state_bytes(const lf_config* cfg, const int32_t* budgets, size_t* bytes);
+
+/*
+ * lf_init_cache - bind a filled static cache and build the device state.
+ *   budgets  host int32[B] or NULL (= max_budget).
+ *   seq_len  host int64[B]: tokens seen so far per sequence (0 <= seq_len < 2^31).
+ *            Contract on the cache contents: slots [0, min(seq_len, budget))
+ *            hold the cached tokens in increasing position order, slots
+ *            [0, sink) hold positions 0..sink-1, and when seq_len >= budget the
+ *            last `recent` slots hold positions seq_len-recent .. seq_len-1.
+ *   k_cache, v_cache  device [B][Hkv][max_budget][d]; must stay valid until
+ *            lf_free.  Only the slots of the first step's eviction are ever
+ *            written.
+ *   state, state_bytes  device buffer of at least lf_state_bytes() bytes,
+ *            caller-owned, 256-byte aligned, kept for the cache's lifetime.
+ *            Holds the per-(sequence, KV head) step counter, fill level, ring
+ *            of recent slots, the split-KV work list and the partial results.
+ *   flags    0, or LF_INIT_ATTACH to reuse a state written by an earlier
+ *            lf_init_cache + lf_decode_step sequence with the same cfg/budgets.
+ *   stream   the state upload is ordered on this stream; the call waits for it.
+ *   out      host, receives the handle.
+ * Errors: LF_ERR_ARG (any bad size, window, budget, pointer or alignment),
+ * LF_ERR_UNSUPPORTED (head_dim, G, dtype), LF_ERR_HIP.
+ */
+lf_status lf_init_cache(const lf_config* cfg, const int32_t* budgets, const int64_t* seq_len,
+                        void* k_cache, void* v_cache, void* state, size_t state_bytes,
+                        int32_t flags, void* stream, lf_cache** out);
+
+/*
+ * lf_decode_step - one fused decode step (attention + importance + argmin +
+ * in-place overwrite) for the whole batch, one kernel launch on `stream`.
+ *   q          device [B][Hq][d]
+ *   k_new      device [B][Hkv][d]   incoming token's keys
+ *   v_new      device [B][Hkv][d]   incoming token's values
+ *   out        device [B][Hq][d]    attention output over cache + new token,
+ *              rounded to nearest-even when dtype is bf16
+ *   evict_idx  device int32 [B][Hkv]: slot overwritten by the new token, or -1
+ *              when the cache was not yet full and the token was appended.
+ * Asynchronous and stream-ordered; no host synchronisation, no allocation.
+ * Calls on one handle must be ordered on one stream.  Validation is limited to
+ * null pointers and the handle; errors: LF_ERR_ARG, LF_ERR_STATE, LF_ERR_HIP.
+ */
+lf_status lf_decode_step(const void* q, const void* k_new, const void* v_new, lf_cache* cache,
+                         void* out, int32_t* evict_idx, void* stream);
+
+/*
+ * lf_decode_step_dbg - lf_decode_step that also exports its intermediates.
+ *   scores  device float [B][Hkv][max_budget] or NULL: importance of every
+ *           cached slot i < fill level, before the window mask (other entries
+ *           are left untouched).
+ *   lse     device float [B][Hq] or NULL: natural-log softmax normaliser
+ *           log(sum_i exp(scale q.k_i)) over cache + new token.
+ * Same semantics and errors as lf_decode_step otherwise.
+ */
+lf_status lf_decode_step_dbg(const void* q, const void* k_new, const void* v_new, lf_cache* cache,
+                             void* out, int32_t* evict_idx, float* scores, float* lse, void* stream);
+
+/* lf_free - release the host handle (NULL-safe).  Device buffers stay the caller's. */
+void lf_free(lf_cache* cache);
+
+/* lf_last_error - message of the last failed call on this thread ("" if none). */
+const char* lf_last_error(void);
+
+/* lf_abi_version - LF_ABI_VERSION of the built library. */
+int32_t lf_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LF_H_ */

@@ -1,0 +1,54 @@
+"""LongFlow-style fused decode step (attention + history-free importance +
+argmin eviction + in-place overwrite) for AMD MI355X, behind a C ABI.
+
+``_lib`` is the ctypes binding of include/lf.h with the same function names;
+``LongFlowCache`` wraps it for torch device tensors."""
+from ._lib import (
+    LF_BF16,
+    LF_F32,
+    LF_INIT_ATTACH,
+    LF_SCORE_ATTN,
+    LF_SCORE_VL1,
+    LFError,
+    lf_abi_version,
+    lf_decode_step,
+    lf_decode_step_dbg,
+    lf_free,
+    lf_init_cache,
+    lf_last_error,
+    lf_probe_copy,
+    lf_probe_read,
+    lf_state_bytes,
+    load_library,
+    make_config,
+)
+
+
+def __getattr__(name):
+    if name == "LongFlowCache":
+        from .cache import LongFlowCache
+
+        return LongFlowCache
+    raise AttributeError(name)
+
+
+__all__ = [
+    "LF_BF16",
+    "LF_F32",
+    "LF_INIT_ATTACH",
+    "LF_SCORE_ATTN",
+    "LF_SCORE_VL1",
+    "LFError",
+    "LongFlowCache",
+    "lf_abi_version",
+    "lf_decode_step",
+    "lf_decode_step_dbg",
+    "lf_free",
+    "lf_init_cache",
+    "lf_last_error",
+    "lf_probe_copy",
+    "lf_probe_read",
+    "lf_state_bytes",
+    "load_library",
+    "make_config",
+]

@@ -1,0 +1,162 @@
+"""ctypes binding of include/lf.h and include/lf_probe.h.
+
+Argument marshalling only: every function forwards to the C ABI of liblf.so
+with the same name and turns a non-zero lf_status into LFError.  Pointers are
+plain integers (device addresses, e.g. torch's ``data_ptr()``) and streams are
+``hipStream_t`` handles as integers (0 = default stream)."""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_float, c_int32, c_int64, c_size_t, c_uint32, c_void_p
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblf.so")
+
+LF_OK, LF_ERR_ARG, LF_ERR_UNSUPPORTED, LF_ERR_STATE, LF_ERR_HIP = range(5)
+LF_F32, LF_BF16 = 0, 1
+LF_SCORE_ATTN, LF_SCORE_VL1 = 0, 1
+LF_INIT_ATTACH = 1
+STATUS_NAMES = {0: "LF_OK", 1: "LF_ERR_ARG", 2: "LF_ERR_UNSUPPORTED", 3: "LF_ERR_STATE", 4: "LF_ERR_HIP"}
+
+
+class LFError(RuntimeError):
+    def __init__(self, status: int, func: str, message: str):
+        super().__init__(f"{func}: {STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class lf_config(ctypes.Structure):
+    _fields_ = [
+        ("batch", c_int32),
+        ("n_q_heads", c_int32),
+        ("n_kv_heads", c_int32),
+        ("head_dim", c_int32),
+        ("max_budget", c_int32),
+        ("sink", c_int32),
+        ("recent", c_int32),
+        ("dtype", c_int32),
+        ("score", c_int32),
+        ("softmax_scale", c_float),
+        ("chunk_slots", c_int32),
+        ("reserved", c_int32),
+    ]
+
+
+# Exported symbols and their prototypes (restype, argtypes).
+PROTOTYPES = {
+    "lf_abi_version": (c_int32, []),
+    "lf_last_error": (ctypes.c_char_p, []),
+    "lf_state_bytes": (c_int32, [POINTER(lf_config), POINTER(c_int32), POINTER(c_size_t)]),
+    "lf_init_cache": (
+        c_int32,
+        [POINTER(lf_config), POINTER(c_int32), POINTER(c_int64), c_void_p, c_void_p, c_void_p, c_size_t, c_int32,
+         c_void_p, POINTER(c_void_p)],
+    ),
+    "lf_decode_step": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "lf_decode_step_dbg": (
+        c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "lf_free": (None, [c_void_p]),
+    "lf_probe_copy": (c_int32, [c_void_p, c_void_p, c_size_t, c_void_p]),
+    "lf_probe_read": (c_int32, [c_void_p, c_size_t, c_void_p, c_void_p]),
+    "lf_probe_read_sink_words": (c_int32, []),
+}
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load liblf.so once.  torch is imported first so that the library binds to
+    the HIP runtime torch already loaded (same SONAME) and shares its streams."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"HIP library {path} is missing; build it with `python -m kv_cache_eviction_lf_amd.build`")
+    try:
+        import torch  # noqa: F401  (HIP runtime of the process)
+    except ImportError:
+        pass
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in PROTOTYPES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int, func: str) -> None:
+    if status != LF_OK:
+        msg = load_library().lf_last_error()
+        raise LFError(status, func, msg.decode() if msg else "")
+
+
+def _i32_array(values):
+    if values is None:
+        return None
+    vals = [int(x) for x in values]
+    return (c_int32 * len(vals))(*vals)
+
+
+def make_config(batch, n_q_heads, n_kv_heads, head_dim, max_budget, sink, recent, dtype=LF_BF16,
+                score=LF_SCORE_ATTN, softmax_scale=0.0, chunk_slots=0) -> lf_config:
+    return lf_config(batch, n_q_heads, n_kv_heads, head_dim, max_budget, sink, recent, dtype, score,
+                     softmax_scale, chunk_slots, 0)
+
+
+def lf_abi_version() -> int:
+    return int(load_library().lf_abi_version())
+
+
+def lf_last_error() -> str:
+    msg = load_library().lf_last_error()
+    return msg.decode() if msg else ""
+
+
+def lf_state_bytes(cfg: lf_config, budgets=None) -> int:
+    out = c_size_t(0)
+    _check(load_library().lf_state_bytes(ctypes.byref(cfg), _i32_array(budgets), ctypes.byref(out)),
+           "lf_state_bytes")
+    return int(out.value)
+
+
+def lf_init_cache(cfg: lf_config, budgets, seq_len, k_cache: int, v_cache: int, state: int, state_bytes: int,
+                  flags: int = 0, stream: int = 0) -> int:
+    sl = [int(x) for x in seq_len]
+    sl_arr = (c_int64 * len(sl))(*sl)
+    handle = c_void_p(0)
+    _check(load_library().lf_init_cache(ctypes.byref(cfg), _i32_array(budgets), sl_arr, c_void_p(k_cache),
+                                        c_void_p(v_cache), c_void_p(state), c_size_t(state_bytes), c_int32(flags),
+                                        c_void_p(stream), ctypes.byref(handle)), "lf_init_cache")
+    return int(handle.value)
+
+
+def lf_decode_step(q: int, k_new: int, v_new: int, cache: int, out: int, evict_idx: int, stream: int = 0) -> None:
+    _check(load_library().lf_decode_step(c_void_p(q), c_void_p(k_new), c_void_p(v_new), c_void_p(cache),
+                                         c_void_p(out), c_void_p(evict_idx), c_void_p(stream)), "lf_decode_step")
+
+
+def lf_decode_step_dbg(q: int, k_new: int, v_new: int, cache: int, out: int, evict_idx: int, scores: int = 0,
+                       lse: int = 0, stream: int = 0) -> None:
+    _check(load_library().lf_decode_step_dbg(c_void_p(q), c_void_p(k_new), c_void_p(v_new), c_void_p(cache),
+                                             c_void_p(out), c_void_p(evict_idx), c_void_p(scores or None),
+                                             c_void_p(lse or None), c_void_p(stream)), "lf_decode_step_dbg")
+
+
+def lf_free(cache: int) -> None:
+    load_library().lf_free(c_void_p(cache))
+
+
+def lf_probe_copy(src: int, dst: int, nbytes: int, stream: int = 0) -> None:
+    _check(load_library().lf_probe_copy(c_void_p(src), c_void_p(dst), c_size_t(nbytes), c_void_p(stream)),
+           "lf_probe_copy")
+
+
+def lf_probe_read(src: int, nbytes: int, sink: int, stream: int = 0) -> None:
+    _check(load_library().lf_probe_read(c_void_p(src), c_size_t(nbytes), c_void_p(sink), c_void_p(stream)),
+           "lf_probe_read")
+
+
+def lf_probe_read_sink_words() -> int:
+    return int(load_library().lf_probe_read_sink_words())

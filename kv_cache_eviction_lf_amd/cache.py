@@ -1,0 +1,107 @@
+"""torch-facing wrapper of the C ABI: device tensors in, device tensors out.
+
+torch provides device memory and the current stream; every step of the decode
+path runs in the HIP library (liblf.so), which must be built: there is no
+fallback."""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+from ._lib import LF_BF16, LF_F32, LF_INIT_ATTACH, LF_SCORE_ATTN, LF_SCORE_VL1
+
+_DTYPES = {torch.bfloat16: LF_BF16, torch.float32: LF_F32}
+_SCORES = {"attn": LF_SCORE_ATTN, "vl1": LF_SCORE_VL1}
+
+
+def _stream_handle(device) -> int:
+    return int(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, shape, dtype, device) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype or t.device != device or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor on {device}")
+
+
+class LongFlowCache:
+    """One layer's static KV cache with per-step LongFlow eviction.
+
+    k_cache, v_cache: contiguous device tensors [B][Hkv][max_budget][d] (bf16 or
+    fp32), filled as the C ABI's lf_init_cache describes; budgets: per-sequence
+    budgets (None = max_budget); seq_len: tokens already seen per sequence."""
+
+    def __init__(self, k_cache: torch.Tensor, v_cache: torch.Tensor, n_q_heads: int, sink: int, recent: int,
+                 seq_len, budgets=None, score: str = "attn", softmax_scale: float = 0.0, chunk_slots: int = 0,
+                 state: torch.Tensor | None = None, attach: bool = False):
+        if k_cache.dim() != 4:
+            raise ValueError("k_cache must be [B][Hkv][max_budget][d]")
+        if k_cache.dtype not in _DTYPES:
+            raise ValueError(f"unsupported dtype {k_cache.dtype}")
+        self.device = k_cache.device
+        B, Hkv, S, d = k_cache.shape
+        _need(k_cache, "k_cache", (B, Hkv, S, d), k_cache.dtype, self.device)
+        _need(v_cache, "v_cache", (B, Hkv, S, d), k_cache.dtype, self.device)
+        self.B, self.Hkv, self.max_budget, self.d = B, Hkv, S, d
+        self.Hq = int(n_q_heads)
+        self.dtype = k_cache.dtype
+        self.k_cache, self.v_cache = k_cache, v_cache
+        self.budgets = None if budgets is None else [int(x) for x in budgets]
+        self.cfg = _lib.make_config(B, self.Hq, Hkv, d, S, sink, recent, _DTYPES[self.dtype], _SCORES[score],
+                                    softmax_scale, chunk_slots)
+        self.state_bytes = _lib.lf_state_bytes(self.cfg, self.budgets)
+        if state is None:
+            if attach:
+                raise ValueError("attach needs the saved state tensor")
+            state = torch.empty(self.state_bytes, dtype=torch.uint8, device=self.device)
+        elif state.numel() < self.state_bytes or state.device != self.device:
+            raise ValueError("state tensor too small or on another device")
+        self.state = state
+        self.handle = _lib.lf_init_cache(self.cfg, self.budgets, list(seq_len), k_cache.data_ptr(),
+                                         v_cache.data_ptr(), state.data_ptr(), state.numel(),
+                                         LF_INIT_ATTACH if attach else 0, _stream_handle(self.device))
+
+    def step(self, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, out: torch.Tensor | None = None,
+             evict_idx: torch.Tensor | None = None, scores: torch.Tensor | None = None,
+             lse: torch.Tensor | None = None):
+        """One fused decode step; returns (out [B][Hq][d], evict_idx int32 [B][Hkv])."""
+        if not self.handle:
+            raise RuntimeError("cache is closed")
+        _need(q, "q", (self.B, self.Hq, self.d), self.dtype, self.device)
+        _need(k_new, "k_new", (self.B, self.Hkv, self.d), self.dtype, self.device)
+        _need(v_new, "v_new", (self.B, self.Hkv, self.d), self.dtype, self.device)
+        if out is None:
+            out = torch.empty_like(q)
+        else:
+            _need(out, "out", (self.B, self.Hq, self.d), self.dtype, self.device)
+        if evict_idx is None:
+            evict_idx = torch.empty((self.B, self.Hkv), dtype=torch.int32, device=self.device)
+        else:
+            _need(evict_idx, "evict_idx", (self.B, self.Hkv), torch.int32, self.device)
+        stream = _stream_handle(self.device)
+        if scores is None and lse is None:
+            _lib.lf_decode_step(q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), self.handle, out.data_ptr(),
+                                evict_idx.data_ptr(), stream)
+        else:
+            if scores is not None:
+                _need(scores, "scores", (self.B, self.Hkv, self.max_budget), torch.float32, self.device)
+            if lse is not None:
+                _need(lse, "lse", (self.B, self.Hq), torch.float32, self.device)
+            _lib.lf_decode_step_dbg(q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), self.handle, out.data_ptr(),
+                                    evict_idx.data_ptr(), 0 if scores is None else scores.data_ptr(),
+                                    0 if lse is None else lse.data_ptr(), stream)
+        return out, evict_idx
+
+    def close(self) -> None:
+        if self.handle:
+            _lib.lf_free(self.handle)
+            self.handle = 0
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,324 @@
+// Host runtime of the fused LongFlow decode step: argument validation, the
+// layout of the caller's device state buffer, the split-KV work list and the
+// C ABI entry points declared in include/lf.h.
+//
+// The cache is static: its slots are fixed at init and every step overwrites
+// one of them in place (the statically pre-allocated KV cache of the LongFlow
+// summary, section 2.C).  This file only plans work and launches it; every
+// arithmetic step of the decode runs in lf_kernel.hip.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "../../include/lf.h"
+#include "lf_internal.h"
+
+struct lf_cache {
+  uint64_t magic;
+  lf_config cfg;
+  int group;
+  lf::StateLayout lay;
+  void* k_cache;
+  void* v_cache;
+  char* state;
+  float scale_log2;
+};
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+lf_status fail(lf_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+size_t align_up(size_t x) { return (x + lf::kAlign - 1) / lf::kAlign * lf::kAlign; }
+
+lf_status validate_config(const lf_config* cfg) {
+  if (!cfg) return fail(LF_ERR_ARG, "cfg is NULL");
+  if (cfg->batch < 1) return fail(LF_ERR_ARG, "batch must be >= 1 (got %d)", cfg->batch);
+  if (cfg->n_kv_heads < 1) return fail(LF_ERR_ARG, "n_kv_heads must be >= 1 (got %d)", cfg->n_kv_heads);
+  if (cfg->n_q_heads < cfg->n_kv_heads || cfg->n_q_heads % cfg->n_kv_heads)
+    return fail(LF_ERR_ARG, "n_q_heads (%d) must be a positive multiple of n_kv_heads (%d)", cfg->n_q_heads,
+                cfg->n_kv_heads);
+  const int group = cfg->n_q_heads / cfg->n_kv_heads;
+  if (group > lf::kMaxGroup)
+    return fail(LF_ERR_UNSUPPORTED, "group size n_q_heads/n_kv_heads = %d; supported 1..%d", group, lf::kMaxGroup);
+  if (cfg->head_dim != 64 && cfg->head_dim != 128)
+    return fail(LF_ERR_UNSUPPORTED, "head_dim %d; supported 64 and 128", cfg->head_dim);
+  if (cfg->dtype != LF_F32 && cfg->dtype != LF_BF16)
+    return fail(LF_ERR_UNSUPPORTED, "dtype %d; supported LF_F32 and LF_BF16", cfg->dtype);
+  if (cfg->score != LF_SCORE_ATTN && cfg->score != LF_SCORE_VL1)
+    return fail(LF_ERR_ARG, "score mode %d; expected LF_SCORE_ATTN or LF_SCORE_VL1", cfg->score);
+  if (cfg->max_budget < 1 || cfg->max_budget > lf::kMaxBudget)
+    return fail(LF_ERR_ARG, "max_budget %d outside [1, %d]", cfg->max_budget, lf::kMaxBudget);
+  if (cfg->sink < 0 || cfg->recent < 0) return fail(LF_ERR_ARG, "sink and recent must be >= 0");
+  if (cfg->reserved != 0) return fail(LF_ERR_ARG, "reserved must be 0");
+  if (!(cfg->softmax_scale == cfg->softmax_scale) || std::isinf(cfg->softmax_scale))
+    return fail(LF_ERR_ARG, "softmax_scale must be finite");
+  if (cfg->chunk_slots < 0) return fail(LF_ERR_ARG, "chunk_slots must be >= 0");
+  if (cfg->chunk_slots > 0) {
+    const int tile = lf::tile_rows(cfg->dtype, cfg->head_dim, group);
+    if (cfg->chunk_slots % tile)
+      return fail(LF_ERR_ARG, "chunk_slots %d must be a multiple of the kernel tile (%d rows)", cfg->chunk_slots,
+                  tile);
+  }
+  const double cache_elems = (double)cfg->batch * cfg->n_kv_heads * cfg->max_budget * cfg->head_dim;
+  if (cache_elems > 9.0e15) return fail(LF_ERR_ARG, "cache too large");
+  return LF_OK;
+}
+
+lf_status validate_budgets(const lf_config* cfg, const int32_t* budgets, std::vector<int32_t>& out) {
+  out.assign(cfg->batch, cfg->max_budget);
+  if (budgets)
+    for (int b = 0; b < cfg->batch; ++b) out[b] = budgets[b];
+  for (int b = 0; b < cfg->batch; ++b) {
+    if (out[b] < 1 || out[b] > cfg->max_budget)
+      return fail(LF_ERR_ARG, "budget[%d] = %d outside [1, max_budget = %d]", b, out[b], cfg->max_budget);
+    if ((int64_t)out[b] <= (int64_t)cfg->sink + cfg->recent)
+      return fail(LF_ERR_ARG, "budget[%d] = %d must exceed sink + recent = %d", b, out[b], cfg->sink + cfg->recent);
+  }
+  return LF_OK;
+}
+
+// Chunk length: a multiple of the kernel tile, about 16 chunks for the largest
+// budget, and never more than kMaxChunks chunks per pair.
+int choose_chunk(const lf_config* cfg, int group, int max_b) {
+  const int tile = lf::tile_rows(cfg->dtype, cfg->head_dim, group);
+  if (cfg->chunk_slots > 0) return cfg->chunk_slots;  // explicit: make_layout checks the chunk count
+  int chunk = (max_b + 15) / 16;
+  const int min_chunk = (max_b + lf::kMaxChunks - 1) / lf::kMaxChunks;
+  if (chunk < min_chunk) chunk = min_chunk;
+  return (chunk + tile - 1) / tile * tile;
+}
+
+lf_status make_layout(const lf_config* cfg, const std::vector<int32_t>& bud, lf::StateLayout& L,
+                      std::vector<lf::WorkItem>* items, std::vector<lf::PairMeta>* meta) {
+  const int group = cfg->n_q_heads / cfg->n_kv_heads;
+  int max_b = 0;
+  for (int x : bud) max_b = x > max_b ? x : max_b;
+  const int chunk = choose_chunk(cfg, group, max_b);
+  const int64_t P = (int64_t)cfg->batch * cfg->n_kv_heads;
+  int64_t W = 0, S = 0;
+  int max_nchunk = 0;
+  for (int b = 0; b < cfg->batch; ++b) {
+    const int nch = (bud[b] + chunk - 1) / chunk;
+    max_nchunk = nch > max_nchunk ? nch : max_nchunk;
+    W += (int64_t)nch * cfg->n_kv_heads;
+    S += (int64_t)bud[b] * cfg->n_kv_heads;
+  }
+  if (max_nchunk > lf::kMaxChunks) return fail(LF_ERR_ARG, "chunk_slots too small: %d chunks per pair", max_nchunk);
+  if (W > 0x7FFFFFFF || P > 0x7FFFFFFF || S > 0x7FFFFFFF) return fail(LF_ERR_ARG, "batch too large");
+  L.n_pairs = (int32_t)P;
+  L.n_items = (int32_t)W;
+  L.total_slots = (int32_t)S;
+  L.chunk = chunk;
+  L.max_nchunk = max_nchunk;
+  size_t off = 0;
+  L.header = off;
+  off = align_up(off + sizeof(lf::StateHeader));
+  L.meta = off;
+  off = align_up(off + sizeof(lf::PairMeta) * P);
+  L.ring = off;
+  off = align_up(off + sizeof(int32_t) * P * (size_t)cfg->recent);
+  L.items = off;
+  off = align_up(off + sizeof(lf::WorkItem) * W);
+  L.part_ml = off;
+  off = align_up(off + sizeof(float) * 2 * group * W);
+  L.part_acc = off;
+  off = align_up(off + sizeof(float) * (size_t)group * cfg->head_dim * W);
+  L.logits = off;
+  off = align_up(off + sizeof(float) * (size_t)group * S);
+  L.vnorm = off;
+  if (cfg->score == LF_SCORE_VL1) off = align_up(off + sizeof(float) * S);
+  L.total = off;
+  if (items || meta) {
+    if (items) items->clear();
+    if (meta) meta->assign(P, lf::PairMeta{});
+    int32_t item = 0, slot = 0;
+    for (int b = 0; b < cfg->batch; ++b) {
+      const int nch = (bud[b] + chunk - 1) / chunk;
+      for (int g = 0; g < cfg->n_kv_heads; ++g) {
+        const int32_t p = b * cfg->n_kv_heads + g;
+        if (meta) {
+          lf::PairMeta& m = (*meta)[p];
+          m.budget = bud[b];
+          m.nchunk = nch;
+          m.item0 = item;
+          m.slot0 = slot;
+        }
+        for (int c = 0; c < nch; ++c) {
+          const int start = c * chunk;
+          const int cnt = bud[b] - start < chunk ? bud[b] - start : chunk;
+          if (items) items->push_back(lf::WorkItem{p, start, cnt, c});
+        }
+        item += nch;
+        slot += bud[b];
+      }
+    }
+  }
+  return LF_OK;
+}
+
+lf_status check_handle(const lf_cache* c) {
+  if (!c) return fail(LF_ERR_ARG, "cache handle is NULL");
+  if (c->magic != lf::kHandleMagic) return fail(LF_ERR_STATE, "cache handle is not a live lf_cache");
+  return LF_OK;
+}
+
+lf_status step_impl(const void* q, const void* k_new, const void* v_new, lf_cache* cache, void* out,
+                    int32_t* evict_idx, float* scores, float* lse, void* stream) {
+  lf_status st = check_handle(cache);
+  if (st != LF_OK) return st;
+  if (!q || !k_new || !v_new || !out || !evict_idx)
+    return fail(LF_ERR_ARG, "q, k_new, v_new, out and evict_idx must be non-NULL");
+  const lf_config& cfg = cache->cfg;
+  lf::StepArgs a{};
+  a.q = q;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_cache = cache->k_cache;
+  a.v_cache = cache->v_cache;
+  a.out = out;
+  a.evict_idx = evict_idx;
+  a.dbg_scores = scores;
+  a.dbg_lse = lse;
+  char* s = cache->state;
+  const lf::StateLayout& L = cache->lay;
+  a.meta = reinterpret_cast<lf::PairMeta*>(s + L.meta);
+  a.ring = reinterpret_cast<int32_t*>(s + L.ring);
+  a.items = reinterpret_cast<const lf::WorkItem*>(s + L.items);
+  a.part_ml = reinterpret_cast<float*>(s + L.part_ml);
+  a.part_acc = reinterpret_cast<float*>(s + L.part_acc);
+  a.logits = reinterpret_cast<float*>(s + L.logits);
+  a.vnorm = reinterpret_cast<float*>(s + L.vnorm);
+  a.n_items = L.n_items;
+  a.n_q_heads = cfg.n_q_heads;
+  a.n_kv_heads = cfg.n_kv_heads;
+  a.max_budget = cfg.max_budget;
+  a.sink = cfg.sink;
+  a.recent = cfg.recent;
+  a.scale_log2 = cache->scale_log2;
+  a.vl1 = cfg.score == LF_SCORE_VL1;
+  if (lf::launch_step(cfg.dtype, cfg.head_dim, cache->group, a, stream, g_err, sizeof(g_err)))
+    return LF_ERR_HIP;
+  return LF_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t lf_abi_version(void) { return LF_ABI_VERSION; }
+
+const char* lf_last_error(void) { return g_err; }
+
+lf_status lf_state_bytes(const lf_config* cfg, const int32_t* budgets, size_t* bytes) {
+  lf_status st = validate_config(cfg);
+  if (st != LF_OK) return st;
+  if (!bytes) return fail(LF_ERR_ARG, "bytes is NULL");
+  std::vector<int32_t> bud;
+  if ((st = validate_budgets(cfg, budgets, bud)) != LF_OK) return st;
+  lf::StateLayout L{};
+  if ((st = make_layout(cfg, bud, L, nullptr, nullptr)) != LF_OK) return st;
+  *bytes = L.total;
+  g_err[0] = 0;
+  return LF_OK;
+}
+
+lf_status lf_init_cache(const lf_config* cfg, const int32_t* budgets, const int64_t* seq_len, void* k_cache,
+                        void* v_cache, void* state, size_t state_bytes, int32_t flags, void* stream,
+                        lf_cache** out) {
+  lf_status st = validate_config(cfg);
+  if (st != LF_OK) return st;
+  if (!out) return fail(LF_ERR_ARG, "out is NULL");
+  *out = nullptr;
+  if (!seq_len || !k_cache || !v_cache || !state)
+    return fail(LF_ERR_ARG, "seq_len, k_cache, v_cache and state must be non-NULL");
+  if (flags & ~LF_INIT_ATTACH) return fail(LF_ERR_ARG, "unknown flags 0x%x", (unsigned)flags);
+  if (reinterpret_cast<uintptr_t>(state) % lf::kAlign) return fail(LF_ERR_ARG, "state must be 256-byte aligned");
+  const size_t esz = cfg->dtype == LF_BF16 ? 2 : 4;
+  if (reinterpret_cast<uintptr_t>(k_cache) % 16 || reinterpret_cast<uintptr_t>(v_cache) % 16)
+    return fail(LF_ERR_ARG, "k_cache and v_cache must be 16-byte aligned");
+  std::vector<int32_t> bud;
+  if ((st = validate_budgets(cfg, budgets, bud)) != LF_OK) return st;
+  for (int b = 0; b < cfg->batch; ++b)
+    if (seq_len[b] < 0 || seq_len[b] > 0x7FFFFFFFll - 0x10000000ll)
+      return fail(LF_ERR_ARG, "seq_len[%d] = %lld out of range", b, (long long)seq_len[b]);
+  lf::StateLayout L{};
+  std::vector<lf::WorkItem> items;
+  std::vector<lf::PairMeta> meta;
+  if ((st = make_layout(cfg, bud, L, &items, &meta)) != LF_OK) return st;
+  if (state_bytes < L.total)
+    return fail(LF_ERR_ARG, "state_bytes %zu < required %zu (see lf_state_bytes)", state_bytes, L.total);
+  (void)esz;
+
+  if (!(flags & LF_INIT_ATTACH)) {
+    // Host image of header + meta + ring + work list, uploaded in one copy.
+    std::vector<char> img(L.part_ml, 0);
+    lf::StateHeader h{lf::kStateMagic, L.n_pairs, L.n_items, L.total_slots};
+    std::memcpy(img.data() + L.header, &h, sizeof(h));
+    const int R = cfg->recent;
+    int32_t* ring = reinterpret_cast<int32_t*>(img.data() + L.ring);
+    for (int b = 0; b < cfg->batch; ++b) {
+      const int64_t t = seq_len[b];
+      const int64_t len = t < bud[b] ? t : bud[b];
+      for (int g = 0; g < cfg->n_kv_heads; ++g) {
+        const int p = b * cfg->n_kv_heads + g;
+        meta[p].t = (int32_t)t;
+        meta[p].len = (int32_t)len;
+        meta[p].ticket = 0;
+        for (int j = 0; j < R; ++j) ring[(size_t)p * R + j] = -1;
+        // The R newest cached positions [t - R, t): slot = position while the
+        // prefill fits, else they are the last R slots (layout contract).
+        for (int64_t pos = t - R < 0 ? 0 : t - R; pos < t; ++pos) {
+          const int64_t slot = t <= bud[b] ? pos : bud[b] - (t - pos);
+          ring[(size_t)p * R + pos % R] = (int32_t)slot;
+        }
+      }
+    }
+    std::memcpy(img.data() + L.meta, meta.data(), sizeof(lf::PairMeta) * meta.size());
+    std::memcpy(img.data() + L.items, items.data(), sizeof(lf::WorkItem) * items.size());
+    if (lf::upload_and_wait(state, img.data(), img.size(), stream, g_err, sizeof(g_err))) return LF_ERR_HIP;
+  }
+
+  lf_cache* c = new (std::nothrow) lf_cache;
+  if (!c) return fail(LF_ERR_ARG, "out of host memory");
+  c->magic = lf::kHandleMagic;
+  c->cfg = *cfg;
+  c->group = cfg->n_q_heads / cfg->n_kv_heads;
+  c->lay = L;
+  c->k_cache = k_cache;
+  c->v_cache = v_cache;
+  c->state = static_cast<char*>(state);
+  const double scale = cfg->softmax_scale > 0 ? cfg->softmax_scale : 1.0 / std::sqrt((double)cfg->head_dim);
+  c->scale_log2 = (float)(scale * 1.4426950408889634);
+  *out = c;
+  g_err[0] = 0;
+  return LF_OK;
+}
+
+lf_status lf_decode_step(const void* q, const void* k_new, const void* v_new, lf_cache* cache, void* out,
+                         int32_t* evict_idx, void* stream) {
+  return step_impl(q, k_new, v_new, cache, out, evict_idx, nullptr, nullptr, stream);
+}
+
+lf_status lf_decode_step_dbg(const void* q, const void* k_new, const void* v_new, lf_cache* cache, void* out,
+                             int32_t* evict_idx, float* scores, float* lse, void* stream) {
+  return step_impl(q, k_new, v_new, cache, out, evict_idx, scores, lse, stream);
+}
+
+void lf_free(lf_cache* cache) {
+  if (!cache || cache->magic != lf::kHandleMagic) return;
+  cache->magic = 0;
+  delete cache;
+}
+
+}  // extern "C"

@@ -1,0 +1,90 @@
+// Internal layout shared by the host runtime (lf_host.cpp) and the kernels
+// (lf_kernel.hip).  Plain C++: no HIP types, so the host part also builds with g++.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+namespace lf {
+
+constexpr uint32_t kStateMagic = 0x4C46535Au;  // "LFSZ"
+constexpr uint64_t kHandleMagic = 0x4C46434143484531ull;
+constexpr int kMaxBudget = 65536;  // LDS bitmap of protected slots: kMaxBudget bits
+constexpr int kMaxChunks = 256;    // chunks per (sequence, KV head): one tail thread each
+constexpr int kMaxGroup = 8;
+constexpr int kThreads = 256;      // threads per workgroup (4 wave64)
+constexpr size_t kAlign = 256;
+
+// Per (sequence, KV head) pair.  Written by lf_init_cache, updated in place by
+// the last-arriving workgroup of the pair at the end of every step.
+struct PairMeta {
+  int32_t t;        // position of the next incoming token
+  int32_t len;      // filled slots, == budget once the cache is full
+  int32_t budget;   // slot budget of this sequence
+  int32_t nchunk;   // split-KV chunks of this pair
+  int32_t item0;    // index of the pair's first work item
+  int32_t slot0;    // first slot of the pair in the logit / |v| workspaces
+  uint32_t ticket;  // chunks finished in the current step (reset to 0 by the last one)
+  int32_t pad;
+};
+static_assert(sizeof(PairMeta) == 32, "PairMeta layout");
+
+// One split-KV work item: rows [start, start + count) of pair `pair`.
+struct WorkItem {
+  int32_t pair;
+  int32_t start;
+  int32_t count;
+  int32_t chunk;  // index of the chunk within its pair
+};
+static_assert(sizeof(WorkItem) == 16, "WorkItem layout");
+
+struct StateHeader {
+  uint32_t magic;
+  int32_t n_pairs;
+  int32_t n_items;
+  int32_t total_slots;
+};
+
+// Byte offsets of the regions of the caller's state buffer.
+struct StateLayout {
+  size_t header, meta, ring, items, part_ml, part_acc, logits, vnorm, total;
+  int32_t n_pairs, n_items, total_slots, chunk, max_nchunk;
+};
+
+// Arguments of one fused decode-step launch (passed by value to the kernel).
+struct StepArgs {
+  const void* q;
+  const void* k_new;
+  const void* v_new;
+  void* k_cache;
+  void* v_cache;
+  void* out;
+  int32_t* evict_idx;
+  float* dbg_scores;  // may be null
+  float* dbg_lse;     // may be null
+  PairMeta* meta;
+  int32_t* ring;
+  const WorkItem* items;
+  float* part_ml;   // [n_items][G][2]: (max of log2-domain logits, sum of exp2)
+  float* part_acc;  // [n_items][G][d]
+  float* logits;    // per pair [G][budget], log2-domain logits of this step
+  float* vnorm;     // per pair [budget], |v|_1 of every slot (VL1 only)
+  int32_t n_items;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t max_budget;
+  int32_t sink;
+  int32_t recent;
+  float scale_log2;  // softmax scale * log2(e)
+  int32_t vl1;
+};
+
+// Tile height (rows per workgroup per pass) of the kernel for a shape; chunk
+// lengths are multiples of it.  Defined next to the kernels.
+int tile_rows(int dtype, int head_dim, int group);
+
+// Kernel launch and runtime helpers, implemented in lf_kernel.hip.
+int launch_step(int dtype, int head_dim, int group, const StepArgs& a, void* stream, char* err, size_t errlen);
+int upload_and_wait(void* dst, const void* src, size_t bytes, void* stream, char* err, size_t errlen);
+
+}  // namespace lf

@@ -1,0 +1,127 @@
+"""The C ABI library without a GPU: it loads, exports every symbol the headers
+declare, and its host-side validation and state sizing behave as documented.
+No call here reaches a kernel or the HIP runtime."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from kv_cache_eviction_lf_amd import _lib
+from kv_cache_eviction_lf_amd._lib import LF_ERR_ARG, LF_ERR_STATE, LF_ERR_UNSUPPORTED, LFError, make_config
+from workloads import WORKLOADS, budgets
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="liblf.so not built")
+
+
+def declared_functions():
+    names = set()
+    for h in HEADERS:
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s+\*?(lf_[a-z0-9_]+)\s*\(", text, re.M):
+            names.add(m.group(1))
+    return names
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert {"lf_init_cache", "lf_decode_step", "lf_free", "lf_state_bytes", "lf_last_error",
+            "lf_decode_step_dbg", "lf_probe_copy", "lf_probe_read"} <= names
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert names <= exported, names - exported
+    lib = _lib.load_library()
+    for n in names:
+        assert hasattr(lib, n)
+    assert set(_lib.PROTOTYPES) == names
+
+
+def test_abi_version():
+    assert _lib.lf_abi_version() == 1
+
+
+def _cfg(**kw):
+    base = dict(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, max_budget=512, sink=4, recent=16)
+    base.update(kw)
+    return make_config(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0), LF_ERR_ARG),
+    (dict(n_kv_heads=0), LF_ERR_ARG),
+    (dict(n_q_heads=7), LF_ERR_ARG),
+    (dict(n_q_heads=18), LF_ERR_UNSUPPORTED),  # G = 9
+    (dict(head_dim=96), LF_ERR_UNSUPPORTED),
+    (dict(dtype=5), LF_ERR_UNSUPPORTED),
+    (dict(score=3), LF_ERR_ARG),
+    (dict(max_budget=0), LF_ERR_ARG),
+    (dict(max_budget=70000), LF_ERR_ARG),
+    (dict(sink=-1), LF_ERR_ARG),
+    (dict(max_budget=20), LF_ERR_ARG),  # budget 20 <= sink + recent
+    (dict(chunk_slots=100), LF_ERR_ARG),  # not a multiple of the tile
+    (dict(chunk_slots=128, max_budget=65536), LF_ERR_ARG),  # 512 chunks per pair
+])
+def test_state_bytes_rejects_bad_configs(kw, status):
+    with pytest.raises(LFError) as ei:
+        _lib.lf_state_bytes(_cfg(**kw))
+    assert ei.value.status == status
+    assert _lib.lf_last_error()
+
+
+def test_state_bytes_rejects_bad_budgets():
+    with pytest.raises(LFError) as ei:
+        _lib.lf_state_bytes(_cfg(), [512, 513])
+    assert ei.value.status == LF_ERR_ARG
+    with pytest.raises(LFError):
+        _lib.lf_state_bytes(_cfg(), [20, 100])  # <= sink + recent
+
+
+def test_state_bytes_of_the_workloads_are_modest():
+    for name, w in WORKLOADS.items():
+        cfg = make_config(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.budget_hi, w.sink, w.recent,
+                          1 if w.dtype == "bf16" else 0)
+        nbytes = _lib.lf_state_bytes(cfg, budgets(w))
+        kv_bytes = int(budgets(w).sum()) * w.n_kv_heads * w.head_dim * (2 if w.dtype == "bf16" else 4) * 2
+        # logits + partials stay a small fraction of the K/V bytes the step streams
+        assert nbytes < 0.15 * kv_bytes + (1 << 20), (name, nbytes, kv_bytes)
+
+
+def test_init_rejects_null_and_misaligned_pointers_before_any_device_call():
+    cfg = _cfg()
+    nbytes = _lib.lf_state_bytes(cfg)
+    with pytest.raises(LFError) as ei:
+        _lib.lf_init_cache(cfg, None, [512, 512], 0, 0, 0, nbytes)
+    assert ei.value.status == LF_ERR_ARG
+    with pytest.raises(LFError) as ei:  # state not 256-byte aligned
+        _lib.lf_init_cache(cfg, None, [512, 512], 4096, 8192, 4096 + 16, nbytes)
+    assert ei.value.status == LF_ERR_ARG
+    with pytest.raises(LFError) as ei:  # state too small
+        _lib.lf_init_cache(cfg, None, [512, 512], 4096, 8192, 1 << 20, nbytes - 1)
+    assert ei.value.status == LF_ERR_ARG
+    with pytest.raises(LFError) as ei:  # negative seq_len
+        _lib.lf_init_cache(cfg, None, [-1, 512], 4096, 8192, 1 << 20, nbytes)
+    assert ei.value.status == LF_ERR_ARG
+    with pytest.raises(LFError) as ei:  # unknown flag
+        _lib.lf_init_cache(cfg, None, [1, 512], 4096, 8192, 1 << 20, nbytes, flags=4)
+    assert ei.value.status == LF_ERR_ARG
+
+
+def test_step_rejects_bad_handles_without_launching():
+    with pytest.raises(LFError) as ei:
+        _lib.lf_decode_step(1, 1, 1, 0, 1, 1)
+    assert ei.value.status == LF_ERR_ARG
+    fake = (ctypes.c_uint64 * 64)()  # zeroed host memory: wrong magic
+    with pytest.raises(LFError) as ei:
+        _lib.lf_decode_step(1, 1, 1, ctypes.addressof(fake), 1, 1)
+    assert ei.value.status == LF_ERR_STATE
+    _lib.lf_free(0)  # NULL-safe
+    _lib.lf_free(ctypes.addressof(fake))  # wrong magic: ignored

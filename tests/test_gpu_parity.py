@@ -1,0 +1,179 @@
+"""GPU parity: the HIP decode step against the float64 oracle, through the C ABI.
+
+Attention outputs within 2e-2 (bf16) / 1e-5 (fp32) absolute, evicted slots
+exact outside 1e-6 score ties, importance and log-normaliser checked through
+the debug entry point, and the final cache bit-identical to the oracle's."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from tests.gpu_harness import log, parity_run
+from workloads import budgets, get_workload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def test_single_hip_runtime_in_process():
+    from kv_cache_eviction_lf_amd import load_library
+
+    load_library()
+    torch.zeros(1, device="cuda:0")
+    maps = open("/proc/self/maps").read()
+    paths = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    log(f"libamdhip64 mappings: {paths}")
+    assert len(paths) == 1, paths
+
+
+# ---------------------------------------------------------------- the named workloads
+
+def test_tiny_f32_all_steps_lockstep():
+    rep = parity_run(get_workload("tiny_f32"), 512, dbg_every=8)
+    assert rep.steps == 512
+
+
+def test_tiny_f32_free_running():
+    rep = parity_run(get_workload("tiny_f32"), 512, free_running=True)
+    assert rep.steps >= 256, rep
+
+
+def test_tiny_f32_vl1_mode():
+    rep = parity_run(get_workload("tiny_f32"), 256, score="vl1", dbg_every=8)
+    assert rep.steps == 256
+
+
+def test_llama8b_full_batch_first_steps():
+    parity_run(get_workload("llama8b_b8"), 16, dbg_every=4)
+
+
+def test_llama8b_subset_long_run():
+    parity_run(get_workload("llama8b_b8"), 768, check=[0, 7], dbg_every=64)
+
+
+def test_llama8b_vl1_subset():
+    parity_run(get_workload("llama8b_b8"), 64, check=[3], score="vl1", dbg_every=8)
+
+
+def test_throughput_b64_sampled():
+    parity_run(get_workload("throughput_b64"), 48, check=[0, 31, 63], dbg_every=16)
+
+
+def test_evict_stress_across_anchor_events():
+    # crosses the anchor queries of steps 500 and 1000
+    parity_run(get_workload("evict_stress"), 1002, check=[0, 1, 2, 15], dbg_every=250)
+
+
+def test_ragged_b128_sampled():
+    w = get_workload("ragged_b128")
+    bud = budgets(w)
+    check = sorted({0, int(np.argmin(bud)), int(np.argmax(bud))})
+    parity_run(w, 40, check=check, dbg_every=13)
+
+
+# ---------------------------------------------------------------- edge cases
+
+def _small(**kw):
+    base = dict(name="edge", batch=3, n_q_heads=8, n_kv_heads=2, head_dim=128, dtype="bf16", budget_lo=300,
+                budget_hi=300, sink=4, recent=16, decode_steps=0, seed=11)
+    base.update(kw)
+    from workloads import Workload
+
+    return Workload(**base)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(prefill="short", prefill_short=100),          # append path, then eviction
+    dict(prefill="short", prefill_short=0, budget_lo=40, budget_hi=40, sink=2, recent=4),  # empty cache
+    dict(n_q_heads=2, n_kv_heads=2),                   # G = 1
+    dict(n_q_heads=16, n_kv_heads=2),                  # G = 8
+    dict(n_q_heads=6, n_kv_heads=2, head_dim=64),      # G = 3, d = 64 bf16
+    dict(dtype="f32", n_q_heads=10, n_kv_heads=2),     # fp32, d = 128, G = 5
+    dict(sink=0, recent=0),                            # no protected window
+    dict(budget_lo=21, budget_hi=21, sink=4, recent=16),  # exactly one evictable slot
+    dict(budget_lo=200, budget_hi=700, prefill="ragged", batch=5),  # ragged budgets and prefill
+])
+def test_edge_cases(kw):
+    w = _small(**kw)
+    steps = 260 if kw.get("prefill") == "short" else 120
+    parity_run(w, steps, dbg_every=7, tag=f" {kw}")
+
+
+def test_small_chunks_and_cache_stride():
+    # many chunks with a ragged last one, and a slot stride larger than every budget
+    w = _small(budget_lo=333, budget_hi=333, batch=2)
+    parity_run(w, 80, chunk_slots=128, max_budget=512, dbg_every=5)
+
+
+def test_vl1_on_ragged_small():
+    w = _small(budget_lo=150, budget_hi=400, prefill="ragged", batch=4, n_q_heads=14, n_kv_heads=2)
+    parity_run(w, 100, score="vl1", dbg_every=9)
+
+
+# ---------------------------------------------------------------- determinism and resume
+
+def _run_steps(w, steps, device, state=None, attach=False, K=None, V=None, start=0):
+    from kv_cache_eviction_lf_amd import LongFlowCache
+    from workloads.device import device_cache, device_step
+
+    if K is None:
+        K, V, seq_len, bud = device_cache(w, device)
+    else:
+        seq_len, bud = None, budgets(w)
+    cache = LongFlowCache(K, V, w.n_q_heads, w.sink, w.recent,
+                          seq_len if seq_len is not None else [0] * w.batch, budgets=bud,
+                          state=state, attach=attach)
+    outs, evs = [], []
+    for s in range(start, start + steps):
+        (qd, kd, vd), _ = device_step(w, s, device)
+        o, e = cache.step(qd, kd, vd)
+        outs.append(o.clone())
+        evs.append(e.clone())
+    torch.cuda.synchronize()
+    return cache, K, V, outs, evs
+
+
+def test_bitwise_deterministic():
+    w = get_workload("llama8b_b8")
+    dev = torch.device("cuda:0")
+    log("[determinism] llama8b_b8 twice, 40 steps")
+    c1, K1, V1, o1, e1 = _run_steps(w, 40, dev)
+    c2, K2, V2, o2, e2 = _run_steps(w, 40, dev)
+    for a, b in zip(o1, o2):
+        assert torch.equal(a, b)
+    for a, b in zip(e1, e2):
+        assert torch.equal(a, b)
+    assert torch.equal(K1, K2) and torch.equal(V1, V2)
+    c1.close()
+    c2.close()
+
+
+def test_resume_from_saved_state():
+    w = get_workload("llama8b_b8").with_(batch=4)
+    dev = torch.device("cuda:0")
+    log("[resume] 20 steps, snapshot, 20 more; restore, attach, 20 more")
+    cache, K, V, _, _ = _run_steps(w, 20, dev)
+    snap = (K.clone(), V.clone(), cache.state.clone())
+    from workloads.device import device_step
+
+    ref_o, ref_e = [], []
+    for s in range(20, 40):
+        (qd, kd, vd), _ = device_step(w, s, dev)
+        o, e = cache.step(qd, kd, vd)
+        ref_o.append(o.clone())
+        ref_e.append(e.clone())
+    cache.close()
+    K2, V2, st2 = snap
+    c2, _, _, o2, e2 = _run_steps(w, 20, dev, state=st2, attach=True, K=K2, V=V2, start=20)
+    for a, b in zip(ref_o, o2):
+        assert torch.equal(a, b)
+    for a, b in zip(ref_e, e2):
+        assert torch.equal(a, b)
+    assert torch.equal(K, K2) and torch.equal(V, V2)
+    c2.close()
