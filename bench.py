@@ -1,0 +1,269 @@
+"""Benchmark of the fused LongFlow decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama8b_b8]
+
+A step is one lf_decode_step over the whole batch of one layer cache:
+attention + importance + argmin + in-place overwrite for every (sequence, KV
+head).  Layer caches rotate (L of them, each a separate static cache) so that
+the K/V bytes of consecutive steps do not fit in the 256 MB Infinity Cache and
+every step streams from HBM.  Steps are captured in HIP graphs and replayed;
+the timed region is bracketed by device synchronisation and HIP events on the
+launch stream.  Inputs are seeded synthetic data already resident in HBM.
+
+Prints one JSON line (rank 0, N = 1): decode steps/s, the roofline of the
+decode kernel (algorithmic bytes per launch / average launch time vs 8 TB/s)
+and the float64 CPU oracle timed on a bounded sample of the same workload."""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+MALL_BYTES = 256 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--workload", default="llama8b_b8")
+    ap.add_argument("--layers", type=int, default=0, help="rotating layer caches (0 = enough to exceed 2x MALL)")
+    ap.add_argument("--score", default="attn", choices=["attn", "vl1"])
+    ap.add_argument("--chunk", type=int, default=0, help="split-KV chunk slots (0 = library default)")
+    ap.add_argument("--eager", action="store_true", help="launch step by step instead of replaying HIP graphs")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--probe", action="store_true", help="also time the HBM read/copy probes")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(w, bud) -> int:
+    """Bytes one step must move: every cached K and V row read, k_new/v_new read
+    and written into the victim slot, q read and the output written."""
+    s = 2 if w.dtype == "bf16" else 4
+    kv = int(np.sum(bud)) * w.n_kv_heads * w.head_dim * 2 * s
+    new = 2 * w.batch * w.n_kv_heads * w.head_dim * 2 * s
+    qo = 2 * w.batch * w.n_q_heads * w.head_dim * s
+    return kv + new + qo
+
+
+def cpu_baseline(w, seconds: float) -> dict:
+    """Time the float64 oracle as it stands, single-threaded, on the same
+    workload (full batch of the first layer) for about `seconds`."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import OracleCache
+    from workloads import budgets, initial_cache, step_inputs
+
+    with threadpool_limits(1):
+        ks, vs, ps, ts = initial_cache(w)
+        oc = OracleCache(ks, vs, ps, ts, budgets(w), w.n_q_heads, w.sink, w.recent)
+        inputs = [step_inputs(w, s) for s in range(4)]
+        oc.step(*inputs[0])  # warm-up
+        n, t0 = 0, time.perf_counter()
+        while True:
+            oc.step(*inputs[(n + 1) % 4])
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= seconds and n >= 2:
+                break
+    return {"value": n / el, "unit": "steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"{w.name} full batch ({w.batch} sequences), {n} float64 oracle steps after 1 warm-up, "
+                      f"{el:.1f} s, numpy with BLAS limited to 1 thread"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the decode step has no cross-GPU exchange, and this build "
+              "runs on a single MI355X; run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from kv_cache_eviction_lf_amd import LongFlowCache, _lib
+    from workloads import budgets, get_workload
+    from workloads.device import device_cache, device_step
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    lib = _lib.load_library()
+    dev = torch.device("cuda:0")
+    w = get_workload(args.workload)
+    bud = budgets(w)
+    step_bytes = algorithmic_bytes(w, bud)
+    layer_kv = int(np.sum(bud)) * w.n_kv_heads * w.head_dim * 2 * (2 if w.dtype == "bf16" else 4)
+    L = args.layers or max(1, math.ceil(2 * MALL_BYTES / layer_kv))
+
+    # L independent layer caches (distinct seeds) and a pool of step inputs.
+    caches = []
+    for layer in range(L):
+        wl = w.with_(seed=w.seed + 7919 * layer)
+        K, V, seq_len, _ = device_cache(wl, dev)
+        caches.append(LongFlowCache(K, V, w.n_q_heads, w.sink, w.recent, seq_len, budgets=bud,
+                                    score=args.score, chunk_slots=args.chunk))
+    P = 8
+    pool = [device_step(w, s, dev)[0] for s in range(P)]
+    outs = [torch.empty_like(pool[0][0]) for _ in range(L)]
+    evs = [torch.empty((w.batch, w.n_kv_heads), dtype=torch.int32, device=dev) for _ in range(L)]
+    ptrs = [(caches[i].handle, outs[i].data_ptr(), evs[i].data_ptr()) for i in range(L)]
+    qptrs = [tuple(t.data_ptr() for t in x) for x in pool]
+    step_fn = lib.lf_decode_step
+
+    def launch(k, stream):
+        h, o, e = ptrs[k % L]
+        q, kn, vn = qptrs[k % P]
+        st = step_fn(q, kn, vn, h, o, e, stream)
+        if st:
+            raise RuntimeError(f"lf_decode_step failed: {_lib.lf_last_error()}")
+
+    torch.cuda.synchronize()
+    cur = torch.cuda.current_stream()
+
+    def run_eager(n, base):
+        sh = cur.cuda_stream
+        for k in range(n):
+            launch(base + k, sh)
+
+    graphs = {}
+
+    def graph_for(n, base):
+        key = (n, base % (L * P))
+        if key not in graphs:
+            g = torch.cuda.CUDAGraph()
+            cs = torch.cuda.Stream()
+            with torch.cuda.graph(g, stream=cs):
+                sh = torch.cuda.current_stream().cuda_stream
+                for k in range(n):
+                    launch(base + k, sh)
+            graphs[key] = g
+        return graphs[key]
+
+    chunk = 512 if not args.eager else 0
+    # pre-capture what the timed region replays (capture launches nothing)
+    if not args.eager:
+        full, rem = divmod(args.steps, chunk)
+        if full:
+            graph_for(chunk, 0)
+        if rem:
+            graph_for(rem, full * chunk)
+        wf, wr = divmod(args.warmup, chunk)
+        if wf:
+            graph_for(chunk, 0)
+        if wr:
+            graph_for(wr, wf * chunk)
+
+    def run(n):
+        if args.eager:
+            run_eager(n, 0)
+            return
+        full, rem = divmod(n, chunk)
+        for i in range(full):
+            graph_for(chunk, 0).replay()
+        if rem:
+            graph_for(rem, full * chunk).replay()
+
+    run(args.warmup)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(cur)
+    run(args.steps)
+    ev1.record(cur)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1)
+    ms_per_step = ms / args.steps
+    steps_per_s = 1e3 / ms_per_step
+    achieved = step_bytes / (ms_per_step * 1e-3) / 1e9  # GB/s
+    for c in caches:
+        c.close()
+
+    probe = None
+    if args.probe:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty(n, dtype=torch.uint8, device=dev)
+        sink = torch.empty(_lib.lf_probe_read_sink_words(), dtype=torch.int32, device=dev)
+        res = {}
+        for name in ("read", "copy"):
+            for _ in range(3):
+                if name == "read":
+                    _lib.lf_probe_read(src.data_ptr(), n, sink.data_ptr(), cur.cuda_stream)
+                else:
+                    _lib.lf_probe_copy(src.data_ptr(), dst.data_ptr(), n, cur.cuda_stream)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(cur)
+            for _ in range(10):
+                if name == "read":
+                    _lib.lf_probe_read(src.data_ptr(), n, sink.data_ptr(), cur.cuda_stream)
+                else:
+                    _lib.lf_probe_copy(src.data_ptr(), dst.data_ptr(), n, cur.cuda_stream)
+            b.record(cur)
+            torch.cuda.synchronize()
+            t = a.elapsed_time(b) / 10 * 1e-3
+            res[name + "_GBps"] = round((n if name == "read" else 2 * n) / t / 1e9, 1)
+        probe = res
+
+    base = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_seconds)
+    line = {
+        "metric": "decode steps/s (one fused attention+score+evict step over the batch of one layer)",
+        "value": round(steps_per_s, 1),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) q/k/v, bf16 round-to-nearest-even)",
+        "config": {
+            "workload": w.name,
+            "batch": w.batch,
+            "n_q_heads": w.n_q_heads,
+            "n_kv_heads": w.n_kv_heads,
+            "head_dim": w.head_dim,
+            "budget": [int(bud.min()), int(bud.max())] if not w.fixed_budget else int(bud[0]),
+            "sink": w.sink,
+            "recent": w.recent,
+            "score": args.score,
+            "layer_caches": L,
+            "launch": "eager" if args.eager else "hip-graph",
+            "chunk_slots": caches[0].cfg.chunk_slots or "auto",
+        },
+        "kv_GBps": round(achieved, 1),
+        "pct_hbm_peak": round(100 * achieved / HBM_PEAK_GBPS, 2),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "bytes_per_launch": step_bytes,
+            "kernel": "lf_step_kernel",
+        },
+        "cpu_baseline": base,
+        "wall_s_timed": round(wall, 4),
+    }
+    if probe:
+        line["hbm_probe"] = probe
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -10,6 +10,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <algorithm>
 #include <new>
 #include <vector>
 
@@ -88,12 +89,16 @@ lf_status validate_budgets(const lf_config* cfg, const int32_t* budgets, std::ve
   return LF_OK;
 }
 
-// Chunk length: a multiple of the kernel tile, about 16 chunks for the largest
-// budget, and never more than kMaxChunks chunks per pair.
+// Chunk length: a multiple of the kernel tile.  Pairs are split only when
+// there are too few of them to give about kTargetItems workgroups; a pair never
+// has more than kMaxChunks chunks.
 int choose_chunk(const lf_config* cfg, int group, int max_b) {
   const int tile = lf::tile_rows(cfg->dtype, cfg->head_dim, group);
   if (cfg->chunk_slots > 0) return cfg->chunk_slots;  // explicit: make_layout checks the chunk count
-  int chunk = (max_b + 15) / 16;
+  const int64_t pairs = (int64_t)cfg->batch * cfg->n_kv_heads;
+  int64_t want = (lf::kTargetItems + pairs - 1) / pairs;  // chunks per pair
+  if (want < 1) want = 1;
+  int chunk = (int)((max_b + want - 1) / want);
   const int min_chunk = (max_b + lf::kMaxChunks - 1) / lf::kMaxChunks;
   if (chunk < min_chunk) chunk = min_chunk;
   return (chunk + tile - 1) / tile * tile;
@@ -112,7 +117,7 @@ lf_status make_layout(const lf_config* cfg, const std::vector<int32_t>& bud, lf:
     const int nch = (bud[b] + chunk - 1) / chunk;
     max_nchunk = nch > max_nchunk ? nch : max_nchunk;
     W += (int64_t)nch * cfg->n_kv_heads;
-    S += (int64_t)bud[b] * cfg->n_kv_heads;
+    S += (int64_t)(bud[b] + lf::kSlotPad - 1) / lf::kSlotPad * lf::kSlotPad * cfg->n_kv_heads;
   }
   if (max_nchunk > lf::kMaxChunks) return fail(LF_ERR_ARG, "chunk_slots too small: %d chunks per pair", max_nchunk);
   if (W > 0x7FFFFFFF || P > 0x7FFFFFFF || S > 0x7FFFFFFF) return fail(LF_ERR_ARG, "batch too large");
@@ -140,27 +145,40 @@ lf_status make_layout(const lf_config* cfg, const std::vector<int32_t>& bud, lf:
   if (cfg->score == LF_SCORE_VL1) off = align_up(off + sizeof(float) * S);
   L.total = off;
   if (items || meta) {
+    // Workspace offsets follow pair order; work items follow sequences in
+    // decreasing budget (longest first, so the dispatcher's greedy placement
+    // balances ragged budgets), the chunks of one pair contiguous.
     if (items) items->clear();
     if (meta) meta->assign(P, lf::PairMeta{});
-    int32_t item = 0, slot = 0;
+    int32_t slot = 0;
     for (int b = 0; b < cfg->batch; ++b) {
+      const int lstride = (bud[b] + lf::kSlotPad - 1) / lf::kSlotPad * lf::kSlotPad;
+      for (int g = 0; g < cfg->n_kv_heads; ++g) {
+        if (meta) {
+          lf::PairMeta& m = (*meta)[b * cfg->n_kv_heads + g];
+          m.budget = bud[b];
+          m.nchunk = (bud[b] + chunk - 1) / chunk;
+          m.slot0 = slot;
+          m.lstride = lstride;
+        }
+        slot += lstride;
+      }
+    }
+    std::vector<int> order(cfg->batch);
+    for (int b = 0; b < cfg->batch; ++b) order[b] = b;
+    std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return bud[x] > bud[y]; });
+    int32_t item = 0;
+    for (int b : order) {
       const int nch = (bud[b] + chunk - 1) / chunk;
       for (int g = 0; g < cfg->n_kv_heads; ++g) {
         const int32_t p = b * cfg->n_kv_heads + g;
-        if (meta) {
-          lf::PairMeta& m = (*meta)[p];
-          m.budget = bud[b];
-          m.nchunk = nch;
-          m.item0 = item;
-          m.slot0 = slot;
-        }
+        if (meta) (*meta)[p].item0 = item;
         for (int c = 0; c < nch; ++c) {
           const int start = c * chunk;
           const int cnt = bud[b] - start < chunk ? bud[b] - start : chunk;
           if (items) items->push_back(lf::WorkItem{p, start, cnt, c});
         }
         item += nch;
-        slot += bud[b];
       }
     }
   }

@@ -14,6 +14,8 @@ constexpr int kMaxChunks = 256;    // chunks per (sequence, KV head): one tail t
 constexpr int kMaxGroup = 8;
 constexpr int kThreads = 256;      // threads per workgroup (4 wave64)
 constexpr size_t kAlign = 256;
+constexpr int kSlotPad = 64;        // per-pair workspace rows are padded to this many slots
+constexpr int kTargetItems = 512;   // split pairs into chunks until about this many work items
 
 // Per (sequence, KV head) pair.  Written by lf_init_cache, updated in place by
 // the last-arriving workgroup of the pair at the end of every step.
@@ -25,7 +27,7 @@ struct PairMeta {
   int32_t item0;    // index of the pair's first work item
   int32_t slot0;    // first slot of the pair in the logit / |v| workspaces
   uint32_t ticket;  // chunks finished in the current step (reset to 0 by the last one)
-  int32_t pad;
+  int32_t lstride;  // row stride of the pair's logit workspace: budget rounded up to 64
 };
 static_assert(sizeof(PairMeta) == 32, "PairMeta layout");
 

@@ -16,22 +16,27 @@
 //  * The step is HBM-bound: every cached K and V byte is read once, so the
 //    kernel is a streaming scan, not a contraction.  Each lane issues 16-byte
 //    loads of one row segment; a 64-lane load covers 64/LPR consecutive rows
-//    (LPR = lanes per row), so every wave load is one contiguous 1 KiB run.
-//    Each lane uses exactly the bytes it loads (q for all G heads of the group
-//    is held in registers), so K/V go HBM -> VGPR with no LDS round trip.
-//  * Split-KV: the (sequence, KV head) pairs are cut into chunks listed in a
-//    static work list; one 256-thread workgroup per chunk.  A chunk keeps a
-//    running max / sum / weighted value sum per head (online softmax in the
-//    log2 domain) and stores its raw logits for the score pass.
-//  * The last-arriving workgroup of a pair (device-scope ticket) merges the
-//    chunk partials in chunk order, adds the incoming token, writes the output,
-//    computes the exact importance of every slot from the stored logits and
-//    the global max / normaliser, takes the lexicographic (score, slot) argmin
-//    outside the sink slots and the ring of recent slots, and copies k_new /
-//    v_new into the victim slot.  No other workgroup touches that pair after
-//    its ticket, so the in-place write cannot race with a reader.
-//  * Reductions across the lanes of a row use DPP (quad_perm, row mirrors);
-//    everything else is fixed-order, so results are bit-reproducible.
+//    (LPR = lanes per row), one contiguous 1 KiB run per wave load.  Each lane
+//    uses exactly the bytes it loads (the group's q is held in registers), so
+//    K/V go HBM -> VGPR.  The tile loop is software-pipelined: the next tile's
+//    K/V loads are in flight while the current tile is computed.
+//  * bf16 q.k uses v_dot2c_f32_bf16 on the packed pairs as loaded (fp32
+//    accumulate); P.V and all softmax arithmetic are fp32.
+//  * Work is a static list of (pair, row range) chunks, pair = (sequence, KV
+//    head).  Pairs are split only when there are too few of them to fill the
+//    GPU.  A chunk keeps a running max / sum / weighted value sum per head
+//    (online softmax, log2 domain) and stores its raw logits for the score pass.
+//  * A pair's tail runs in the workgroup that finishes it: directly when the
+//    pair is one chunk, else in the last-arriving chunk (device-scope ticket,
+//    one release per workgroup).  The tail merges the partials in chunk order,
+//    adds the incoming token, writes the output, computes the exact importance
+//    of every slot from the stored logits with the global max / normaliser,
+//    takes the lexicographic (score, slot) argmin outside the sink slots and the
+//    ring of recent slots, and copies k_new / v_new into the victim slot.  No
+//    other workgroup reads the pair after its ticket, so the in-place write
+//    cannot race with a reader.
+//  * Row reductions use DPP (quad_perm, row mirrors); every other reduction has
+//    a fixed order, so results are bit-reproducible.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -44,6 +49,8 @@ namespace {
 
 constexpr float kNegBig = -1.0e30f;  // running-max start: finite, so empty partials merge without NaN
 constexpr int kWaves = kThreads / 64;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 struct F32T {
   using elem = float;
@@ -59,12 +66,14 @@ struct Shape {
   static constexpr int kEpl = T::kEpl;
   static constexpr int kLpr = D / kEpl;   // lanes per row
   static constexpr int kRpl = 64 / kLpr;  // rows per wave load
-  static constexpr int kU = G <= 4 ? 8 : 4;  // row loads per lane per tile (per tensor)
+  static constexpr int kU = 4;            // row loads per lane per tile per tensor (double-buffered)
   static constexpr int kTile = kWaves * kRpl * kU;
-  // LDS: cross-wave merge [wave][head][D + 2] before the ticket; tail buffers after.
+  // LDS: merged chunk partial [G][D + 2] kept for the tail, then a region used
+  // first for the cross-wave merge [wave][G][D + 2] and later by the tail.
+  static constexpr int kPartFloats = G * (D + 2);
   static constexpr int kMergeFloats = kWaves * G * (D + 2);
-  static constexpr int kTailFloats = kMaxChunks * G + 2 * kWaves * G + 3 * G + kMaxBudget / 32 + 2 * kWaves;
-  static constexpr int kSmemFloats = kMergeFloats > kTailFloats ? kMergeFloats : kTailFloats;
+  static constexpr int kTailFloats = kMaxChunks * G + 2 * kWaves * G + kMaxBudget / 32 + 2 * kWaves;
+  static constexpr int kSmemFloats = kPartFloats + (kMergeFloats > kTailFloats ? kMergeFloats : kTailFloats);
 };
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -132,6 +141,56 @@ __device__ __forceinline__ float row_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// The group's q for this lane's dimensions.  bf16: raw packed pairs (logits are
+// scaled after the dot); fp32: values pre-multiplied by scale * log2(e).
+template <class T, int G>
+struct QReg {
+  uint32_t w[G][4];
+};
+template <int G>
+struct QReg<F32T, G> {
+  float x[G][4];
+};
+
+template <class T, int G>
+__device__ __forceinline__ void load_q(QReg<T, G>& q, const typename T::elem* qb, int D, float scale_log2) {
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const uint4 r = *reinterpret_cast<const uint4*>(qb + h * D);
+    if constexpr (T::kEpl == 8) {
+      q.w[h][0] = r.x;
+      q.w[h][1] = r.y;
+      q.w[h][2] = r.z;
+      q.w[h][3] = r.w;
+    } else {
+      q.x[h][0] = __uint_as_float(r.x) * scale_log2;
+      q.x[h][1] = __uint_as_float(r.y) * scale_log2;
+      q.x[h][2] = __uint_as_float(r.z) * scale_log2;
+      q.x[h][3] = __uint_as_float(r.w) * scale_log2;
+    }
+  }
+}
+
+// This lane's part of q_h . k (before the row reduction and, for bf16, before scaling).
+template <class T, int G>
+__device__ __forceinline__ float qk_part(const QReg<T, G>& q, int h, const uint4& k) {
+  if constexpr (T::kEpl == 8) {
+    float p = dot2_bf16(q.w[h][0], k.x, 0.f);
+    p = dot2_bf16(q.w[h][1], k.y, p);
+    p = dot2_bf16(q.w[h][2], k.z, p);
+    return dot2_bf16(q.w[h][3], k.w, p);
+  } else {
+    float p = q.x[h][0] * __uint_as_float(k.x);
+    p = fmaf(q.x[h][1], __uint_as_float(k.y), p);
+    p = fmaf(q.x[h][2], __uint_as_float(k.z), p);
+    return fmaf(q.x[h][3], __uint_as_float(k.w), p);
+  }
+}
+
 // (score, slot) lexicographic minimum of two candidates.
 __device__ __forceinline__ void argmin_merge(float& s, int& i, float so, int io) {
   if (so < s || (so == s && io < i)) {
@@ -140,234 +199,59 @@ __device__ __forceinline__ void argmin_merge(float& s, int& i, float so, int io)
   }
 }
 
+// Tail of one pair: merge chunk partials, output, importance, argmin, insert.
+// s_part: this workgroup's merged partial ([G][D + 2], used when nchunk == 1);
+// s_tail: scratch of Shape::kTailFloats floats.
 template <class T, int D, int G>
-__global__ __launch_bounds__(kThreads) void lf_step_kernel(StepArgs a) {
+__device__ void pair_tail(const StepArgs& a, int pair, const QReg<T, G>& q, float post_scale, const float* s_part,
+                          float* s_tail) {
   using S = Shape<T, D, G>;
-  constexpr int EPL = S::kEpl, LPR = S::kLpr, RPL = S::kRpl, U = S::kU;
+  constexpr int EPL = S::kEpl, LPR = S::kLpr;
   using elem = typename T::elem;
-  __shared__ float smem[S::kSmemFloats];
-  __shared__ int s_last;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int r = lane / LPR, c = lane % LPR;
-  const WorkItem it = a.items[blockIdx.x];
-  const int pair = it.pair;
-  const int b = pair / a.n_kv_heads, g = pair - b * a.n_kv_heads;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = lane % LPR;
   PairMeta* meta = a.meta + pair;
-  const int len = meta->len;
-  const int budget = meta->budget;
-  const int slot0 = meta->slot0;
-
-  // q of the group's heads, this lane's EPL dimensions, in the log2 domain.
-  float q2[G][EPL];
-  {
-    const elem* qb = static_cast<const elem*>(a.q) + ((size_t)b * a.n_q_heads + (size_t)g * G) * D + c * EPL;
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float x[EPL];
-      unpack<T>(*reinterpret_cast<const uint4*>(qb + h * D), x);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) q2[h][e] = x[e] * a.scale_log2;
-    }
-  }
-
+  const int b = pair / a.n_kv_heads, g = pair - b * a.n_kv_heads;
+  const int t = meta->t, len = meta->len, budget = meta->budget;
+  const int nchunk = meta->nchunk, item0 = meta->item0, lstride = meta->lstride;
   const size_t pair_off = (size_t)pair * a.max_budget * D;
-  const elem* Kp = static_cast<const elem*>(a.k_cache) + pair_off + c * EPL;
-  const elem* Vp = static_cast<const elem*>(a.v_cache) + pair_off + c * EPL;
-  float* lg = a.logits + (size_t)slot0 * G;  // [G][budget]
-  float* vn = a.vnorm + slot0;               // [budget]
 
-  float m[G], l[G], acc[G][EPL];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = kNegBig;
-    l[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
-  }
+  float* s_w = s_tail;                                               // [kMaxChunks][G] chunk weights
+  float* s_red = s_w + kMaxChunks * G;                               // [2][kWaves][G]
+  uint32_t* s_bits = reinterpret_cast<uint32_t*>(s_red + 2 * kWaves * G);  // protected slots
+  float* s_arg = reinterpret_cast<float*>(s_bits + kMaxBudget / 32);       // [kWaves] score, [kWaves] slot
 
-  const int row_end = min(it.start + it.count, len);
-  for (int tb = it.start; tb < row_end; tb += S::kTile) {
-    uint4 kr[U], vr[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int row = tb + (wave * U + u) * RPL + r;
-      if (row < row_end) {
-        kr[u] = *reinterpret_cast<const uint4*>(Kp + (size_t)row * D);
-        vr[u] = *reinterpret_cast<const uint4*>(Vp + (size_t)row * D);
-      } else {
-        kr[u] = make_uint4(0, 0, 0, 0);
-        vr[u] = make_uint4(0, 0, 0, 0);
-      }
-    }
-    // S = q K^T for the tile (log2 domain); masked rows get -inf.
-    float s[U][G];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int row = tb + (wave * U + u) * RPL + r;
-      float kx[EPL];
-      unpack<T>(kr[u], kx);
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float p = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) p = fmaf(q2[h][e], kx[e], p);
-        s[u][h] = row_sum<LPR>(p);
-      }
-      if (row < row_end) {
-        if (c < G) {
-          float mine = s[u][0];
-#pragma unroll
-          for (int h = 1; h < G; ++h) mine = c == h ? s[u][h] : mine;
-          lg[(size_t)c * budget + row] = mine;
-        }
-      } else {
-#pragma unroll
-        for (int h = 0; h < G; ++h) s[u][h] = -INFINITY;
-      }
-    }
-    if (a.vl1) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int row = tb + (wave * U + u) * RPL + r;
-        float vx[EPL];
-        unpack<T>(vr[u], vx);
-        float n1 = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) n1 += fabsf(vx[e]);
-        n1 = row_sum<LPR>(n1);
-        if (c == 0 && row < row_end) vn[row] = n1;
-      }
-    }
-    // Online softmax: rescale once per tile, then accumulate P V.
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float mt = s[0][h];
-#pragma unroll
-      for (int u = 1; u < U; ++u) mt = fmaxf(mt, s[u][h]);
-      const float mn = fmaxf(m[h], mt);
-      const float corr = fast_exp2(m[h] - mn);
-      m[h] = mn;
-      l[h] *= corr;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[h][e] *= corr;
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float vx[EPL];
-      unpack<T>(vr[u], vx);
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float p = fast_exp2(s[u][h] - m[h]);
-        l[h] += p;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(p, vx[e], acc[h][e]);
-      }
-    }
-  }
-
-  // Merge the RPL row lineages of the wave (lanes c, c + LPR, ...).
-#pragma unroll
-  for (int off = LPR; off < 64; off <<= 1) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float mo = __shfl_xor(m[h], off);
-      const float lo = __shfl_xor(l[h], off);
-      const float mn = fmaxf(m[h], mo);
-      const float fa = fast_exp2(m[h] - mn), fb = fast_exp2(mo - mn);
-      l[h] = l[h] * fa + lo * fb;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        const float ao = __shfl_xor(acc[h][e], off);
-        acc[h][e] = acc[h][e] * fa + ao * fb;
-      }
-      m[h] = mn;
-    }
-  }
-  // Merge the waves through LDS and write this chunk's partial.
-  if (r == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float* dst = smem + (wave * G + h) * (D + 2);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) dst[c * EPL + e] = acc[h][e];
-      if (c == 0) {
-        dst[D] = m[h];
-        dst[D + 1] = l[h];
-      }
-    }
-  }
-  __syncthreads();
-  const size_t item = blockIdx.x;
-  for (int idx = tid; idx < G * D; idx += kThreads) {
-    const int h = idx / D, dim = idx - h * D;
-    float mm = kNegBig;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) mm = fmaxf(mm, smem[(w * G + h) * (D + 2) + D]);
-    float sa = 0.f, sl = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float* src = smem + (w * G + h) * (D + 2);
-      const float f = fast_exp2(src[D] - mm);
-      sa += src[dim] * f;
-      sl += src[D + 1] * f;
-    }
-    a.part_acc[(item * G + h) * D + dim] = sa;
-    if (dim == 0) {
-      a.part_ml[(item * G + h) * 2] = mm;
-      a.part_ml[(item * G + h) * 2 + 1] = sl;
-    }
-  }
-
-  // Ticket: the last chunk of the pair to finish runs the tail.
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const unsigned prev = atomicAdd(&meta->ticket, 1u);
-    s_last = prev + 1 == static_cast<unsigned>(meta->nchunk);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-
-  // ---------------------------------------------------------------- tail
-  const int t = meta->t;
-  const int nchunk = meta->nchunk, item0 = meta->item0;
-  float* s_w = smem;                              // [kMaxChunks][G] chunk weights exp2(m_c - M)
-  float* s_redm = s_w + kMaxChunks * G;           // [kWaves][G]
-  float* s_reds = s_redm + kWaves * G;            // [kWaves][G]
-  float* s_ML = s_reds + kWaves * G;              // M[G], 1/L[G], exp2(s_new - M)[G]
-  uint32_t* s_bits = reinterpret_cast<uint32_t*>(s_ML + 3 * G);  // protected-slot bitmap
-  float* s_arg = reinterpret_cast<float*>(s_bits + kMaxBudget / 32);  // [kWaves] score, [kWaves] slot
+  const int nwords = (budget + 31) >> 5;
+  for (int i = tid; i < nwords; i += kThreads) s_bits[i] = 0u;
 
   // Logit of the incoming token (every row lineage computes the same value).
   float snew[G];
   {
-    const elem* knp = static_cast<const elem*>(a.k_new) + (size_t)pair * D + c * EPL;
-    float kx[EPL];
-    unpack<T>(*reinterpret_cast<const uint4*>(knp), kx);
+    const uint4 kn = *reinterpret_cast<const uint4*>(static_cast<const elem*>(a.k_new) + (size_t)pair * D + c * EPL);
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float p = 0.f;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) p = fmaf(q2[h][e], kx[e], p);
-      snew[h] = row_sum<LPR>(p);
-    }
+    for (int h = 0; h < G; ++h) snew[h] = row_sum<LPR>(qk_part<T, G>(q, h, kn)) * post_scale;
   }
-  // Global max over chunks and the new token.
+  // Chunk maxima and sums: one chunk per thread.
   float mc[G], lc[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     mc[h] = kNegBig;
     lc[h] = 0.f;
   }
-  if (tid < nchunk) {
-    const float* src = a.part_ml + (size_t)(item0 + tid) * G * 2;
+  if (nchunk == 1) {
+    if (tid == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        mc[h] = s_part[h * (D + 2) + D];
+        lc[h] = s_part[h * (D + 2) + D + 1];
+      }
+    }
+  } else if (tid < nchunk) {
+    const float2* src = reinterpret_cast<const float2*>(a.part_ml) + (size_t)(item0 + tid) * G;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      mc[h] = src[2 * h];
-      lc[h] = src[2 * h + 1];
+      const float2 v = src[h];
+      mc[h] = v.x;
+      lc[h] = v.y;
     }
   }
 #pragma unroll
@@ -375,89 +259,119 @@ __global__ __launch_bounds__(kThreads) void lf_step_kernel(StepArgs a) {
     float x = mc[h];
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
-    if (lane == 0) s_redm[wave * G + h] = x;
+    if (lane == 0) s_red[wave * G + h] = x;
   }
-  __syncthreads();
+  __syncthreads();  // bitmap zeroed, per-wave maxima visible
+  {
+    const int R = a.recent;
+    const int32_t* ring = a.ring + (size_t)pair * R;
+    for (int j = tid; j < R; j += kThreads) {
+      const int sl = ring[j];
+      if (sl >= 0 && sl < budget) atomicOr(&s_bits[sl >> 5], 1u << (sl & 31));
+    }
+  }
   float M[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     float x = snew[h];
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) x = fmaxf(x, s_redm[w * G + h]);
+    for (int w = 0; w < kWaves; ++w) x = fmaxf(x, s_red[w * G + h]);
     M[h] = x;
-  }
-  // Chunk weights and the normaliser.
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
     const float wgt = fast_exp2(mc[h] - M[h]);
     if (tid < nchunk) s_w[tid * G + h] = wgt;
-    float x = lc[h] * wgt;
+    float y = lc[h] * wgt;
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
-    if (lane == 0) s_reds[wave * G + h] = x;
+    for (int off = 32; off > 0; off >>= 1) y += __shfl_xor(y, off);
+    if (lane == 0) s_red[(kWaves + wave) * G + h] = y;
   }
-  __syncthreads();
-  float invL[G];
+  __syncthreads();  // chunk weights, per-wave sums and the bitmap complete
+  float invL[G], en[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const float en = fast_exp2(snew[h] - M[h]);
-    float L = en;
+    en[h] = fast_exp2(snew[h] - M[h]);
+    float L = en[h];
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) L += s_reds[w * G + h];
+    for (int w = 0; w < kWaves; ++w) L += s_red[(kWaves + w) * G + h];
     invL[h] = 1.0f / L;
-    if (tid == 0) {
-      s_ML[h] = M[h];
-      s_ML[G + h] = invL[h];
-      s_ML[2 * G + h] = en;
-      if (a.dbg_lse)
-        a.dbg_lse[(size_t)b * a.n_q_heads + g * G + h] = (M[h] + __log2f(L)) * 0.6931471805599453f;
-    }
+    if (tid == 0 && a.dbg_lse)
+      a.dbg_lse[(size_t)b * a.n_q_heads + g * G + h] = (M[h] + __log2f(L)) * 0.6931471805599453f;
   }
-  // Protected-slot bitmap from the ring of recent slots (the sink is an index test).
-  const int nwords = (budget + 31) >> 5;
-  for (int i = tid; i < nwords; i += kThreads) s_bits[i] = 0u;
-  __syncthreads();
-  const int R = a.recent;
-  const int32_t* ring = a.ring + (size_t)pair * R;
-  for (int j = tid; j < R; j += kThreads) {
-    const int sl = ring[j];
-    if (sl >= 0 && sl < budget) atomicOr(&s_bits[sl >> 5], 1u << (sl & 31));
-  }
-  // Output: merge chunk partials in chunk order, add the new token, normalise.
+
+  // Output: chunk partials in chunk order + the new token, normalised.
   {
     const elem* vnp = static_cast<const elem*>(a.v_new) + (size_t)pair * D;
     const float* pacc = a.part_acc + (size_t)item0 * G * D;
     for (int idx = tid; idx < G * D; idx += kThreads) {
       const int h = idx / D, dim = idx - h * D;
-      float o = s_ML[2 * G + h] * load_elem<T>(vnp, dim);
-      int ci = 0;
-      for (; ci + 8 <= nchunk; ci += 8) {
-        float x[8];
+      float enh = en[0], il = invL[0];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) x[k] = pacc[(size_t)(ci + k) * G * D + idx];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) o = fmaf(x[k], s_w[(ci + k) * G + h], o);
+      for (int hh = 1; hh < G; ++hh) {
+        enh = h == hh ? en[hh] : enh;
+        il = h == hh ? invL[hh] : il;
       }
-      for (; ci < nchunk; ++ci) o = fmaf(pacc[(size_t)ci * G * D + idx], s_w[ci * G + h], o);
-      store_elem<T>(a.out, ((size_t)b * a.n_q_heads + g * G + h) * D + dim, o * s_ML[G + h]);
+      float o = enh * load_elem<T>(vnp, dim);
+      if (nchunk == 1) {
+        o = fmaf(s_part[h * (D + 2) + dim], s_w[h], o);
+      } else {
+        int ci = 0;
+        for (; ci + 16 <= nchunk; ci += 16) {
+          float x[16];
+#pragma unroll
+          for (int k = 0; k < 16; ++k) x[k] = pacc[(size_t)(ci + k) * G * D + idx];
+#pragma unroll
+          for (int k = 0; k < 16; ++k) o = fmaf(x[k], s_w[(ci + k) * G + h], o);
+        }
+        if (ci < nchunk) {
+          float x[16];
+#pragma unroll
+          for (int k = 0; k < 16; ++k) x[k] = ci + k < nchunk ? pacc[(size_t)(ci + k) * G * D + idx] : 0.f;
+#pragma unroll
+          for (int k = 0; k < 16; ++k)
+            if (ci + k < nchunk) o = fmaf(x[k], s_w[(ci + k) * G + h], o);
+        }
+      }
+      store_elem<T>(a.out, ((size_t)b * a.n_q_heads + g * G + h) * D + dim, o * il);
     }
   }
-  __syncthreads();
-  // Importance of every filled slot and the masked argmin.
+
+  // Importance of every filled slot and the masked first-index argmin.
   float best = INFINITY;
   int besti = 0x7FFFFFFF;
   {
+    const float* lg = a.logits + (size_t)meta->slot0 * G;  // [G][lstride]
+    const float* vn = a.vnorm + meta->slot0;                // [lstride]
     float* dbg = a.dbg_scores ? a.dbg_scores + (size_t)pair * a.max_budget : nullptr;
-    for (int i = tid; i < len; i += kThreads) {
-      float sc = 0.f;
+#pragma unroll 2
+    for (int base = 4 * tid; base < len; base += 4 * kThreads) {
+      float4 lv[G];
 #pragma unroll
-      for (int h = 0; h < G; ++h) sc = fmaf(fast_exp2(lg[(size_t)h * budget + i] - M[h]), invL[h], sc);
-      if (a.vl1) sc *= vn[i];
-      if (dbg) dbg[i] = sc;
-      const bool prot = i < a.sink || ((s_bits[i >> 5] >> (i & 31)) & 1u);
-      if (!prot && sc < best) {  // i increases per thread: first index kept on ties
-        best = sc;
-        besti = i;
+      for (int h = 0; h < G; ++h) lv[h] = *reinterpret_cast<const float4*>(lg + (size_t)h * lstride + base);
+      float4 v1 = make_float4(1.f, 1.f, 1.f, 1.f);
+      if (a.vl1) v1 = *reinterpret_cast<const float4*>(vn + base);
+      const uint32_t bits = s_bits[base >> 5] >> (base & 31);
+      float sc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        sc[0] = fmaf(fast_exp2(lv[h].x - M[h]), invL[h], sc[0]);
+        sc[1] = fmaf(fast_exp2(lv[h].y - M[h]), invL[h], sc[1]);
+        sc[2] = fmaf(fast_exp2(lv[h].z - M[h]), invL[h], sc[2]);
+        sc[3] = fmaf(fast_exp2(lv[h].w - M[h]), invL[h], sc[3]);
+      }
+      sc[0] *= v1.x;
+      sc[1] *= v1.y;
+      sc[2] *= v1.z;
+      sc[3] *= v1.w;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = base + j;
+        if (i < len) {
+          if (dbg) dbg[i] = sc[j];
+          const bool prot = i < a.sink || ((bits >> j) & 1u);
+          if (!prot && sc[j] < best) {  // i increases per thread: first index kept on ties
+            best = sc[j];
+            besti = i;
+          }
+        }
       }
     }
   }
@@ -500,13 +414,223 @@ __global__ __launch_bounds__(kThreads) void lf_step_kernel(StepArgs a) {
   }
   if (tid == 0) {
     if (e >= 0) {
-      if (R > 0) a.ring[(size_t)pair * R + (t % R)] = e;
+      if (a.recent > 0) a.ring[(size_t)pair * a.recent + (t % a.recent)] = e;
       meta->t = t + 1;
       meta->len = len < budget ? len + 1 : budget;
     }
     a.evict_idx[pair] = ev;
     meta->ticket = 0u;
   }
+}
+
+template <class T, int D, int G>
+__global__ __launch_bounds__(kThreads) void lf_step_kernel(StepArgs a) {
+  using S = Shape<T, D, G>;
+  constexpr int EPL = S::kEpl, LPR = S::kLpr, RPL = S::kRpl, U = S::kU, TILE = S::kTile;
+  using elem = typename T::elem;
+  __shared__ float smem[S::kSmemFloats];
+  __shared__ int s_last;
+  float* s_part = smem;                   // [G][D + 2]: merged partial of this chunk
+  float* s_work = smem + S::kPartFloats;  // cross-wave merge, then tail scratch
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int r = lane / LPR, c = lane % LPR;
+  const WorkItem it = a.items[blockIdx.x];
+  const int pair = it.pair;
+  const int b = pair / a.n_kv_heads, g = pair - b * a.n_kv_heads;
+  PairMeta* meta = a.meta + pair;
+  const int len = meta->len;
+  const int lstride = meta->lstride;
+  const int nchunk = meta->nchunk;
+
+  QReg<T, G> q;
+  load_q<T, G>(q, static_cast<const elem*>(a.q) + ((size_t)b * a.n_q_heads + (size_t)g * G) * D + c * EPL, D,
+               a.scale_log2);
+  const float post_scale = T::kEpl == 8 ? a.scale_log2 : 1.0f;
+
+  const size_t pair_off = (size_t)pair * a.max_budget * D;
+  const elem* Kp = static_cast<const elem*>(a.k_cache) + pair_off + c * EPL;
+  const elem* Vp = static_cast<const elem*>(a.v_cache) + pair_off + c * EPL;
+  float* lg = a.logits + (size_t)meta->slot0 * G;  // [G][lstride]
+  float* vn = a.vnorm + meta->slot0;                // [lstride]
+
+  float m[G], l[G], acc[G][EPL];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = kNegBig;
+    l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+  }
+
+  const int row_end = min(it.start + it.count, len);
+  const int lane_row = wave * U * RPL + r;  // row of load u = 0 within a tile
+
+  auto load_tile = [&](int tb, uint4(&kk)[U], uint4(&vv)[U]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int row = tb + lane_row + u * RPL;
+      if (row < row_end) {
+        kk[u] = *reinterpret_cast<const uint4*>(Kp + (size_t)row * D);
+        vv[u] = *reinterpret_cast<const uint4*>(Vp + (size_t)row * D);
+      } else {
+        kk[u] = make_uint4(0, 0, 0, 0);
+        vv[u] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+
+  auto process_tile = [&](int tb, const uint4(&kk)[U], const uint4(&vv)[U]) {
+    float s[U][G];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int row = tb + lane_row + u * RPL;
+#pragma unroll
+      for (int h = 0; h < G; ++h) s[u][h] = row_sum<LPR>(qk_part<T, G>(q, h, kk[u])) * post_scale;
+      if (row < row_end) {
+        if (c < G) {
+          float mine = s[u][0];
+#pragma unroll
+          for (int h = 1; h < G; ++h) mine = c == h ? s[u][h] : mine;
+          lg[(size_t)c * lstride + row] = mine;
+        }
+      } else {
+#pragma unroll
+        for (int h = 0; h < G; ++h) s[u][h] = -INFINITY;
+      }
+    }
+    if (a.vl1) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int row = tb + lane_row + u * RPL;
+        float vx[EPL];
+        unpack<T>(vv[u], vx);
+        float n1 = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) n1 += fabsf(vx[e]);
+        n1 = row_sum<LPR>(n1);
+        if (c == 0 && row < row_end) vn[row] = n1;
+      }
+    }
+    // Online softmax: rescale once per tile, then accumulate P V.
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float mt = s[0][h];
+#pragma unroll
+      for (int u = 1; u < U; ++u) mt = fmaxf(mt, s[u][h]);
+      const float mn = fmaxf(m[h], mt);
+      const float corr = fast_exp2(m[h] - mn);
+      m[h] = mn;
+      l[h] *= corr;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[h][e] *= corr;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float vx[EPL];
+      unpack<T>(vv[u], vx);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float p = fast_exp2(s[u][h] - m[h]);
+        l[h] += p;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(p, vx[e], acc[h][e]);
+      }
+    }
+  };
+
+  // Software pipeline over tiles: tile t + 1 loads while tile t computes.
+  {
+    uint4 ka[U], va[U], kb[U], vb[U];
+    int tb = it.start;
+    if (tb < row_end) load_tile(tb, ka, va);
+    while (tb < row_end) {
+      const int t1 = tb + TILE;
+      if (t1 < row_end) load_tile(t1, kb, vb);
+      process_tile(tb, ka, va);
+      if (t1 >= row_end) break;
+      const int t2 = t1 + TILE;
+      if (t2 < row_end) load_tile(t2, ka, va);
+      process_tile(t1, kb, vb);
+      tb = t2;
+    }
+  }
+
+  // Merge the RPL row lineages of the wave (lanes c, c + LPR, ...).
+#pragma unroll
+  for (int off = LPR; off < 64; off <<= 1) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float mo = __shfl_xor(m[h], off);
+      const float lo = __shfl_xor(l[h], off);
+      const float mn = fmaxf(m[h], mo);
+      const float fa = fast_exp2(m[h] - mn), fb = fast_exp2(mo - mn);
+      l[h] = l[h] * fa + lo * fb;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const float ao = __shfl_xor(acc[h][e], off);
+        acc[h][e] = acc[h][e] * fa + ao * fb;
+      }
+      m[h] = mn;
+    }
+  }
+  // Merge the waves through LDS into this chunk's partial.
+  if (r == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float* dst = s_work + (wave * G + h) * (D + 2);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) dst[c * EPL + e] = acc[h][e];
+      if (c == 0) {
+        dst[D] = m[h];
+        dst[D + 1] = l[h];
+      }
+    }
+  }
+  __syncthreads();
+  const size_t item = blockIdx.x;
+  for (int idx = tid; idx < G * D; idx += kThreads) {
+    const int h = idx / D, dim = idx - h * D;
+    float mm = kNegBig;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) mm = fmaxf(mm, s_work[(w * G + h) * (D + 2) + D]);
+    float sa = 0.f, sl = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float* src = s_work + (w * G + h) * (D + 2);
+      const float f = fast_exp2(src[D] - mm);
+      sa += src[dim] * f;
+      sl += src[D + 1] * f;
+    }
+    if (nchunk == 1) {
+      s_part[h * (D + 2) + dim] = sa;
+      if (dim == 0) {
+        s_part[h * (D + 2) + D] = mm;
+        s_part[h * (D + 2) + D + 1] = sl;
+      }
+    } else {
+      a.part_acc[(item * G + h) * D + dim] = sa;
+      if (dim == 0) reinterpret_cast<float2*>(a.part_ml)[item * G + h] = make_float2(mm, sl);
+    }
+  }
+  __syncthreads();
+
+  if (nchunk > 1) {
+    // Ticket: the barrier orders every wave's partial stores before thread 0's
+    // agent-scope release RMW (one L2 write-back per workgroup); only the last
+    // arrival pays for the acquire before reading the other chunks' partials.
+    if (tid == 0) {
+      const unsigned prev = __hip_atomic_fetch_add(&meta->ticket, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      const bool last = prev + 1 == static_cast<unsigned>(nchunk);
+      if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      s_last = last;
+    }
+    __syncthreads();
+    if (!s_last) return;
+  }
+  (void)lstride;
+  pair_tail<T, D, G>(a, pair, q, post_scale, s_part, s_work);
 }
 
 template <class T, int D, int G>
