@@ -27,6 +27,9 @@ HIP_FLAGS = [
     "-fPIC",
     "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: the online-softmax rescale touches them with
+    # VALU ops, and AGPR homes would cost a copy per row group.
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"),
 ]
 

@@ -15,7 +15,7 @@ constexpr int kMaxGroup = 8;
 constexpr int kThreads = 256;      // threads per workgroup (4 wave64)
 constexpr size_t kAlign = 256;
 constexpr int kSlotPad = 64;        // per-pair workspace rows are padded to this many slots
-constexpr int kTargetItems = 512;   // split pairs into chunks until about this many work items
+constexpr int kTargetItems = 256;   // split pairs into chunks until about this many work items
 
 // Per (sequence, KV head) pair.  Written by lf_init_cache, updated in place by
 // the last-arriving workgroup of the pair at the end of every step.

@@ -41,6 +41,7 @@
 
 #include <cstdint>
 #include <cstdio>
+#include <type_traits>
 
 #include "lf_internal.h"
 
@@ -67,13 +68,17 @@ struct Shape {
   static constexpr int kLpr = D / kEpl;   // lanes per row
   static constexpr int kRpl = 64 / kLpr;  // rows per wave load
   static constexpr int kU = 4;            // row loads per lane per tile per tensor (double-buffered)
-  static constexpr int kTile = kWaves * kRpl * kU;
+  static constexpr int kTile = kEpl == 8 ? 16 * kWaves : kWaves * kRpl * kU;
   // LDS: merged chunk partial [G][D + 2] kept for the tail, then a region used
   // first for the cross-wave merge [wave][G][D + 2] and later by the tail.
   static constexpr int kPartFloats = G * (D + 2);
   static constexpr int kMergeFloats = kWaves * G * (D + 2);
   static constexpr int kTailFloats = kMaxChunks * G + 2 * kWaves * G + kMaxBudget / 32 + 2 * kWaves;
-  static constexpr int kSmemFloats = kPartFloats + (kMergeFloats > kTailFloats ? kMergeFloats : kTailFloats);
+  // bf16: per-wave tile of 16 value rows, rows padded by 32 bytes against LDS bank conflicts.
+  static constexpr int kStageRowBytes = D * 2 + 32;
+  static constexpr int kStageFloats = kEpl == 8 ? kWaves * 16 * kStageRowBytes / 4 : 0;
+  static constexpr int kStreamFloats = kMergeFloats + kStageFloats;
+  static constexpr int kSmemFloats = kPartFloats + (kStreamFloats > kTailFloats ? kStreamFloats : kTailFloats);
 };
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -200,58 +205,84 @@ __device__ __forceinline__ void argmin_merge(float& s, int& i, float so, int io)
 }
 
 // Tail of one pair: merge chunk partials, output, importance, argmin, insert.
+// Every load that does not depend on the merged statistics (chunk maxima and
+// sums, the ring, the chunk partials, the first logits, the new token) is
+// issued before the first barrier, so the tail costs about one memory round
+// trip plus arithmetic.
 // s_part: this workgroup's merged partial ([G][D + 2], used when nchunk == 1);
 // s_tail: scratch of Shape::kTailFloats floats.
 template <class T, int D, int G>
-__device__ void pair_tail(const StepArgs& a, int pair, const QReg<T, G>& q, float post_scale, const float* s_part,
-                          float* s_tail) {
-  using S = Shape<T, D, G>;
-  constexpr int EPL = S::kEpl, LPR = S::kLpr;
+__device__ void pair_tail(const StepArgs& a, int pair, const float (&snew)[G], const float* s_part, float* s_tail) {
   using elem = typename T::elem;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = lane % LPR;
+  constexpr int kOut = (G * D + kThreads - 1) / kThreads;  // output elements per thread
+  constexpr int kCB = G <= 4 ? 8 : 4;                       // chunk partials loaded per batch
+  constexpr int kVec = D * sizeof(elem) / 16;               // 16-byte pieces of one K/V row
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   PairMeta* meta = a.meta + pair;
   const int b = pair / a.n_kv_heads, g = pair - b * a.n_kv_heads;
   const int t = meta->t, len = meta->len, budget = meta->budget;
   const int nchunk = meta->nchunk, item0 = meta->item0, lstride = meta->lstride;
+  const int R = a.recent;
+  const bool split = nchunk > 1;
   const size_t pair_off = (size_t)pair * a.max_budget * D;
 
-  float* s_w = s_tail;                                               // [kMaxChunks][G] chunk weights
-  float* s_red = s_w + kMaxChunks * G;                               // [2][kWaves][G]
+  float* s_w = s_tail;                                                     // [kMaxChunks][G] chunk weights
+  float* s_red = s_w + kMaxChunks * G;                                     // [2][kWaves][G]
   uint32_t* s_bits = reinterpret_cast<uint32_t*>(s_red + 2 * kWaves * G);  // protected slots
   float* s_arg = reinterpret_cast<float*>(s_bits + kMaxBudget / 32);       // [kWaves] score, [kWaves] slot
 
-  const int nwords = (budget + 31) >> 5;
-  for (int i = tid; i < nwords; i += kThreads) s_bits[i] = 0u;
-
-  // Logit of the incoming token (every row lineage computes the same value).
-  float snew[G];
-  {
-    const uint4 kn = *reinterpret_cast<const uint4*>(static_cast<const elem*>(a.k_new) + (size_t)pair * D + c * EPL);
-#pragma unroll
-    for (int h = 0; h < G; ++h) snew[h] = row_sum<LPR>(qk_part<T, G>(q, h, kn)) * post_scale;
-  }
-  // Chunk maxima and sums: one chunk per thread.
+  // ---- loads that depend on nothing computed here
   float mc[G], lc[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     mc[h] = kNegBig;
     lc[h] = 0.f;
   }
-  if (nchunk == 1) {
-    if (tid == 0) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        mc[h] = s_part[h * (D + 2) + D];
-        lc[h] = s_part[h * (D + 2) + D + 1];
-      }
-    }
-  } else if (tid < nchunk) {
+  if (split && tid < nchunk) {
     const float2* src = reinterpret_cast<const float2*>(a.part_ml) + (size_t)(item0 + tid) * G;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float2 v = src[h];
       mc[h] = v.x;
       lc[h] = v.y;
+    }
+  }
+  const int32_t* ring = a.ring + (size_t)pair * R;
+  const int ring_sl = tid < R ? ring[tid] : -1;
+  uint4 ins = make_uint4(0, 0, 0, 0);
+  if (tid < 2 * kVec) {
+    const int which = tid / kVec, part = tid - which * kVec;
+    ins = reinterpret_cast<const uint4*>(static_cast<const elem*>(which ? a.v_new : a.k_new) + (size_t)pair * D)[part];
+  }
+  const elem* vnp = static_cast<const elem*>(a.v_new) + (size_t)pair * D;
+  const float* pacc = a.part_acc + (size_t)item0 * G * D;
+  float vnv[kOut], pa[kOut][kCB];
+#pragma unroll
+  for (int o = 0; o < kOut; ++o) {
+    const int idx = tid + o * kThreads;
+    const bool ok = idx < G * D;
+    vnv[o] = ok ? load_elem<T>(vnp, idx % D) : 0.f;
+#pragma unroll
+    for (int k = 0; k < kCB; ++k) pa[o][k] = (split && ok && k < nchunk) ? pacc[(size_t)k * G * D + idx] : 0.f;
+  }
+  const float* lg = a.logits + (size_t)meta->slot0 * G;  // [G][lstride]
+  const float* vn = a.vnorm + meta->slot0;                // [lstride]
+  float4 lv0[G];
+  float4 v10 = make_float4(1.f, 1.f, 1.f, 1.f);
+  if (4 * tid < len) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) lv0[h] = *reinterpret_cast<const float4*>(lg + (size_t)h * lstride + 4 * tid);
+    if (a.vl1) v10 = *reinterpret_cast<const float4*>(vn + 4 * tid);
+  }
+
+  // ---- global max and normaliser over the chunks and the incoming token
+  const int nwords = (budget + 31) >> 5;
+  for (int i = tid; i < nwords; i += kThreads) s_bits[i] = 0u;
+  if (!split && tid == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      mc[h] = s_part[h * (D + 2) + D];
+      lc[h] = s_part[h * (D + 2) + D + 1];
     }
   }
 #pragma unroll
@@ -262,13 +293,10 @@ __device__ void pair_tail(const StepArgs& a, int pair, const QReg<T, G>& q, floa
     if (lane == 0) s_red[wave * G + h] = x;
   }
   __syncthreads();  // bitmap zeroed, per-wave maxima visible
-  {
-    const int R = a.recent;
-    const int32_t* ring = a.ring + (size_t)pair * R;
-    for (int j = tid; j < R; j += kThreads) {
-      const int sl = ring[j];
-      if (sl >= 0 && sl < budget) atomicOr(&s_bits[sl >> 5], 1u << (sl & 31));
-    }
+  if (ring_sl >= 0 && ring_sl < budget) atomicOr(&s_bits[ring_sl >> 5], 1u << (ring_sl & 31));
+  for (int j = tid + kThreads; j < R; j += kThreads) {
+    const int sl = ring[j];
+    if (sl >= 0 && sl < budget) atomicOr(&s_bits[sl >> 5], 1u << (sl & 31));
   }
   float M[G];
 #pragma unroll
@@ -297,83 +325,78 @@ __device__ void pair_tail(const StepArgs& a, int pair, const QReg<T, G>& q, floa
       a.dbg_lse[(size_t)b * a.n_q_heads + g * G + h] = (M[h] + __log2f(L)) * 0.6931471805599453f;
   }
 
-  // Output: chunk partials in chunk order + the new token, normalised.
-  {
-    const elem* vnp = static_cast<const elem*>(a.v_new) + (size_t)pair * D;
-    const float* pacc = a.part_acc + (size_t)item0 * G * D;
-    for (int idx = tid; idx < G * D; idx += kThreads) {
-      const int h = idx / D, dim = idx - h * D;
+  // ---- output: chunk partials in chunk order + the new token, normalised
+#pragma unroll
+  for (int o = 0; o < kOut; ++o) {
+    const int idx = tid + o * kThreads;
+    if (idx < G * D) {
+      const int h = idx / D;
       float enh = en[0], il = invL[0];
 #pragma unroll
       for (int hh = 1; hh < G; ++hh) {
         enh = h == hh ? en[hh] : enh;
         il = h == hh ? invL[hh] : il;
       }
-      float o = enh * load_elem<T>(vnp, dim);
-      if (nchunk == 1) {
-        o = fmaf(s_part[h * (D + 2) + dim], s_w[h], o);
+      float acc = enh * vnv[o];
+      if (!split) {
+        acc = fmaf(s_part[h * (D + 2) + idx - h * D], s_w[h], acc);
       } else {
-        int ci = 0;
-        for (; ci + 16 <= nchunk; ci += 16) {
-          float x[16];
 #pragma unroll
-          for (int k = 0; k < 16; ++k) x[k] = pacc[(size_t)(ci + k) * G * D + idx];
+        for (int k = 0; k < kCB; ++k)
+          if (k < nchunk) acc = fmaf(pa[o][k], s_w[k * G + h], acc);
+        for (int ci = kCB; ci < nchunk; ci += kCB) {
+          float x[kCB];
 #pragma unroll
-          for (int k = 0; k < 16; ++k) o = fmaf(x[k], s_w[(ci + k) * G + h], o);
-        }
-        if (ci < nchunk) {
-          float x[16];
+          for (int k = 0; k < kCB; ++k) x[k] = ci + k < nchunk ? pacc[(size_t)(ci + k) * G * D + idx] : 0.f;
 #pragma unroll
-          for (int k = 0; k < 16; ++k) x[k] = ci + k < nchunk ? pacc[(size_t)(ci + k) * G * D + idx] : 0.f;
-#pragma unroll
-          for (int k = 0; k < 16; ++k)
-            if (ci + k < nchunk) o = fmaf(x[k], s_w[(ci + k) * G + h], o);
+          for (int k = 0; k < kCB; ++k)
+            if (ci + k < nchunk) acc = fmaf(x[k], s_w[(ci + k) * G + h], acc);
         }
       }
-      store_elem<T>(a.out, ((size_t)b * a.n_q_heads + g * G + h) * D + dim, o * il);
+      store_elem<T>(a.out, ((size_t)b * a.n_q_heads + g * G + h) * D + idx - h * D, acc * il);
     }
   }
 
-  // Importance of every filled slot and the masked first-index argmin.
+  // ---- importance of every filled slot and the masked first-index argmin
   float best = INFINITY;
   int besti = 0x7FFFFFFF;
-  {
-    const float* lg = a.logits + (size_t)meta->slot0 * G;  // [G][lstride]
-    const float* vn = a.vnorm + meta->slot0;                // [lstride]
-    float* dbg = a.dbg_scores ? a.dbg_scores + (size_t)pair * a.max_budget : nullptr;
-#pragma unroll 2
-    for (int base = 4 * tid; base < len; base += 4 * kThreads) {
-      float4 lv[G];
+  float* dbg = a.dbg_scores ? a.dbg_scores + (size_t)pair * a.max_budget : nullptr;
+  auto score4 = [&](int base, const float4(&lv)[G], const float4& v1) {
+    const uint32_t bits = s_bits[base >> 5] >> (base & 31);
+    float sc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int h = 0; h < G; ++h) lv[h] = *reinterpret_cast<const float4*>(lg + (size_t)h * lstride + base);
-      float4 v1 = make_float4(1.f, 1.f, 1.f, 1.f);
-      if (a.vl1) v1 = *reinterpret_cast<const float4*>(vn + base);
-      const uint32_t bits = s_bits[base >> 5] >> (base & 31);
-      float sc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int h = 0; h < G; ++h) {
+      sc[0] = fmaf(fast_exp2(lv[h].x - M[h]), invL[h], sc[0]);
+      sc[1] = fmaf(fast_exp2(lv[h].y - M[h]), invL[h], sc[1]);
+      sc[2] = fmaf(fast_exp2(lv[h].z - M[h]), invL[h], sc[2]);
+      sc[3] = fmaf(fast_exp2(lv[h].w - M[h]), invL[h], sc[3]);
+    }
+    sc[0] *= v1.x;
+    sc[1] *= v1.y;
+    sc[2] *= v1.z;
+    sc[3] *= v1.w;
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        sc[0] = fmaf(fast_exp2(lv[h].x - M[h]), invL[h], sc[0]);
-        sc[1] = fmaf(fast_exp2(lv[h].y - M[h]), invL[h], sc[1]);
-        sc[2] = fmaf(fast_exp2(lv[h].z - M[h]), invL[h], sc[2]);
-        sc[3] = fmaf(fast_exp2(lv[h].w - M[h]), invL[h], sc[3]);
-      }
-      sc[0] *= v1.x;
-      sc[1] *= v1.y;
-      sc[2] *= v1.z;
-      sc[3] *= v1.w;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i = base + j;
-        if (i < len) {
-          if (dbg) dbg[i] = sc[j];
-          const bool prot = i < a.sink || ((bits >> j) & 1u);
-          if (!prot && sc[j] < best) {  // i increases per thread: first index kept on ties
-            best = sc[j];
-            besti = i;
-          }
+    for (int j = 0; j < 4; ++j) {
+      const int i = base + j;
+      if (i < len) {
+        if (dbg) dbg[i] = sc[j];
+        const bool prot = i < a.sink || ((bits >> j) & 1u);
+        if (!prot && sc[j] < best) {  // i increases per thread: first index kept on ties
+          best = sc[j];
+          besti = i;
         }
       }
     }
+  };
+  if (4 * tid < len) score4(4 * tid, lv0, v10);
+#pragma unroll 2
+  for (int base = 4 * tid + 4 * kThreads; base < len; base += 4 * kThreads) {
+    float4 lv[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) lv[h] = *reinterpret_cast<const float4*>(lg + (size_t)h * lstride + base);
+    float4 v1 = make_float4(1.f, 1.f, 1.f, 1.f);
+    if (a.vl1) v1 = *reinterpret_cast<const float4*>(vn + base);
+    score4(base, lv, v1);
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
@@ -389,7 +412,7 @@ __device__ void pair_tail(const StepArgs& a, int pair, const QReg<T, G>& q, floa
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) argmin_merge(best, besti, s_arg[w], reinterpret_cast<int*>(s_arg)[kWaves + w]);
 
-  // Insert the incoming token: append while filling, else overwrite the victim.
+  // ---- insert the incoming token: append while filling, else overwrite the victim
   int e, ev;
   if (len < budget) {
     e = len;
@@ -401,20 +424,14 @@ __device__ void pair_tail(const StepArgs& a, int pair, const QReg<T, G>& q, floa
     e = -1;  // no evictable slot (prevented by init-time validation)
     ev = -2;
   }
-  if (e >= 0) {
-    constexpr int kVec = D * sizeof(elem) / 16;
-    if (tid < 2 * kVec) {
-      const int which = tid / kVec, part = tid - which * kVec;
-      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const elem*>(which ? a.v_new : a.k_new) +
-                                                        (size_t)pair * D) + part;
-      uint4* dst = reinterpret_cast<uint4*>(static_cast<elem*>(which ? a.v_cache : a.k_cache) + pair_off +
-                                            (size_t)e * D) + part;
-      *dst = *src;
-    }
+  if (e >= 0 && tid < 2 * kVec) {
+    const int which = tid / kVec, part = tid - which * kVec;
+    reinterpret_cast<uint4*>(static_cast<elem*>(which ? a.v_cache : a.k_cache) + pair_off + (size_t)e * D)[part] =
+        ins;
   }
   if (tid == 0) {
     if (e >= 0) {
-      if (a.recent > 0) a.ring[(size_t)pair * a.recent + (t % a.recent)] = e;
+      if (R > 0) a.ring[(size_t)pair * R + (t % R)] = e;
       meta->t = t + 1;
       meta->len = len < budget ? len + 1 : budget;
     }
@@ -423,37 +440,26 @@ __device__ void pair_tail(const StepArgs& a, int pair, const QReg<T, G>& q, floa
   }
 }
 
+// Streaming of one chunk on the vector ALUs (fp32 cache): 16-byte loads of one
+// row segment per lane, q.k on the lane's segment + DPP row sum, online softmax
+// per row lineage, P.V by FMA.  Leaves the wave's partial (max, sum, weighted
+// value sum per head) in s_merge[wave][G][D + 2].
 template <class T, int D, int G>
-__global__ __launch_bounds__(kThreads) void lf_step_kernel(StepArgs a) {
+__device__ void stream_valu(const StepArgs& a, int pair, int start, int row_end, float* lg, float* vn, int lstride,
+                            float* s_merge) {
   using S = Shape<T, D, G>;
   constexpr int EPL = S::kEpl, LPR = S::kLpr, RPL = S::kRpl, U = S::kU, TILE = S::kTile;
   using elem = typename T::elem;
-  __shared__ float smem[S::kSmemFloats];
-  __shared__ int s_last;
-  float* s_part = smem;                   // [G][D + 2]: merged partial of this chunk
-  float* s_work = smem + S::kPartFloats;  // cross-wave merge, then tail scratch
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane / LPR, c = lane % LPR;
-  const WorkItem it = a.items[blockIdx.x];
-  const int pair = it.pair;
   const int b = pair / a.n_kv_heads, g = pair - b * a.n_kv_heads;
-  PairMeta* meta = a.meta + pair;
-  const int len = meta->len;
-  const int lstride = meta->lstride;
-  const int nchunk = meta->nchunk;
-
   QReg<T, G> q;
   load_q<T, G>(q, static_cast<const elem*>(a.q) + ((size_t)b * a.n_q_heads + (size_t)g * G) * D + c * EPL, D,
                a.scale_log2);
   const float post_scale = T::kEpl == 8 ? a.scale_log2 : 1.0f;
-
   const size_t pair_off = (size_t)pair * a.max_budget * D;
   const elem* Kp = static_cast<const elem*>(a.k_cache) + pair_off + c * EPL;
   const elem* Vp = static_cast<const elem*>(a.v_cache) + pair_off + c * EPL;
-  float* lg = a.logits + (size_t)meta->slot0 * G;  // [G][lstride]
-  float* vn = a.vnorm + meta->slot0;                // [lstride]
 
   float m[G], l[G], acc[G][EPL];
 #pragma unroll
@@ -463,8 +469,6 @@ __global__ __launch_bounds__(kThreads) void lf_step_kernel(StepArgs a) {
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
   }
-
-  const int row_end = min(it.start + it.count, len);
   const int lane_row = wave * U * RPL + r;  // row of load u = 0 within a tile
 
   auto load_tile = [&](int tb, uint4(&kk)[U], uint4(&vv)[U]) {
@@ -480,7 +484,6 @@ __global__ __launch_bounds__(kThreads) void lf_step_kernel(StepArgs a) {
       }
     }
   };
-
   auto process_tile = [&](int tb, const uint4(&kk)[U], const uint4(&vv)[U]) {
     float s[U][G];
 #pragma unroll
@@ -513,7 +516,6 @@ __global__ __launch_bounds__(kThreads) void lf_step_kernel(StepArgs a) {
         if (c == 0 && row < row_end) vn[row] = n1;
       }
     }
-    // Online softmax: rescale once per tile, then accumulate P V.
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float mt = s[0][h];
@@ -539,11 +541,9 @@ __global__ __launch_bounds__(kThreads) void lf_step_kernel(StepArgs a) {
       }
     }
   };
-
-  // Software pipeline over tiles: tile t + 1 loads while tile t computes.
   {
     uint4 ka[U], va[U], kb[U], vb[U];
-    int tb = it.start;
+    int tb = start;
     if (tb < row_end) load_tile(tb, ka, va);
     while (tb < row_end) {
       const int t1 = tb + TILE;
@@ -556,7 +556,6 @@ __global__ __launch_bounds__(kThreads) void lf_step_kernel(StepArgs a) {
       tb = t2;
     }
   }
-
   // Merge the RPL row lineages of the wave (lanes c, c + LPR, ...).
 #pragma unroll
   for (int off = LPR; off < 64; off <<= 1) {
@@ -575,11 +574,10 @@ __global__ __launch_bounds__(kThreads) void lf_step_kernel(StepArgs a) {
       m[h] = mn;
     }
   }
-  // Merge the waves through LDS into this chunk's partial.
   if (r == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float* dst = s_work + (wave * G + h) * (D + 2);
+      float* dst = s_merge + (wave * G + h) * (D + 2);
 #pragma unroll
       for (int e = 0; e < EPL; ++e) dst[c * EPL + e] = acc[h][e];
       if (c == 0) {
@@ -588,7 +586,237 @@ __global__ __launch_bounds__(kThreads) void lf_step_kernel(StepArgs a) {
       }
     }
   }
+}
+
+// Streaming of one chunk on the matrix cores (bf16 cache).  A wave handles
+// groups of 16 rows:
+//  * q.k: v_mfma_f32_16x16x32_bf16 with the K rows as operand A (lane l loads
+//    row l % 16, dims [32 kb + 8 (l / 16), +8)) and the group's q as operand B
+//    (column n = query head n, zero beyond G).  Lane (j = l / 16, n = l % 16)
+//    receives the logits of rows 4 j + i, i < 4, for head n.
+//  * P.V: v_mfma_f32_16x16x16_bf16 per block of 16 value dims.  The group's
+//    value rows are written row-major to a per-wave LDS tile and read back with
+//    ds_read_b64_tr_b16, which transposes 4 x 4 blocks across each 16-lane
+//    group: lane (j, n) receives dims 16 blk + n of rows 4 j .. 4 j + 3, the A
+//    operand whose contraction index k = 4 j + e is row 4 j + e.  The B operand
+//    (row 4 j + e, head n) is then exactly the lane's own probability of logit
+//    e, so P never moves between lanes.  P enters as a bf16 hi part plus a bf16
+//    residual (two MFMAs), which keeps it to about 2^-17 relative error.
+//  * Online softmax with lazy rescaling: the reference max only moves when a
+//    group's max exceeds it by more than 2^8, so the accumulators are rescaled
+//    rarely; every quantity stays relative to the same reference, so results
+//    equal the eager form up to rounding.
+// Leaves the wave's partial in s_merge[wave][G][D + 2] like stream_valu.
+template <int D, int G>
+__device__ void stream_mfma(const StepArgs& a, int pair, int start, int row_end, float* lg, float* vn, int lstride,
+                            float* s_merge, unsigned char* s_stage) {
+  constexpr int KB = D / 32;  // q.k MFMAs per row group
+  constexpr int EV = D / 16;  // value dims per lane per row = P.V MFMAs per value row
+  constexpr float kLazy = 8.0f;
+  using VLoad = typename std::conditional<EV == 8, uint4, uint2>::type;
+  typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+  typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+  typedef short i16x4_t __attribute__((ext_vector_type(4)));
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
+  constexpr int RS = D * 2 + 32;  // staged row stride in bytes
+  constexpr int NB = D / 16;      // value-dim blocks
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, j = lane >> 4;
+  const int b = pair / a.n_kv_heads, g = pair - b * a.n_kv_heads;
+  const size_t pair_off = (size_t)pair * a.max_budget * D;
+  const uint16_t* Kp = static_cast<const uint16_t*>(a.k_cache) + pair_off;
+  const uint16_t* Vp = static_cast<const uint16_t*>(a.v_cache) + pair_off;
+
+  uint4 qb[KB];
+  {
+    const uint16_t* qh = static_cast<const uint16_t*>(a.q) + ((size_t)b * a.n_q_heads + (size_t)g * G + n) * D + 8 * j;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+      qb[kb] = n < G ? *reinterpret_cast<const uint4*>(qh + 32 * kb) : make_uint4(0, 0, 0, 0);
+  }
+  f32x4_t acc[NB];
+#pragma unroll
+  for (int e = 0; e < NB; ++e) acc[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // This wave's staging tile; lane (j, n) writes value rows 4 j + u at dims
+  // [EV n, EV n + EV) and reads, through the transposing load, the address of
+  // row 4 j + n / 4, dims 4 (n % 4) (+ 16 blk).
+  unsigned char* tile = s_stage + wave * 16 * RS;
+  unsigned char* wr = tile + 4 * j * RS + EV * 2 * n;
+  const unsigned char* rd = tile + (4 * j + (n >> 2)) * RS + 8 * (n & 3);
+  float m = kNegBig, lsum = 0.f;
+
+  // Loads never branch: rows past the end are clamped to the last valid row
+  // (their logits are masked to -inf, so their probabilities are exactly 0),
+  // which keeps the loads straight-line and the prefetch of the next group in
+  // flight while the current one is computed.
+  auto load_group = [&](int R, uint4(&kk)[KB], VLoad(&vv)[4]) {
+    const int last = row_end - 1;
+    const uint16_t* kr = Kp + (size_t)min(R + n, last) * D + 8 * j;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) kk[kb] = *reinterpret_cast<const uint4*>(kr + 32 * kb);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      vv[u] = *reinterpret_cast<const VLoad*>(Vp + (size_t)min(R + 4 * j + u, last) * D + EV * n);
+  };
+  auto process_group = [&](int R, const uint4(&kk)[KB], const VLoad(&vv)[4]) {
+    f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kk[kb]),
+                                                     __builtin_bit_cast(bf16x8_t, qb[kb]), sacc, 0, 0, 0);
+    float sv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sv[i] = sacc[i] * a.scale_log2;
+    const int r0 = R + 4 * j;
+    const bool full = R + 16 <= row_end;
+    if (!full) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sv[i] = r0 + i < row_end ? sv[i] : -INFINITY;
+    }
+    if (n < G) {
+      float* dst = lg + (size_t)n * lstride + r0;
+      if (full) {
+        *reinterpret_cast<float4*>(dst) = make_float4(sv[0], sv[1], sv[2], sv[3]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (r0 + i < row_end) dst[i] = sv[i];
+      }
+    }
+    // Group max per head: in-lane over 4 rows, then across the 4 lane groups.
+    float mt = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    mt = fmaxf(mt, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(mt), 0x401F)));  // lane ^ 16
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
+      mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));  // lane ^ 32
+    }
+    if (__builtin_amdgcn_ballot_w64(mt > m + kLazy)) {
+      const float mn = fmaxf(m, mt);
+      const float corr = fast_exp2(m - mn);
+      m = mn;
+      lsum *= corr;
+#pragma unroll
+      for (int e = 0; e < NB; ++e) acc[e] *= corr;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) *reinterpret_cast<VLoad*>(wr + u * RS) = vv[u];
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = fast_exp2(sv[i] - m);
+      lsum += p[i];
+    }
+    const bf16x4_t phi = {(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3]};
+    const bf16x4_t plo = {(__bf16)(p[0] - (float)phi[0]), (__bf16)(p[1] - (float)phi[1]),
+                          (__bf16)(p[2] - (float)phi[2]), (__bf16)(p[3] - (float)phi[3])};
+    const i16x4_t bhi = __builtin_bit_cast(i16x4_t, phi), blo = __builtin_bit_cast(i16x4_t, plo);
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) {
+      const i16x4_t av = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4_t*)(rd + 32 * blk));
+      acc[blk] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bhi, acc[blk], 0, 0, 0);
+      acc[blk] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, blo, acc[blk], 0, 0, 0);
+    }
+    if (a.vl1) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        float vf[EV];
+        if constexpr (EV == 8) {
+          unpack<BF16T>(vv[u], vf);
+        } else {
+          vf[0] = bf16_lo(vv[u].x);
+          vf[1] = bf16_hi(vv[u].x);
+          vf[2] = bf16_lo(vv[u].y);
+          vf[3] = bf16_hi(vv[u].y);
+        }
+        float n1 = 0.f;
+#pragma unroll
+        for (int e = 0; e < EV; ++e) n1 += fabsf(vf[e]);
+        n1 = row_sum<16>(n1);
+        if (n == 0 && r0 + u < row_end) vn[r0 + u] = n1;
+      }
+    }
+  };
+  {
+    constexpr int kStep = 16 * kWaves;  // rows per workgroup step
+    uint4 ka[KB], kb2[KB];
+    VLoad va[4], vb[4];
+    int R = start + 16 * wave;
+    if (R < row_end) load_group(R, ka, va);
+    while (R < row_end) {
+      const int R1 = R + kStep;
+      if (R1 < row_end) load_group(R1, kb2, vb);
+      process_group(R, ka, va);
+      if (R1 >= row_end) break;
+      const int R2 = R1 + kStep;
+      if (R2 < row_end) load_group(R2, ka, va);
+      process_group(R1, kb2, vb);
+      R = R2;
+    }
+  }
+  lsum += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(lsum), 0x401F));
+  {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum), false, false);
+    lsum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  }
+  if (n < G) {
+    float* dst = s_merge + (wave * G + n) * (D + 2);
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[16 * blk + 4 * j + i] = acc[blk][i];
+    if (j == 0) {
+      dst[D] = m;
+      dst[D + 1] = lsum;
+    }
+  }
+}
+
+template <class T, int D, int G>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(T::kEpl == 8 ? 3 : 1, 8))) void lf_step_kernel(StepArgs a) {
+  using S = Shape<T, D, G>;
+  constexpr int EPL = S::kEpl, LPR = S::kLpr;
+  using elem = typename T::elem;
+  __shared__ float smem[S::kSmemFloats];
+  __shared__ int s_last;
+  float* s_part = smem;                   // [G][D + 2]: merged partial of this chunk
+  float* s_work = smem + S::kPartFloats;  // cross-wave merge, then tail scratch
+
+  const int tid = threadIdx.x;
+  const WorkItem it = a.items[blockIdx.x];
+  const int pair = it.pair;
+  const int b = pair / a.n_kv_heads, g = pair - b * a.n_kv_heads;
+  PairMeta* meta = a.meta + pair;
+  const int len = meta->len;
+  const int lstride = meta->lstride;
+  const int nchunk = meta->nchunk;
+  float* lg = a.logits + (size_t)meta->slot0 * G;  // [G][lstride]
+  float* vn = a.vnorm + meta->slot0;                // [lstride]
+  const int row_end = min(it.start + it.count, len);
+
+  // Logit of the incoming token, computed up front so that the tail does not
+  // wait for it (every row lineage gets the same value).
+  float snew[G];
+  {
+    const int c = (tid & 63) % LPR;
+    QReg<T, G> q;
+    load_q<T, G>(q, static_cast<const elem*>(a.q) + ((size_t)b * a.n_q_heads + (size_t)g * G) * D + c * EPL, D,
+                 a.scale_log2);
+    const uint4 kn =
+        *reinterpret_cast<const uint4*>(static_cast<const elem*>(a.k_new) + (size_t)pair * D + c * EPL);
+    const float post_scale = T::kEpl == 8 ? a.scale_log2 : 1.0f;
+#pragma unroll
+    for (int h = 0; h < G; ++h) snew[h] = row_sum<LPR>(qk_part<T, G>(q, h, kn)) * post_scale;
+  }
+
+  if constexpr (T::kEpl == 8)
+    stream_mfma<D, G>(a, pair, it.start, row_end, lg, vn, lstride, s_work,
+                      reinterpret_cast<unsigned char*>(s_work + S::kMergeFloats));
+  else
+    stream_valu<T, D, G>(a, pair, it.start, row_end, lg, vn, lstride, s_work);
   __syncthreads();
+
+  // Merge the waves' partials into this chunk's partial.
   const size_t item = blockIdx.x;
   for (int idx = tid; idx < G * D; idx += kThreads) {
     const int h = idx / D, dim = idx - h * D;
@@ -629,8 +857,7 @@ __global__ __launch_bounds__(kThreads) void lf_step_kernel(StepArgs a) {
     __syncthreads();
     if (!s_last) return;
   }
-  (void)lstride;
-  pair_tail<T, D, G>(a, pair, q, post_scale, s_part, s_work);
+  pair_tail<T, D, G>(a, pair, snew, s_part, s_work);
 }
 
 template <class T, int D, int G>
