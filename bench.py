@@ -16,6 +16,7 @@ and the float64 CPU oracle timed on a bounded sample of the same workload."""
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -56,6 +57,19 @@ def algorithmic_bytes(w, bud) -> int:
     new = 2 * w.batch * w.n_kv_heads * w.head_dim * 2 * s
     qo = 2 * w.batch * w.n_q_heads * w.head_dim * s
     return kv + new + qo
+
+
+def profiled_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary of this workload, if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"lf_step_kernel_{workload}_traffic.json")
+    src = os.path.join(ROOT, "kv_cache_eviction_lf_amd", "csrc", "lf_kernel.hip")
+    try:
+        rec = json.load(open(path))
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    return rec.get("traffic_bytes_per_launch") if rec.get("kernel_source_sha256") == sha else None
 
 
 def cpu_baseline(w, seconds: float) -> dict:
@@ -253,7 +267,7 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": profiled_traffic(w.name),
             "bytes_per_launch": step_bytes,
             "kernel": "lf_step_kernel",
         },

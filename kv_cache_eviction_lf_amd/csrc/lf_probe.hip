@@ -1,5 +1,5 @@
-// HBM probes: a streaming copy and a streaming read with 16-byte lanes, one
-// contiguous 4 KiB run per workgroup load step, grid-stride over the buffer.
+// HBM probes: a streaming copy and a streaming read with 16-byte lanes, each
+// workgroup sweeping one contiguous slice of the buffer.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -8,37 +8,53 @@
 
 namespace {
 
+// Each workgroup streams one contiguous slice of the buffer with 8 16-byte
+// loads per lane in flight; 1024 workgroups of 256 threads.
 constexpr int kProbeThreads = 256;
-constexpr int kProbeBlocks = 256 * 8;  // 8 workgroups per CU on 256 CUs
-constexpr int kUnroll = 4;
+constexpr int kProbeBlocks = 1024;
+constexpr int kUnroll = 8;
+
+__device__ __forceinline__ void slice(size_t n, size_t& lo, size_t& hi) {
+  const size_t per = (n + gridDim.x - 1) / gridDim.x;
+  lo = per * blockIdx.x;
+  hi = lo + per < n ? lo + per : n;
+}
 
 __global__ __launch_bounds__(kProbeThreads) void probe_copy_kernel(const uint4* __restrict__ src,
                                                                     uint4* __restrict__ dst, size_t n) {
-  const size_t stride = (size_t)gridDim.x * kProbeThreads;
-  size_t i = (size_t)blockIdx.x * kProbeThreads + threadIdx.x;
-  for (; i + (kUnroll - 1) * stride < n; i += kUnroll * stride) {
+  size_t lo, hi;
+  slice(n, lo, hi);
+  for (size_t i = lo + threadIdx.x; i < hi; i += (size_t)kProbeThreads * kUnroll) {
     uint4 v[kUnroll];
 #pragma unroll
-    for (int k = 0; k < kUnroll; ++k) v[k] = src[i + k * stride];
+    for (int k = 0; k < kUnroll; ++k) {
+      const size_t j = i + (size_t)k * kProbeThreads;
+      v[k] = j < hi ? src[j] : make_uint4(0, 0, 0, 0);
+    }
 #pragma unroll
-    for (int k = 0; k < kUnroll; ++k) dst[i + k * stride] = v[k];
+    for (int k = 0; k < kUnroll; ++k) {
+      const size_t j = i + (size_t)k * kProbeThreads;
+      if (j < hi) dst[j] = v[k];
+    }
   }
-  for (; i < n; i += stride) dst[i] = src[i];
 }
 
 __global__ __launch_bounds__(kProbeThreads) void probe_read_kernel(const uint4* __restrict__ src, size_t n,
                                                                     uint32_t* __restrict__ sink) {
-  const size_t stride = (size_t)gridDim.x * kProbeThreads;
-  size_t i = (size_t)blockIdx.x * kProbeThreads + threadIdx.x;
+  size_t lo, hi;
+  slice(n, lo, hi);
   uint32_t x = 0;
-  for (; i + (kUnroll - 1) * stride < n; i += kUnroll * stride) {
+  for (size_t i = lo + threadIdx.x; i < hi; i += (size_t)kProbeThreads * kUnroll) {
     uint4 v[kUnroll];
 #pragma unroll
-    for (int k = 0; k < kUnroll; ++k) v[k] = src[i + k * stride];
+    for (int k = 0; k < kUnroll; ++k) {
+      const size_t j = i + (size_t)k * kProbeThreads;
+      v[k] = src[j < hi ? j : hi - 1];
+    }
 #pragma unroll
-    for (int k = 0; k < kUnroll; ++k) x ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
+    for (int k = 0; k < kUnroll; ++k)
+      if (i + (size_t)k * kProbeThreads < hi) x ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
   }
-  for (; i < n; i += stride) x ^= src[i].x ^ src[i].y ^ src[i].z ^ src[i].w;
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) x ^= __shfl_xor(x, off);
   __shared__ uint32_t s[kProbeThreads / 64];
