@@ -77,7 +77,10 @@ struct Shape {
   // bf16: per-wave tile of 16 value rows, rows padded by 32 bytes against LDS bank conflicts.
   static constexpr int kStageRowBytes = D * 2 + 32;
   static constexpr int kStageFloats = kEpl == 8 ? kWaves * 16 * kStageRowBytes / 4 : 0;
-  static constexpr int kStreamFloats = kMergeFloats + kStageFloats;
+  // bf16: per-wave logit buffer [G][128 rows], flushed to HBM in contiguous runs.
+  static constexpr int kLogitRows = 128;
+  static constexpr int kLogitFloats = kEpl == 8 ? kWaves * G * kLogitRows : 0;
+  static constexpr int kStreamFloats = kMergeFloats + kStageFloats + kLogitFloats;
   static constexpr int kSmemFloats = kPartFloats + (kStreamFloats > kTailFloats ? kStreamFloats : kTailFloats);
 };
 
@@ -145,6 +148,18 @@ __device__ __forceinline__ float row_sum(float x) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Non-temporal (streaming) 16- and 8-byte loads.
+__device__ __forceinline__ uint4 load_nt(const uint4* p) {
+  typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+  const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(x[0], x[1], x[2], x[3]);
+}
+__device__ __forceinline__ uint2 load_nt(const uint2* p) {
+  typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+  const u32x2_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+  return make_uint2(x[0], x[1]);
+}
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
@@ -267,6 +282,8 @@ __device__ void pair_tail(const StepArgs& a, int pair, const float (&snew)[G], c
   }
   const float* lg = a.logits + (size_t)meta->slot0 * G;  // [G][lstride]
   const float* vn = a.vnorm + meta->slot0;                // [lstride]
+  // bf16 streaming stores raw q.k; fp32 streaming stores log2-domain logits.
+  const float ls = T::kEpl == 8 ? a.scale_log2 : 1.0f;
   float4 lv0[G];
   float4 v10 = make_float4(1.f, 1.f, 1.f, 1.f);
   if (4 * tid < len) {
@@ -366,10 +383,10 @@ __device__ void pair_tail(const StepArgs& a, int pair, const float (&snew)[G], c
     float sc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      sc[0] = fmaf(fast_exp2(lv[h].x - M[h]), invL[h], sc[0]);
-      sc[1] = fmaf(fast_exp2(lv[h].y - M[h]), invL[h], sc[1]);
-      sc[2] = fmaf(fast_exp2(lv[h].z - M[h]), invL[h], sc[2]);
-      sc[3] = fmaf(fast_exp2(lv[h].w - M[h]), invL[h], sc[3]);
+      sc[0] = fmaf(fast_exp2(fmaf(lv[h].x, ls, -M[h])), invL[h], sc[0]);
+      sc[1] = fmaf(fast_exp2(fmaf(lv[h].y, ls, -M[h])), invL[h], sc[1]);
+      sc[2] = fmaf(fast_exp2(fmaf(lv[h].z, ls, -M[h])), invL[h], sc[2]);
+      sc[3] = fmaf(fast_exp2(fmaf(lv[h].w, ls, -M[h])), invL[h], sc[3]);
     }
     sc[0] *= v1.x;
     sc[1] *= v1.y;
@@ -609,7 +626,7 @@ __device__ void stream_valu(const StepArgs& a, int pair, int start, int row_end,
 // Leaves the wave's partial in s_merge[wave][G][D + 2] like stream_valu.
 template <int D, int G>
 __device__ void stream_mfma(const StepArgs& a, int pair, int start, int row_end, float* lg, float* vn, int lstride,
-                            float* s_merge, unsigned char* s_stage) {
+                            float* s_merge, unsigned char* s_stage, float* s_logit) {
   constexpr int KB = D / 32;  // q.k MFMAs per row group
   constexpr int EV = D / 16;  // value dims per lane per row = P.V MFMAs per value row
   constexpr float kLazy = 8.0f;
@@ -645,50 +662,75 @@ __device__ void stream_mfma(const StepArgs& a, int pair, int start, int row_end,
   const unsigned char* rd = tile + (4 * j + (n >> 2)) * RS + 8 * (n & 3);
   float m = kNegBig, lsum = 0.f;
 
-  // Loads never branch: rows past the end are clamped to the last valid row
-  // (their logits are masked to -inf, so their probabilities are exactly 0),
-  // which keeps the loads straight-line and the prefetch of the next group in
-  // flight while the current one is computed.
-  auto load_group = [&](int R, uint4(&kk)[KB], VLoad(&vv)[4]) {
-    const int last = row_end - 1;
-    const uint16_t* kr = Kp + (size_t)min(R + n, last) * D + 8 * j;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) kk[kb] = *reinterpret_cast<const uint4*>(kr + 32 * kb);
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      vv[u] = *reinterpret_cast<const VLoad*>(Vp + (size_t)min(R + 4 * j + u, last) * D + EV * n);
+  // Each wave walks its own contiguous quarter of the chunk in 16-row groups.
+  // Full groups run in a two-stage pipeline with pointer bumps and immediate
+  // offsets (the next group's loads are in flight while the current one
+  // computes); at most one ragged group per wave remains and is loaded with
+  // rows clamped to the last valid row (their logits are masked to -inf, so
+  // their probabilities are exactly 0).  The raw q.k of every row goes to a
+  // per-wave LDS buffer and is written to HBM 128 rows at a time as contiguous
+  // runs: scattered 16-byte logit stores mixed into the K/V read stream cost
+  // far more HBM time than their size.
+  constexpr int LR = 128;  // rows per logit flush
+  const float scale = a.scale_log2;
+  const int quarter = ((row_end - start + kWaves - 1) / kWaves + 15) & ~15;
+  const int R0 = start + wave * quarter;
+  const int Rend = min(R0 + quarter, row_end);
+  const int nfull = Rend - R0 >= 16 ? (Rend - R0) / 16 : 0;
+  const int Rp = R0 + 16 * nfull;  // first row of the ragged group, if any
+  const uint16_t* kp = Kp + (size_t)(R0 + n) * D + 8 * j;
+  const uint16_t* vp = Vp + (size_t)(R0 + 4 * j) * D + EV * n;
+  float* lbuf = s_logit + wave * G * LR;  // [G][LR]
+  int flushed = R0;                       // rows below this are already in HBM
+
+  auto flush = [&](int upto) {  // write buffered logits of rows [flushed, upto)
+    const int nrows = upto - flushed;
+    const int n4 = (nrows + 3) >> 2;
+    for (int idx = lane; idx < G * n4; idx += 64) {
+      const int h = idx / n4, r4 = idx - h * n4;
+      const float* src = lbuf + h * LR + 4 * r4;
+      float* dst = lg + (size_t)h * lstride + flushed + 4 * r4;
+      if (4 * r4 + 4 <= nrows) {
+        *reinterpret_cast<float4*>(dst) = *reinterpret_cast<const float4*>(src);
+      } else {
+        for (int i = 0; 4 * r4 + i < nrows; ++i) dst[i] = src[i];
+      }
+    }
+    flushed = upto;
   };
-  auto process_group = [&](int R, const uint4(&kk)[KB], const VLoad(&vv)[4]) {
+  // K/V are read once per step: non-temporal loads keep them from displacing
+  // the workspace (logits, partials) in L2 and the Infinity Cache.
+  auto load_full = [&](uint4(&kk)[KB], VLoad(&vv)[4]) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) kk[kb] = load_nt(reinterpret_cast<const uint4*>(kp + 32 * kb));
+#pragma unroll
+    for (int u = 0; u < 4; ++u) vv[u] = load_nt(reinterpret_cast<const VLoad*>(vp + u * D));
+    kp += 16 * D;
+    vp += 16 * D;
+  };
+  auto process = [&](auto full_tag, const uint4(&kk)[KB], const VLoad(&vv)[4], int R) {
+    constexpr bool kFull = decltype(full_tag)::value;
+    const int r0 = R + 4 * j;
     f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
       sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kk[kb]),
                                                      __builtin_bit_cast(bf16x8_t, qb[kb]), sacc, 0, 0, 0);
-    float sv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sv[i] = sacc[i] * a.scale_log2;
-    const int r0 = R + 4 * j;
-    const bool full = R + 16 <= row_end;
-    if (!full) {
+    float sv[4] = {sacc[0], sacc[1], sacc[2], sacc[3]};  // raw q.k of rows r0 + i, head n
+    if constexpr (!kFull) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) sv[i] = r0 + i < row_end ? sv[i] : -INFINITY;
     }
-    if (n < G) {
-      float* dst = lg + (size_t)n * lstride + r0;
-      if (full) {
-        *reinterpret_cast<float4*>(dst) = make_float4(sv[0], sv[1], sv[2], sv[3]);
-      } else {
+    if (n < G)
+      *reinterpret_cast<float4*>(lbuf + n * LR + (r0 - flushed)) = make_float4(sv[0], sv[1], sv[2], sv[3]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (r0 + i < row_end) dst[i] = sv[i];
-      }
-    }
-    // Group max per head: in-lane over 4 rows, then across the 4 lane groups.
+    for (int u = 0; u < 4; ++u) *reinterpret_cast<VLoad*>(wr + u * RS) = vv[u];
+    // Group max per head (log2 domain): in-lane over 4 rows, then across the 4 lane groups.
     float mt = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
     mt = fmaxf(mt, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(mt), 0x401F)));  // lane ^ 16
     {
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
-      mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));  // lane ^ 32
+      mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale;  // lane ^ 32
     }
     if (__builtin_amdgcn_ballot_w64(mt > m + kLazy)) {
       const float mn = fmaxf(m, mt);
@@ -698,12 +740,10 @@ __device__ void stream_mfma(const StepArgs& a, int pair, int start, int row_end,
 #pragma unroll
       for (int e = 0; e < NB; ++e) acc[e] *= corr;
     }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) *reinterpret_cast<VLoad*>(wr + u * RS) = vv[u];
     float p[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      p[i] = fast_exp2(sv[i] - m);
+      p[i] = fast_exp2(fmaf(sv[i], scale, -m));
       lsum += p[i];
     }
     const bf16x4_t phi = {(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3]};
@@ -733,26 +773,37 @@ __device__ void stream_mfma(const StepArgs& a, int pair, int start, int row_end,
 #pragma unroll
         for (int e = 0; e < EV; ++e) n1 += fabsf(vf[e]);
         n1 = row_sum<16>(n1);
-        if (n == 0 && r0 + u < row_end) vn[r0 + u] = n1;
+        if (n == 0 && (kFull || r0 + u < row_end)) vn[r0 + u] = n1;
       }
     }
   };
   {
-    constexpr int kStep = 16 * kWaves;  // rows per workgroup step
     uint4 ka[KB], kb2[KB];
     VLoad va[4], vb[4];
-    int R = start + 16 * wave;
-    if (R < row_end) load_group(R, ka, va);
-    while (R < row_end) {
-      const int R1 = R + kStep;
-      if (R1 < row_end) load_group(R1, kb2, vb);
-      process_group(R, ka, va);
-      if (R1 >= row_end) break;
-      const int R2 = R1 + kStep;
-      if (R2 < row_end) load_group(R2, ka, va);
-      process_group(R1, kb2, vb);
-      R = R2;
+    int g = 0;
+    if (nfull > 0) load_full(ka, va);
+    while (g < nfull) {
+      if (g + 1 < nfull) load_full(kb2, vb);
+      process(std::true_type{}, ka, va, R0 + 16 * g);
+      ++g;
+      if ((g & (LR / 16 - 1)) == 0) flush(R0 + 16 * g);
+      if (g >= nfull) break;
+      if (g + 1 < nfull) load_full(ka, va);
+      process(std::true_type{}, kb2, vb, R0 + 16 * g);
+      ++g;
+      if ((g & (LR / 16 - 1)) == 0) flush(R0 + 16 * g);
     }
+    if (Rp < Rend) {
+      const int last = row_end - 1;
+      const uint16_t* kr = Kp + (size_t)min(Rp + n, last) * D + 8 * j;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) ka[kb] = *reinterpret_cast<const uint4*>(kr + 32 * kb);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        va[u] = *reinterpret_cast<const VLoad*>(Vp + (size_t)min(Rp + 4 * j + u, last) * D + EV * n);
+      process(std::false_type{}, ka, va, Rp);
+    }
+    if (flushed < Rend) flush(Rend);
   }
   lsum += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(lsum), 0x401F));
   {
@@ -811,7 +862,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(T::kEp
 
   if constexpr (T::kEpl == 8)
     stream_mfma<D, G>(a, pair, it.start, row_end, lg, vn, lstride, s_work,
-                      reinterpret_cast<unsigned char*>(s_work + S::kMergeFloats));
+                      reinterpret_cast<unsigned char*>(s_work + S::kMergeFloats),
+                      s_work + S::kMergeFloats + S::kStageFloats);
   else
     stream_valu<T, D, G>(a, pair, it.start, row_end, lg, vn, lstride, s_work);
   __syncthreads();
