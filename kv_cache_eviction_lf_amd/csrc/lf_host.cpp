@@ -218,6 +218,7 @@ lf_status step_impl(const void* q, const void* k_new, const void* v_new, lf_cach
   a.logits = reinterpret_cast<float*>(s + L.logits);
   a.vnorm = reinterpret_cast<float*>(s + L.vnorm);
   a.n_items = L.n_items;
+  a.n_pairs = cfg.batch * cfg.n_kv_heads;
   a.n_q_heads = cfg.n_q_heads;
   a.n_kv_heads = cfg.n_kv_heads;
   a.max_budget = cfg.max_budget;

@@ -72,6 +72,7 @@ struct StepArgs {
   float* logits;    // per pair [G][budget], log2-domain logits of this step
   float* vnorm;     // per pair [budget], |v|_1 of every slot (VL1 only)
   int32_t n_items;
+  int32_t n_pairs;  // batch * n_kv_heads
   int32_t n_q_heads;
   int32_t n_kv_heads;
   int32_t max_budget;

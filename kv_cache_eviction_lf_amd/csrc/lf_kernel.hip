@@ -147,6 +147,25 @@ __device__ __forceinline__ float row_sum(float x) {
   return x;
 }
 
+// Reductions over the 64 lanes of a wave with DPP and lane swaps (no LDS
+// round trips); every lane gets the result.
+template <class Op>
+__device__ __forceinline__ float wave_reduce(float x, Op op) {
+  x = op(x, dpp<0xB1>(x));
+  x = op(x, dpp<0x4E>(x));
+  x = op(x, dpp<0x141>(x));
+  x = op(x, dpp<0x140>(x));
+  x = op(x, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F)));  // lane ^ 16
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return op(__uint_as_float(sw[0]), __uint_as_float(sw[1]));  // lane ^ 32
+}
+__device__ __forceinline__ float wave_max(float x) {
+  return wave_reduce(x, [](float u, float v) { return fmaxf(u, v); });
+}
+__device__ __forceinline__ float wave_sum(float x) {
+  return wave_reduce(x, [](float u, float v) { return u + v; });
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Non-temporal (streaming) 16- and 8-byte loads.
@@ -159,6 +178,51 @@ __device__ __forceinline__ uint2 load_nt(const uint2* p) {
   typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
   const u32x2_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
   return make_uint2(x[0], x[1]);
+}
+
+// Data one workgroup hands to another in the same launch (logits, |v| norms,
+// chunk partials of a split pair) moves only through device-scope atomic
+// stores and loads (relaxed, agent scope; "sc1" on gfx950: written through the
+// non-coherent per-XCD L2 to memory, and read past it).  Each chunk drains its
+// stores (s_waitcnt vmcnt(0): a device-scope store has then reached memory)
+// before its thread 0 increments the pair's ticket with a device-scope RMW, and
+// the chunk that takes the last ticket reads the others' data with
+// device-scope loads issued after that RMW returned.  This is the ordering a
+// release/acquire pair would give, without the L2 write-back and invalidate
+// that only plain (non-atomic) stores and loads need.
+__device__ __forceinline__ void store_wt(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_wt(float2* p, float2 v) {
+  const unsigned long long x =
+      (unsigned long long)__float_as_uint(v.x) | ((unsigned long long)__float_as_uint(v.y) << 32);
+  __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// 16-byte device-scope store through a buffer resource over [base, base + bytes).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t wt_rsrc(float* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ void store_wt4(__amdgpu_buffer_rsrc_t r, int byte_off, float4 v) {
+  typedef unsigned u32x4_t __attribute__((vector_size(16)));
+  const u32x4_t x = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)};
+  __builtin_amdgcn_raw_buffer_store_b128(x, r, byte_off, 0, 16 /* sc1 */);
+}
+__device__ __forceinline__ float load_x(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 load_x(const float2* p) {
+  const unsigned long long x =
+      __hip_atomic_load(reinterpret_cast<const unsigned long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float(static_cast<unsigned>(x)), __uint_as_float(static_cast<unsigned>(x >> 32)));
+}
+__device__ __forceinline__ float4 load_x(const float4* p) {
+  const float2 lo = load_x(reinterpret_cast<const float2*>(p)), hi = load_x(reinterpret_cast<const float2*>(p) + 1);
+  return make_float4(lo.x, lo.y, hi.x, hi.y);
+}
+// Workspace read in the tail: written by other workgroups when the pair is
+// split, else by this one (then a plain load, which may hit in L2).
+__device__ __forceinline__ float4 load_ws(const float* p, bool split) {
+  return split ? load_x(reinterpret_cast<const float4*>(p)) : *reinterpret_cast<const float4*>(p);
 }
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
@@ -219,6 +283,25 @@ __device__ __forceinline__ void argmin_merge(float& s, int& i, float so, int io)
   }
 }
 
+// Wave-wide lexicographic (score, slot) minimum; every lane gets the result.
+__device__ __forceinline__ void wave_argmin(float& s, int& i) {
+  auto step = [&](float so, int io) { argmin_merge(s, i, so, io); };
+#define LF_DPP_STEP(CTRL) step(dpp<CTRL>(s), __builtin_amdgcn_mov_dpp(i, CTRL, 0xF, 0xF, false))
+  LF_DPP_STEP(0xB1);
+  LF_DPP_STEP(0x4E);
+  LF_DPP_STEP(0x141);
+  LF_DPP_STEP(0x140);
+#undef LF_DPP_STEP
+  step(__int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(s), 0x401F)), __builtin_amdgcn_ds_swizzle(i, 0x401F));
+  const auto ss = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+  const auto si = __builtin_amdgcn_permlane32_swap(static_cast<unsigned>(i), static_cast<unsigned>(i), false, false);
+  float s0 = __uint_as_float(ss[0]);
+  int i0 = static_cast<int>(si[0]);
+  argmin_merge(s0, i0, __uint_as_float(ss[1]), static_cast<int>(si[1]));
+  s = s0;
+  i = i0;
+}
+
 // Tail of one pair: merge chunk partials, output, importance, argmin, insert.
 // Every load that does not depend on the merged statistics (chunk maxima and
 // sums, the ring, the chunk partials, the first logits, the new token) is
@@ -227,16 +310,17 @@ __device__ __forceinline__ void argmin_merge(float& s, int& i, float so, int io)
 // s_part: this workgroup's merged partial ([G][D + 2], used when nchunk == 1);
 // s_tail: scratch of Shape::kTailFloats floats.
 template <class T, int D, int G>
-__device__ void pair_tail(const StepArgs& a, int pair, const float (&snew)[G], const float* s_part, float* s_tail) {
+__device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const float* s_part, float* s_tail) {
   using elem = typename T::elem;
   constexpr int kOut = (G * D + kThreads - 1) / kThreads;  // output elements per thread
   constexpr int kCB = G <= 4 ? 8 : 4;                       // chunk partials loaded per batch
   constexpr int kVec = D * sizeof(elem) / 16;               // 16-byte pieces of one K/V row
+  constexpr int kPre = G <= 2 ? 8 : 16 / G;                  // float4 logit cells per head preloaded
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   PairMeta* meta = a.meta + pair;
   const int b = pair / a.n_kv_heads, g = pair - b * a.n_kv_heads;
-  const int t = meta->t, len = meta->len, budget = meta->budget;
-  const int nchunk = meta->nchunk, item0 = meta->item0, lstride = meta->lstride;
+  const int t = pm.t, len = pm.len, budget = pm.budget;
+  const int nchunk = pm.nchunk, item0 = pm.item0, lstride = pm.lstride;
   const int R = a.recent;
   const bool split = nchunk > 1;
   const size_t pair_off = (size_t)pair * a.max_budget * D;
@@ -246,27 +330,30 @@ __device__ void pair_tail(const StepArgs& a, int pair, const float (&snew)[G], c
   uint32_t* s_bits = reinterpret_cast<uint32_t*>(s_red + 2 * kWaves * G);  // protected slots
   float* s_arg = reinterpret_cast<float*>(s_bits + kMaxBudget / 32);       // [kWaves] score, [kWaves] slot
 
-  // ---- loads that depend on nothing computed here
-  float mc[G], lc[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    mc[h] = kNegBig;
-    lc[h] = 0.f;
+  // ---- loads that depend on nothing computed here.  Addresses are clamped to
+  // valid memory and nothing is branched around, so the loads issue back to
+  // back and one wait covers them; out-of-range lanes are masked where used.
+  using S = Shape<T, D, G>;
+  constexpr int EPL = S::kEpl, LPR = S::kLpr;
+  QReg<T, G> q;
+  uint4 kn;
+  {
+    const int c = lane % LPR;
+    load_q<T, G>(q, static_cast<const elem*>(a.q) + ((size_t)b * a.n_q_heads + (size_t)g * G) * D + c * EPL, D,
+                 a.scale_log2);
+    kn = *reinterpret_cast<const uint4*>(static_cast<const elem*>(a.k_new) + (size_t)pair * D + c * EPL);
   }
-  if (split && tid < nchunk) {
-    const float2* src = reinterpret_cast<const float2*>(a.part_ml) + (size_t)(item0 + tid) * G;
+  float2 ml[G];
+  if (split) {
+    const float2* src = reinterpret_cast<const float2*>(a.part_ml) + (size_t)(item0 + min(tid, nchunk - 1)) * G;
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float2 v = src[h];
-      mc[h] = v.x;
-      lc[h] = v.y;
-    }
+    for (int h = 0; h < G; ++h) ml[h] = load_x(&src[h]);
   }
   const int32_t* ring = a.ring + (size_t)pair * R;
-  const int ring_sl = tid < R ? ring[tid] : -1;
-  uint4 ins = make_uint4(0, 0, 0, 0);
-  if (tid < 2 * kVec) {
-    const int which = tid / kVec, part = tid - which * kVec;
+  const int ring_raw = R > 0 ? ring[min(tid, R - 1)] : -1;
+  uint4 ins;
+  {
+    const int c = min(tid, 2 * kVec - 1), which = c / kVec, part = c - which * kVec;
     ins = reinterpret_cast<const uint4*>(static_cast<const elem*>(which ? a.v_new : a.k_new) + (size_t)pair * D)[part];
   }
   const elem* vnp = static_cast<const elem*>(a.v_new) + (size_t)pair * D;
@@ -274,25 +361,44 @@ __device__ void pair_tail(const StepArgs& a, int pair, const float (&snew)[G], c
   float vnv[kOut], pa[kOut][kCB];
 #pragma unroll
   for (int o = 0; o < kOut; ++o) {
-    const int idx = tid + o * kThreads;
-    const bool ok = idx < G * D;
-    vnv[o] = ok ? load_elem<T>(vnp, idx % D) : 0.f;
+    const int idx = min(tid + o * kThreads, G * D - 1);
+    vnv[o] = load_elem<T>(vnp, idx % D);
+    if (split) {
 #pragma unroll
-    for (int k = 0; k < kCB; ++k) pa[o][k] = (split && ok && k < nchunk) ? pacc[(size_t)k * G * D + idx] : 0.f;
+      for (int k = 0; k < kCB; ++k) pa[o][k] = load_x(&pacc[(size_t)min(k, nchunk - 1) * G * D + idx]);
+    }
   }
-  const float* lg = a.logits + (size_t)meta->slot0 * G;  // [G][lstride]
-  const float* vn = a.vnorm + meta->slot0;                // [lstride]
+  const float* lg = a.logits + (size_t)pm.slot0 * G;  // [G][lstride]
+  const float* vn = a.vnorm + pm.slot0;                // [lstride]
   // bf16 streaming stores raw q.k; fp32 streaming stores log2-domain logits.
   const float ls = T::kEpl == 8 ? a.scale_log2 : 1.0f;
-  float4 lv0[G];
-  float4 v10 = make_float4(1.f, 1.f, 1.f, 1.f);
-  if (4 * tid < len) {
+  // The first kPre * 4 * kThreads slots' logits (all of them for budgets up to
+  // that) are in flight together with everything above.
+  float4 lvp[kPre][G];
+  float4 v1p[kPre];
 #pragma unroll
-    for (int h = 0; h < G; ++h) lv0[h] = *reinterpret_cast<const float4*>(lg + (size_t)h * lstride + 4 * tid);
-    if (a.vl1) v10 = *reinterpret_cast<const float4*>(vn + 4 * tid);
+  for (int p = 0; p < kPre; ++p) {
+    const int base = min(4 * (tid + p * kThreads), lstride - 4);
+#pragma unroll
+    for (int h = 0; h < G; ++h) lvp[p][h] = load_ws(lg + (size_t)h * lstride + base, split);
+    v1p[p] = a.vl1 ? load_ws(vn + base, split) : make_float4(1.f, 1.f, 1.f, 1.f);
+  }
+  const int ring_sl = tid < R ? ring_raw : -1;
+  float mc[G], lc[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    mc[h] = split && tid < nchunk ? ml[h].x : kNegBig;
+    lc[h] = split && tid < nchunk ? ml[h].y : 0.f;
   }
 
   // ---- global max and normaliser over the chunks and the incoming token
+  // Logit of the incoming token (every lane of a row lineage holds it).
+  float snew[G];
+  {
+    const float post_scale = T::kEpl == 8 ? a.scale_log2 : 1.0f;
+#pragma unroll
+    for (int h = 0; h < G; ++h) snew[h] = row_sum<LPR>(qk_part<T, G>(q, h, kn)) * post_scale;
+  }
   const int nwords = (budget + 31) >> 5;
   for (int i = tid; i < nwords; i += kThreads) s_bits[i] = 0u;
   if (!split && tid == 0) {
@@ -304,9 +410,7 @@ __device__ void pair_tail(const StepArgs& a, int pair, const float (&snew)[G], c
   }
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    float x = mc[h];
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+    const float x = wave_max(mc[h]);
     if (lane == 0) s_red[wave * G + h] = x;
   }
   __syncthreads();  // bitmap zeroed, per-wave maxima visible
@@ -324,9 +428,7 @@ __device__ void pair_tail(const StepArgs& a, int pair, const float (&snew)[G], c
     M[h] = x;
     const float wgt = fast_exp2(mc[h] - M[h]);
     if (tid < nchunk) s_w[tid * G + h] = wgt;
-    float y = lc[h] * wgt;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) y += __shfl_xor(y, off);
+    const float y = wave_sum(lc[h] * wgt);
     if (lane == 0) s_red[(kWaves + wave) * G + h] = y;
   }
   __syncthreads();  // chunk weights, per-wave sums and the bitmap complete
@@ -364,7 +466,7 @@ __device__ void pair_tail(const StepArgs& a, int pair, const float (&snew)[G], c
         for (int ci = kCB; ci < nchunk; ci += kCB) {
           float x[kCB];
 #pragma unroll
-          for (int k = 0; k < kCB; ++k) x[k] = ci + k < nchunk ? pacc[(size_t)(ci + k) * G * D + idx] : 0.f;
+          for (int k = 0; k < kCB; ++k) x[k] = ci + k < nchunk ? load_x(&pacc[(size_t)(ci + k) * G * D + idx]) : 0.f;
 #pragma unroll
           for (int k = 0; k < kCB; ++k)
             if (ci + k < nchunk) acc = fmaf(x[k], s_w[(ci + k) * G + h], acc);
@@ -405,22 +507,19 @@ __device__ void pair_tail(const StepArgs& a, int pair, const float (&snew)[G], c
       }
     }
   };
-  if (4 * tid < len) score4(4 * tid, lv0, v10);
+#pragma unroll
+  for (int p = 0; p < kPre; ++p)
+    if (4 * (tid + p * kThreads) < len) score4(4 * (tid + p * kThreads), lvp[p], v1p[p]);
 #pragma unroll 2
-  for (int base = 4 * tid + 4 * kThreads; base < len; base += 4 * kThreads) {
+  for (int base = 4 * (tid + kPre * kThreads); base < len; base += 4 * kThreads) {
     float4 lv[G];
 #pragma unroll
-    for (int h = 0; h < G; ++h) lv[h] = *reinterpret_cast<const float4*>(lg + (size_t)h * lstride + base);
+    for (int h = 0; h < G; ++h) lv[h] = load_ws(lg + (size_t)h * lstride + base, split);
     float4 v1 = make_float4(1.f, 1.f, 1.f, 1.f);
-    if (a.vl1) v1 = *reinterpret_cast<const float4*>(vn + base);
+    if (a.vl1) v1 = load_ws(vn + base, split);
     score4(base, lv, v1);
   }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const float so = __shfl_xor(best, off);
-    const int io = __shfl_xor(besti, off);
-    argmin_merge(best, besti, so, io);
-  }
+  wave_argmin(best, besti);
   if (lane == 0) {
     s_arg[wave] = best;
     reinterpret_cast<int*>(s_arg)[kWaves + wave] = besti;
@@ -513,7 +612,7 @@ __device__ void stream_valu(const StepArgs& a, int pair, int start, int row_end,
           float mine = s[u][0];
 #pragma unroll
           for (int h = 1; h < G; ++h) mine = c == h ? s[u][h] : mine;
-          lg[(size_t)c * lstride + row] = mine;
+          store_wt(&lg[(size_t)c * lstride + row], mine);
         }
       } else {
 #pragma unroll
@@ -530,7 +629,7 @@ __device__ void stream_valu(const StepArgs& a, int pair, int start, int row_end,
 #pragma unroll
         for (int e = 0; e < EPL; ++e) n1 += fabsf(vx[e]);
         n1 = row_sum<LPR>(n1);
-        if (c == 0 && row < row_end) vn[row] = n1;
+        if (c == 0 && row < row_end) store_wt(&vn[row], n1);
       }
     }
 #pragma unroll
@@ -682,19 +781,23 @@ __device__ void stream_mfma(const StepArgs& a, int pair, int start, int row_end,
   const uint16_t* vp = Vp + (size_t)(R0 + 4 * j) * D + EV * n;
   float* lbuf = s_logit + wave * G * LR;  // [G][LR]
   int flushed = R0;                       // rows below this are already in HBM
+  const __amdgpu_buffer_rsrc_t lrs = wt_rsrc(lg, G * lstride * 4);
 
   auto flush = [&](int upto) {  // write buffered logits of rows [flushed, upto)
+    // Fixed trip count (no data-dependent loop): the compiler can then count
+    // the outstanding stores exactly and never waits for them to complete.
+    constexpr int NV = G * LR / 4;  // float4 cells of the buffer
     const int nrows = upto - flushed;
-    const int n4 = (nrows + 3) >> 2;
-    for (int idx = lane; idx < G * n4; idx += 64) {
-      const int h = idx / n4, r4 = idx - h * n4;
-      const float* src = lbuf + h * LR + 4 * r4;
-      float* dst = lg + (size_t)h * lstride + flushed + 4 * r4;
-      if (4 * r4 + 4 <= nrows) {
-        *reinterpret_cast<float4*>(dst) = *reinterpret_cast<const float4*>(src);
-      } else {
-        for (int i = 0; 4 * r4 + i < nrows; ++i) dst[i] = src[i];
-      }
+#pragma unroll
+    for (int it = 0; it < (NV + 63) / 64; ++it) {
+      const int idx = lane + 64 * it;
+      const int h = idx / (LR / 4), r4 = idx % (LR / 4);
+      // A ragged end is only possible at the pair's last filled row (chunk
+      // bounds are tile multiples, wave bounds multiples of 16); the slots
+      // between it and the next multiple of 4 are unfilled and never read, so
+      // whole float4 cells are written (the buffer holds -inf there).
+      if ((NV % 64 == 0 || idx < NV) && 4 * r4 < nrows)
+        store_wt4(lrs, 4 * (h * lstride + flushed + 4 * r4), *reinterpret_cast<const float4*>(lbuf + h * LR + 4 * r4));
     }
     flushed = upto;
   };
@@ -773,7 +876,7 @@ __device__ void stream_mfma(const StepArgs& a, int pair, int start, int row_end,
 #pragma unroll
         for (int e = 0; e < EV; ++e) n1 += fabsf(vf[e]);
         n1 = row_sum<16>(n1);
-        if (n == 0 && (kFull || r0 + u < row_end)) vn[r0 + u] = n1;
+        if (n == 0 && (kFull || r0 + u < row_end)) store_wt(&vn[r0 + u], n1);
       }
     }
   };
@@ -826,8 +929,6 @@ __device__ void stream_mfma(const StepArgs& a, int pair, int start, int row_end,
 template <class T, int D, int G>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(T::kEpl == 8 ? 3 : 1, 8))) void lf_step_kernel(StepArgs a) {
   using S = Shape<T, D, G>;
-  constexpr int EPL = S::kEpl, LPR = S::kLpr;
-  using elem = typename T::elem;
   __shared__ float smem[S::kSmemFloats];
   __shared__ int s_last;
   float* s_part = smem;                   // [G][D + 2]: merged partial of this chunk
@@ -836,29 +937,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(T::kEp
   const int tid = threadIdx.x;
   const WorkItem it = a.items[blockIdx.x];
   const int pair = it.pair;
-  const int b = pair / a.n_kv_heads, g = pair - b * a.n_kv_heads;
   PairMeta* meta = a.meta + pair;
-  const int len = meta->len;
-  const int lstride = meta->lstride;
-  const int nchunk = meta->nchunk;
-  float* lg = a.logits + (size_t)meta->slot0 * G;  // [G][lstride]
-  float* vn = a.vnorm + meta->slot0;                // [lstride]
+  const PairMeta pm = *meta;  // written only by this pair's tail, after every chunk is done
+  const int len = pm.len;
+  const int lstride = pm.lstride;
+  const int nchunk = pm.nchunk;
+  float* lg = a.logits + (size_t)pm.slot0 * G;  // [G][lstride]
+  float* vn = a.vnorm + pm.slot0;                // [lstride]
   const int row_end = min(it.start + it.count, len);
-
-  // Logit of the incoming token, computed up front so that the tail does not
-  // wait for it (every row lineage gets the same value).
-  float snew[G];
-  {
-    const int c = (tid & 63) % LPR;
-    QReg<T, G> q;
-    load_q<T, G>(q, static_cast<const elem*>(a.q) + ((size_t)b * a.n_q_heads + (size_t)g * G) * D + c * EPL, D,
-                 a.scale_log2);
-    const uint4 kn =
-        *reinterpret_cast<const uint4*>(static_cast<const elem*>(a.k_new) + (size_t)pair * D + c * EPL);
-    const float post_scale = T::kEpl == 8 ? a.scale_log2 : 1.0f;
-#pragma unroll
-    for (int h = 0; h < G; ++h) snew[h] = row_sum<LPR>(qk_part<T, G>(q, h, kn)) * post_scale;
-  }
 
   if constexpr (T::kEpl == 8)
     stream_mfma<D, G>(a, pair, it.start, row_end, lg, vn, lstride, s_work,
@@ -890,26 +976,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(T::kEp
         s_part[h * (D + 2) + D + 1] = sl;
       }
     } else {
-      a.part_acc[(item * G + h) * D + dim] = sa;
-      if (dim == 0) reinterpret_cast<float2*>(a.part_ml)[item * G + h] = make_float2(mm, sl);
+      store_wt(&a.part_acc[(item * G + h) * D + dim], sa);
+      if (dim == 0) store_wt(&reinterpret_cast<float2*>(a.part_ml)[item * G + h], make_float2(mm, sl));
     }
   }
-  __syncthreads();
 
-  if (nchunk > 1) {
-    // Ticket: the barrier orders every wave's partial stores before thread 0's
-    // agent-scope release RMW (one L2 write-back per workgroup); only the last
-    // arrival pays for the acquire before reading the other chunks' partials.
+  if (nchunk == 1) {
+    __syncthreads();  // merged partial complete
+  } else {
+    // Ticket (the hand-over protocol is described at store_wt): every wave
+    // drains its device-scope stores, the barrier orders that before thread
+    // 0's device-scope increment, and the last arrival runs the tail.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
     if (tid == 0) {
-      const unsigned prev = __hip_atomic_fetch_add(&meta->ticket, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-      const bool last = prev + 1 == static_cast<unsigned>(nchunk);
-      if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      s_last = last;
+      const unsigned prev = __hip_atomic_fetch_add(&meta->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = prev + 1 == static_cast<unsigned>(nchunk);
     }
     __syncthreads();
     if (!s_last) return;
   }
-  pair_tail<T, D, G>(a, pair, snew, s_part, s_work);
+  pair_tail<T, D, G>(a, pair, pm, s_part, s_work);
 }
 
 template <class T, int D, int G>
