@@ -69,9 +69,9 @@ struct Shape {
   static constexpr int kRpl = 64 / kLpr;  // rows per wave load
   static constexpr int kU = 4;            // row loads per lane per tile per tensor (double-buffered)
   static constexpr int kTile = kEpl == 8 ? 16 * kWaves : kWaves * kRpl * kU;
-  // LDS: merged chunk partial [G][D + 2] kept for the tail; a region used first
-  // for the cross-wave merge [wave][G][D + 2] and V staging, later by the tail;
-  // then the per-wave logit buffers, which the tail of an unsplit pair reads.
+  // LDS: merged chunk partial [G][D + 2] kept for the tail, then a region used
+  // first for the cross-wave merge [wave][G][D + 2], V staging and the logit
+  // buffers, and later by the tail.
   static constexpr int kPartFloats = G * (D + 2);
   static constexpr int kMergeFloats = kWaves * G * (D + 2);
   static constexpr int kTailFloats = kMaxChunks * G + 2 * kWaves * G + kMaxBudget / 32 + 2 * kWaves;
@@ -80,14 +80,14 @@ struct Shape {
   static constexpr int kStageFloats = kEpl == 8 ? kWaves * 16 * kStageRowBytes / 4 : 0;
   // bf16: per-wave logit buffer [G][kLogitRows], written out in kLogitRows-row
   // runs.  Logit stores leaving the chip interleave DRAM writes with the K/V
-  // read stream and cost far more than their bytes; fewer, larger runs cost
-  // much less (and the last run of an unsplit pair is never written: its tail
-  // reads it here).  Sized to keep two workgroups per compute unit.
+  // read stream and cost far more than their bytes, in proportion to the
+  // number of runs rather than their size: 512-row runs take the throughput
+  // shape from 212 to 180 us per step against 128-row runs.  Sized to keep
+  // two workgroups per compute unit.
   static constexpr int kLogitRows = G <= 5 ? 512 : 256;
   static constexpr int kLogitFloats = kEpl == 8 ? kWaves * G * kLogitRows : 0;
-  static constexpr int kUnionFloats =
-      kMergeFloats + kStageFloats > kTailFloats ? kMergeFloats + kStageFloats : kTailFloats;
-  static constexpr int kSmemFloats = kPartFloats + kUnionFloats + kLogitFloats;
+  static constexpr int kStreamFloats = kMergeFloats + kStageFloats + kLogitFloats;
+  static constexpr int kSmemFloats = kPartFloats + (kStreamFloats > kTailFloats ? kStreamFloats : kTailFloats);
 };
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -316,8 +316,7 @@ __device__ __forceinline__ void wave_argmin(float& s, int& i) {
 // s_part: this workgroup's merged partial ([G][D + 2], used when nchunk == 1);
 // s_tail: scratch of Shape::kTailFloats floats.
 template <class T, int D, int G>
-__device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const float* s_part, float* s_tail,
-                          const float* s_logit) {
+__device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const float* s_part, float* s_tail) {
   using elem = typename T::elem;
   constexpr int kOut = (G * D + kThreads - 1) / kThreads;  // output elements per thread
   constexpr int kCB = G <= 4 ? 8 : 4;                       // chunk partials loaded per batch
@@ -379,20 +378,7 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
   const float* vn = a.vnorm + pm.slot0;                // [lstride]
   // bf16 streaming stores raw q.k; fp32 streaming stores log2-domain logits.
   const float ls = T::kEpl == 8 ? a.scale_log2 : 1.0f;
-  // Logits of 4 slots [base, base + 4) of head h.  For an unsplit bf16 pair the
-  // rows after each wave's last flush are still in its LDS buffer (never
-  // written out); the wave ranges are those of the stream (start 0, end len).
-  constexpr int LR = Shape<T, D, G>::kLogitRows;
-  const int quarter = ((len + kWaves - 1) / kWaves + 15) & ~15;
-  auto logit4 = [&](int h, int base) -> float4 {
-    if (T::kEpl == 8 && !split && base < len) {
-      const int w = base / quarter;
-      const int r0 = w * quarter;
-      const int seg = r0 + (min(r0 + quarter, len) - r0 - 1) / LR * LR;  // first unflushed row of wave w
-      if (base >= seg) return *reinterpret_cast<const float4*>(s_logit + (w * G + h) * LR + (base - seg));
-    }
-    return load_ws(lg + (size_t)h * lstride + base, split);
-  };
+  auto logit4 = [&](int h, int base) { return load_ws(lg + (size_t)h * lstride + base, split); };
   // The first kPre * 4 * kThreads slots' logits (all of them for budgets up to
   // that) are in flight together with everything above.
   float4 lvp[kPre][G];
@@ -746,7 +732,7 @@ __device__ void stream_valu(const StepArgs& a, int pair, int start, int row_end,
 // Leaves the wave's partial in s_merge[wave][G][D + 2] like stream_valu.
 template <int D, int G>
 __device__ void stream_mfma(const StepArgs& a, int pair, int start, int row_end, float* lg, float* vn, int lstride,
-                            float* s_merge, unsigned char* s_stage, float* s_logit, bool keep_last) {
+                            float* s_merge, unsigned char* s_stage, float* s_logit) {
   constexpr int KB = D / 32;  // q.k MFMAs per row group
   constexpr int EV = D / 16;  // value dims per lane per row = P.V MFMAs per value row
   constexpr float kLazy = 8.0f;
@@ -789,8 +775,7 @@ __device__ void stream_mfma(const StepArgs& a, int pair, int start, int row_end,
   // rows clamped to the last valid row (their logits are masked to -inf, so
   // their probabilities are exactly 0).  The raw q.k of every row goes to a
   // per-wave LDS buffer and is written out LR rows at a time as contiguous
-  // runs (see Shape::kLogitRows); with keep_last (an unsplit pair, whose tail
-  // runs in this workgroup) the last run stays in LDS for the tail.
+  // runs (see Shape::kLogitRows).
   constexpr int LR = Shape<BF16T, D, G>::kLogitRows;  // rows per logit flush
   const float scale = a.scale_log2;
   const int quarter = ((row_end - start + kWaves - 1) / kWaves + 15) & ~15;
@@ -927,7 +912,7 @@ __device__ void stream_mfma(const StepArgs& a, int pair, int start, int row_end,
         va[u] = *reinterpret_cast<const VLoad*>(Vp + (size_t)min(Rp + 4 * j + u, last) * D + EV * n);
       process(std::false_type{}, ka, va, Rp);
     }
-    if (flushed < Rend && !keep_last) flush(Rend);
+    if (flushed < Rend) flush(Rend);
   }
   lsum += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(lsum), 0x401F));
   {
@@ -967,10 +952,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(T::kEp
   float* vn = a.vnorm + pm.slot0;                // [lstride]
   const int row_end = min(it.start + it.count, len);
 
-  float* s_logit = s_work + S::kUnionFloats;  // per-wave logit buffers
   if constexpr (T::kEpl == 8)
     stream_mfma<D, G>(a, pair, it.start, row_end, lg, vn, lstride, s_work,
-                      reinterpret_cast<unsigned char*>(s_work + S::kMergeFloats), s_logit, nchunk == 1);
+                      reinterpret_cast<unsigned char*>(s_work + S::kMergeFloats),
+                      s_work + S::kMergeFloats + S::kStageFloats);
   else
     stream_valu<T, D, G>(a, pair, it.start, row_end, lg, vn, lstride, s_work);
   __syncthreads();
@@ -1017,7 +1002,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(T::kEp
     __syncthreads();
     if (!s_last) return;
   }
-  pair_tail<T, D, G>(a, pair, pm, s_part, s_work, s_logit);
+  pair_tail<T, D, G>(a, pair, pm, s_part, s_work);
 }
 
 template <class T, int D, int G>
