@@ -81,10 +81,11 @@ struct Shape {
   // bf16: per-wave logit buffer [G][kLogitRows], written out in kLogitRows-row
   // runs.  Logit stores leaving the chip interleave DRAM writes with the K/V
   // read stream and cost far more than their bytes, in proportion to the
-  // number of runs rather than their size: 512-row runs take the throughput
-  // shape from 212 to 180 us per step against 128-row runs.  Sized to keep
-  // two workgroups per compute unit.
-  static constexpr int kLogitRows = G <= 5 ? 512 : 256;
+  // number of runs rather than their size: against 128-row runs, 512-row runs
+  // take the throughput shape (B64, budget 4096) from 212 to 180 us per step,
+  // 1024-row runs the ragged shape (budgets up to 8192) from 530 to 448 us, at
+  // the price of one workgroup per compute unit for G = 5.
+  static constexpr int kLogitRows = G <= 5 ? 1024 : 256;
   static constexpr int kLogitFloats = kEpl == 8 ? kWaves * G * kLogitRows : 0;
   static constexpr int kStreamFloats = kMergeFloats + kStageFloats + kLogitFloats;
   static constexpr int kSmemFloats = kPartFloats + (kStreamFloats > kTailFloats ? kStreamFloats : kTailFloats);
