@@ -89,6 +89,9 @@ struct Shape {
   static constexpr int kLogitFloats = kEpl == 8 ? kWaves * G * kLogitRows : 0;
   static constexpr int kStreamFloats = kMergeFloats + kStageFloats + kLogitFloats;
   static constexpr int kSmemFloats = kPartFloats + (kStreamFloats > kTailFloats ? kStreamFloats : kTailFloats);
+  // The tail's scratch fits in the merge and staging areas, so the logit
+  // buffers survive into the tail (see resident pairs in the kernel).
+  static_assert(kEpl != 8 || kTailFloats <= kMergeFloats + kStageFloats, "tail scratch overlaps logit buffers");
 };
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -317,7 +320,8 @@ __device__ __forceinline__ void wave_argmin(float& s, int& i) {
 // s_part: this workgroup's merged partial ([G][D + 2], used when nchunk == 1);
 // s_tail: scratch of Shape::kTailFloats floats.
 template <class T, int D, int G>
-__device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const float* s_part, float* s_tail) {
+__device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const float* s_part, float* s_tail,
+                          const float* s_logit, bool resident) {
   using elem = typename T::elem;
   constexpr int kOut = (G * D + kThreads - 1) / kThreads;  // output elements per thread
   constexpr int kCB = G <= 4 ? 8 : 4;                       // chunk partials loaded per batch
@@ -384,12 +388,14 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
   // that) are in flight together with everything above.
   float4 lvp[kPre][G];
   float4 v1p[kPre];
+  if (!resident) {
 #pragma unroll
-  for (int p = 0; p < kPre; ++p) {
-    const int base = min(4 * (tid + p * kThreads), lstride - 4);
+    for (int p = 0; p < kPre; ++p) {
+      const int base = min(4 * (tid + p * kThreads), lstride - 4);
 #pragma unroll
-    for (int h = 0; h < G; ++h) lvp[p][h] = logit4(h, base);
-    v1p[p] = a.vl1 ? load_ws(vn + base, split) : make_float4(1.f, 1.f, 1.f, 1.f);
+      for (int h = 0; h < G; ++h) lvp[p][h] = logit4(h, base);
+      v1p[p] = a.vl1 ? load_ws(vn + base, split) : make_float4(1.f, 1.f, 1.f, 1.f);
+    }
   }
   const int ring_sl = tid < R ? ring_raw : -1;
   float mc[G], lc[G];
@@ -515,17 +521,35 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
       }
     }
   };
+  if (resident) {
+    // Every logit of the pair is still in the streaming waves' LDS buffers:
+    // slot s of wave w = s / quarter sits at row s - w * quarter of its buffer
+    // (the wave ranges of the stream: start 0, end len).
+    constexpr int LR = Shape<T, D, G>::kLogitRows;
+    const int quarter = ((len + kWaves - 1) / kWaves + 15) & ~15;
+    for (int base = 4 * tid; base < len; base += 4 * kThreads) {
+      const int w = base / quarter;
+      const float* src = s_logit + w * G * LR + (base - w * quarter);
+      float4 lv[G];
 #pragma unroll
-  for (int p = 0; p < kPre; ++p)
-    if (4 * (tid + p * kThreads) < len) score4(4 * (tid + p * kThreads), lvp[p], v1p[p]);
+      for (int h = 0; h < G; ++h) lv[h] = *reinterpret_cast<const float4*>(src + h * LR);
+      float4 v1 = make_float4(1.f, 1.f, 1.f, 1.f);
+      if (a.vl1) v1 = load_ws(vn + base, split);
+      score4(base, lv, v1);
+    }
+  } else {
+#pragma unroll
+    for (int p = 0; p < kPre; ++p)
+      if (4 * (tid + p * kThreads) < len) score4(4 * (tid + p * kThreads), lvp[p], v1p[p]);
 #pragma unroll 2
-  for (int base = 4 * (tid + kPre * kThreads); base < len; base += 4 * kThreads) {
-    float4 lv[G];
+    for (int base = 4 * (tid + kPre * kThreads); base < len; base += 4 * kThreads) {
+      float4 lv[G];
 #pragma unroll
-    for (int h = 0; h < G; ++h) lv[h] = logit4(h, base);
-    float4 v1 = make_float4(1.f, 1.f, 1.f, 1.f);
-    if (a.vl1) v1 = load_ws(vn + base, split);
-    score4(base, lv, v1);
+      for (int h = 0; h < G; ++h) lv[h] = logit4(h, base);
+      float4 v1 = make_float4(1.f, 1.f, 1.f, 1.f);
+      if (a.vl1) v1 = load_ws(vn + base, split);
+      score4(base, lv, v1);
+    }
   }
   wave_argmin(best, besti);
   if (lane == 0) {
@@ -733,7 +757,7 @@ __device__ void stream_valu(const StepArgs& a, int pair, int start, int row_end,
 // Leaves the wave's partial in s_merge[wave][G][D + 2] like stream_valu.
 template <int D, int G>
 __device__ void stream_mfma(const StepArgs& a, int pair, int start, int row_end, float* lg, float* vn, int lstride,
-                            float* s_merge, unsigned char* s_stage, float* s_logit) {
+                            float* s_merge, unsigned char* s_stage, float* s_logit, bool keep_last) {
   constexpr int KB = D / 32;  // q.k MFMAs per row group
   constexpr int EV = D / 16;  // value dims per lane per row = P.V MFMAs per value row
   constexpr float kLazy = 8.0f;
@@ -776,7 +800,8 @@ __device__ void stream_mfma(const StepArgs& a, int pair, int start, int row_end,
   // rows clamped to the last valid row (their logits are masked to -inf, so
   // their probabilities are exactly 0).  The raw q.k of every row goes to a
   // per-wave LDS buffer and is written out LR rows at a time as contiguous
-  // runs (see Shape::kLogitRows).
+  // runs (see Shape::kLogitRows).  With keep_last (an unsplit pair whose wave
+  // ranges fit the buffers) nothing is written: the tail reads the buffers.
   constexpr int LR = Shape<BF16T, D, G>::kLogitRows;  // rows per logit flush
   const float scale = a.scale_log2;
   const int quarter = ((row_end - start + kWaves - 1) / kWaves + 15) & ~15;
@@ -913,7 +938,7 @@ __device__ void stream_mfma(const StepArgs& a, int pair, int start, int row_end,
         va[u] = *reinterpret_cast<const VLoad*>(Vp + (size_t)min(Rp + 4 * j + u, last) * D + EV * n);
       process(std::false_type{}, ka, va, Rp);
     }
-    if (flushed < Rend) flush(Rend);
+    if (flushed < Rend && !keep_last) flush(Rend);
   }
   lsum += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(lsum), 0x401F));
   {
@@ -953,10 +978,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(T::kEp
   float* vn = a.vnorm + pm.slot0;                // [lstride]
   const int row_end = min(it.start + it.count, len);
 
+  // An unsplit bf16 pair whose wave ranges fit the logit buffers keeps its
+  // logits in LDS: the tail runs in this workgroup and reads them there.
+  float* s_logit = s_work + S::kMergeFloats + S::kStageFloats;
+  const int quarter = ((row_end - it.start + kWaves - 1) / kWaves + 15) & ~15;
+  const bool resident = T::kEpl == 8 && nchunk == 1 && quarter <= S::kLogitRows;
   if constexpr (T::kEpl == 8)
     stream_mfma<D, G>(a, pair, it.start, row_end, lg, vn, lstride, s_work,
-                      reinterpret_cast<unsigned char*>(s_work + S::kMergeFloats),
-                      s_work + S::kMergeFloats + S::kStageFloats);
+                      reinterpret_cast<unsigned char*>(s_work + S::kMergeFloats), s_logit, resident);
   else
     stream_valu<T, D, G>(a, pair, it.start, row_end, lg, vn, lstride, s_work);
   __syncthreads();
@@ -1003,7 +1032,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(T::kEp
     __syncthreads();
     if (!s_last) return;
   }
-  pair_tail<T, D, G>(a, pair, pm, s_part, s_work);
+  pair_tail<T, D, G>(a, pair, pm, s_part, s_work, s_logit, resident);
 }
 
 template <class T, int D, int G>
