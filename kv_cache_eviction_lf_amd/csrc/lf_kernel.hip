@@ -508,17 +508,21 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
     sc[1] *= v1.y;
     sc[2] *= v1.z;
     sc[3] *= v1.w;
+    if (dbg) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (base + j < len) dbg[base + j] = sc[j];
+    }
+    // Branch-free masked minimum; i increases per thread, so the strict
+    // comparison keeps the first index on ties.
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int i = base + j;
-      if (i < len) {
-        if (dbg) dbg[i] = sc[j];
-        const bool prot = i < a.sink || ((bits >> j) & 1u);
-        if (!prot && sc[j] < best) {  // i increases per thread: first index kept on ties
-          best = sc[j];
-          besti = i;
-        }
-      }
+      const bool ok = i < len && i >= a.sink && !((bits >> j) & 1u);
+      const float v = ok ? sc[j] : INFINITY;
+      const bool lt = v < best;
+      best = lt ? v : best;
+      besti = lt ? i : besti;
     }
   };
   if (resident) {
@@ -527,6 +531,7 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
     // (the wave ranges of the stream: start 0, end len).
     constexpr int LR = Shape<T, D, G>::kLogitRows;
     const int quarter = ((len + kWaves - 1) / kWaves + 15) & ~15;
+#pragma unroll 4
     for (int base = 4 * tid; base < len; base += 4 * kThreads) {
       const int w = base / quarter;
       const float* src = s_logit + w * G * LR + (base - w * quarter);
