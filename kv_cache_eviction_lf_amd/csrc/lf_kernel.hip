@@ -88,7 +88,21 @@ struct Shape {
   static constexpr int kLogitRows = G <= 5 ? 1024 : 256;
   static constexpr int kLogitFloats = kEpl == 8 ? kWaves * G * kLogitRows : 0;
   static constexpr int kStreamFloats = kMergeFloats + kStageFloats + kLogitFloats;
-  static constexpr int kSmemFloats = kPartFloats + (kStreamFloats > kTailFloats ? kStreamFloats : kTailFloats);
+  // bf16: the tail's inputs that do not depend on the stream (the group's q,
+  // k_new and v_new rows, the ring of recent slots) are copied to LDS when the
+  // workgroup starts (LDS DMA, no registers held), in 1 KB blocks of 16-byte
+  // cells, then up to kPreRing ring entries.
+  static constexpr int kPreCells = kEpl == 8 ? (G + 2) * D / 8 : 0;
+  static constexpr int kPreBlocks = (kPreCells + 63) / 64;
+  static constexpr int kPreRing = kEpl == 8 ? 256 : 0;
+  static constexpr int kPreFloats = kPreBlocks * 256 + kPreRing;
+  static constexpr int kSmemFloats =
+      kPartFloats + (kStreamFloats > kTailFloats ? kStreamFloats : kTailFloats) + kPreFloats;
+  // Waves per SIMD the register budget is sized for: bf16 workgroups that fit
+  // 3+ per compute unit by LDS get 3 (168 VGPRs), those that fit only fewer
+  // get registers to match.
+  static constexpr int kBlocksByLds = (160 * 1024) / (kSmemFloats * 4);
+  static constexpr int kMinWavesPerSimd = kEpl != 8 ? 1 : kBlocksByLds >= 3 ? 3 : kBlocksByLds < 1 ? 1 : kBlocksByLds;
   // The tail's scratch fits in the merge and staging areas, so the logit
   // buffers survive into the tail (see resident pairs in the kernel).
   static_assert(kEpl != 8 || kTailFloats <= kMergeFloats + kStageFloats, "tail scratch overlaps logit buffers");
@@ -293,6 +307,46 @@ __device__ __forceinline__ void argmin_merge(float& s, int& i, float so, int io)
   }
 }
 
+// Copies a pair's tail inputs to s_pre with LDS DMA (wave 0 of a bf16
+// workgroup, at its start): q of the group [G][D], then the k_new and v_new
+// rows, in 16-byte cells; then ring entries (4-byte cells).  Lanes past the
+// end load a clamped valid cell into padding that nobody reads.
+// Whether wave 0 has no row of the item to stream (then it waits for its
+// prefetch explicitly).
+template <int D>
+__device__ __forceinline__ bool start_wave_empty(int start, int row_end) {
+  const int quarter = ((row_end - start + kWaves - 1) / kWaves + 15) & ~15;
+  return min(start + quarter, row_end) <= start;
+}
+
+template <int D, int G>
+__device__ void prefetch_tail(const StepArgs& a, int pair, float* s_pre) {
+  using S = Shape<BF16T, D, G>;
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  constexpr int QC = G * D / 8, KC = D / 8, NC = S::kPreCells;
+  const int lane = threadIdx.x & 63;
+  const int b = pair / a.n_kv_heads, g = pair - b * a.n_kv_heads;
+  const uint16_t* qg = static_cast<const uint16_t*>(a.q) + ((size_t)b * a.n_q_heads + (size_t)g * G) * D;
+  const uint16_t* kr = static_cast<const uint16_t*>(a.k_new) + (size_t)pair * D;
+  const uint16_t* vr = static_cast<const uint16_t*>(a.v_new) + (size_t)pair * D;
+#pragma unroll
+  for (int blk = 0; blk < S::kPreBlocks; ++blk) {
+    const int c = min(blk * 64 + lane, NC - 1);
+    const uint16_t* src = c < QC ? qg + 8 * c : c < QC + KC ? kr + 8 * (c - QC) : vr + 8 * (c - QC - KC);
+    __builtin_amdgcn_global_load_lds(src, (lds_ptr)(s_pre + blk * 256), 16, 0, 0);
+  }
+  const int R = a.recent;
+  if (R > 0) {
+    const int32_t* ring = a.ring + (size_t)pair * R;
+    float* s_ring = s_pre + S::kPreBlocks * 256;
+#pragma unroll
+    for (int blk = 0; blk < S::kPreRing / 64; ++blk)
+      if (blk * 64 < R)
+        __builtin_amdgcn_global_load_lds(ring + min(blk * 64 + lane, R - 1), (lds_ptr)(s_ring + blk * 64),
+                                         4, 0, 0);
+  }
+}
+
 // Wave-wide lexicographic (score, slot) minimum; every lane gets the result.
 __device__ __forceinline__ void wave_argmin(float& s, int& i) {
   auto step = [&](float so, int io) { argmin_merge(s, i, so, io); };
@@ -321,7 +375,7 @@ __device__ __forceinline__ void wave_argmin(float& s, int& i) {
 // s_tail: scratch of Shape::kTailFloats floats.
 template <class T, int D, int G>
 __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const float* s_part, float* s_tail,
-                          const float* s_logit, bool resident) {
+                          const float* s_logit, bool resident, const float* s_pre) {
   using elem = typename T::elem;
   constexpr int kOut = (G * D + kThreads - 1) / kThreads;  // output elements per thread
   constexpr int kCB = G <= 4 ? 8 : 4;                       // chunk partials loaded per batch
@@ -346,13 +400,19 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
   // back and one wait covers them; out-of-range lanes are masked where used.
   using S = Shape<T, D, G>;
   constexpr int EPL = S::kEpl, LPR = S::kLpr;
+  // bf16: q, k_new, v_new and the first ring entries were copied to s_pre when
+  // the workgroup started (prefetch_tail).
+  constexpr bool kPre16 = T::kEpl == 8;
+  const elem* pre = reinterpret_cast<const elem*>(s_pre);
+  const elem* qsrc = kPre16 ? pre : static_cast<const elem*>(a.q) + ((size_t)b * a.n_q_heads + (size_t)g * G) * D;
+  const elem* knsrc = kPre16 ? pre + G * D : static_cast<const elem*>(a.k_new) + (size_t)pair * D;
+  const elem* vnsrc = kPre16 ? pre + (G + 1) * D : static_cast<const elem*>(a.v_new) + (size_t)pair * D;
   QReg<T, G> q;
   uint4 kn;
   {
     const int c = lane % LPR;
-    load_q<T, G>(q, static_cast<const elem*>(a.q) + ((size_t)b * a.n_q_heads + (size_t)g * G) * D + c * EPL, D,
-                 a.scale_log2);
-    kn = *reinterpret_cast<const uint4*>(static_cast<const elem*>(a.k_new) + (size_t)pair * D + c * EPL);
+    load_q<T, G>(q, qsrc + c * EPL, D, a.scale_log2);
+    kn = *reinterpret_cast<const uint4*>(knsrc + c * EPL);
   }
   float2 ml[G];
   if (split) {
@@ -361,13 +421,15 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
     for (int h = 0; h < G; ++h) ml[h] = load_x(&src[h]);
   }
   const int32_t* ring = a.ring + (size_t)pair * R;
-  const int ring_raw = R > 0 ? ring[min(tid, R - 1)] : -1;
+  const int32_t* ring_src =
+      kPre16 ? reinterpret_cast<const int32_t*>(s_pre + Shape<T, D, G>::kPreBlocks * 256) : ring;  // first kThreads
+  const int ring_raw = R > 0 ? ring_src[min(tid, R - 1)] : -1;
   uint4 ins;
   {
     const int c = min(tid, 2 * kVec - 1), which = c / kVec, part = c - which * kVec;
-    ins = reinterpret_cast<const uint4*>(static_cast<const elem*>(which ? a.v_new : a.k_new) + (size_t)pair * D)[part];
+    ins = reinterpret_cast<const uint4*>(which ? vnsrc : knsrc)[part];
   }
-  const elem* vnp = static_cast<const elem*>(a.v_new) + (size_t)pair * D;
+  const elem* vnp = vnsrc;
   const float* pacc = a.part_acc + (size_t)item0 * G * D;
   float vnv[kOut], pa[kOut][kCB];
 #pragma unroll
@@ -964,7 +1026,7 @@ __device__ void stream_mfma(const StepArgs& a, int pair, int start, int row_end,
 }
 
 template <class T, int D, int G>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(T::kEpl == 8 ? 3 : 1, 8))) void lf_step_kernel(StepArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Shape<T, D, G>::kMinWavesPerSimd, 8))) void lf_step_kernel(StepArgs a) {
   using S = Shape<T, D, G>;
   __shared__ float smem[S::kSmemFloats];
   __shared__ int s_last;
@@ -986,6 +1048,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(T::kEp
   // An unsplit bf16 pair whose wave ranges fit the logit buffers keeps its
   // logits in LDS: the tail runs in this workgroup and reads them there.
   float* s_logit = s_work + S::kMergeFloats + S::kStageFloats;
+  float* s_pre = smem + S::kSmemFloats - S::kPreFloats;  // prefetched tail inputs
+  if constexpr (T::kEpl == 8) {
+    if (tid < 64) {
+      prefetch_tail<D, G>(a, pair, s_pre);
+      // Completion is implied by this wave's first stream wait (loads return in
+      // order); a wave with nothing to stream waits for it here.
+      if (start_wave_empty<D>(it.start, row_end)) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+  }
   const int quarter = ((row_end - it.start + kWaves - 1) / kWaves + 15) & ~15;
   const bool resident = T::kEpl == 8 && nchunk == 1 && quarter <= S::kLogitRows;
   if constexpr (T::kEpl == 8)
@@ -1037,7 +1108,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(T::kEp
     __syncthreads();
     if (!s_last) return;
   }
-  pair_tail<T, D, G>(a, pair, pm, s_part, s_work, s_logit, resident);
+  pair_tail<T, D, G>(a, pair, pm, s_part, s_work, s_logit, resident, s_pre);
 }
 
 template <class T, int D, int G>
