@@ -380,7 +380,9 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
   constexpr int kOut = (G * D + kThreads - 1) / kThreads;  // output elements per thread
   constexpr int kCB = G <= 4 ? 8 : 4;                       // chunk partials loaded per batch
   constexpr int kVec = D * sizeof(elem) / 16;               // 16-byte pieces of one K/V row
-  constexpr int kPre = G <= 2 ? 8 : 16 / G;                  // float4 logit cells per head preloaded
+  // float4 logit cells per head preloaded (more when the register budget is
+  // not sized for 3 waves per SIMD)
+  constexpr int kPre = Shape<T, D, G>::kMinWavesPerSimd == 1 ? 32 / G : (G <= 2 ? 8 : 16 / G);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   PairMeta* meta = a.meta + pair;
   const int b = pair / a.n_kv_heads, g = pair - b * a.n_kv_heads;
