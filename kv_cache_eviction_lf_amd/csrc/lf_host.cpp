@@ -26,6 +26,7 @@ struct lf_cache {
   void* v_cache;
   char* state;
   float scale_log2;
+  int32_t u_budget;  // the common budget when every sequence has the same one, else 0
 };
 
 namespace {
@@ -226,6 +227,9 @@ lf_status step_impl(const void* q, const void* k_new, const void* v_new, lf_cach
   a.recent = cfg.recent;
   a.scale_log2 = cache->scale_log2;
   a.vl1 = cfg.score == LF_SCORE_VL1;
+  a.u_budget = cache->u_budget;
+  a.u_chunk = L.chunk;
+  a.u_nchunk = cache->u_budget > 0 ? (cache->u_budget + L.chunk - 1) / L.chunk : 0;
   if (lf::launch_step(cfg.dtype, cfg.head_dim, cache->group, a, stream, g_err, sizeof(g_err)))
     return LF_ERR_HIP;
   return LF_OK;
@@ -314,6 +318,9 @@ lf_status lf_init_cache(const lf_config* cfg, const int32_t* budgets, const int6
   c->cfg = *cfg;
   c->group = cfg->n_q_heads / cfg->n_kv_heads;
   c->lay = L;
+  c->u_budget = bud[0];
+  for (int b = 1; b < cfg->batch; ++b)
+    if (bud[b] != bud[0]) c->u_budget = 0;
   c->k_cache = k_cache;
   c->v_cache = v_cache;
   c->state = static_cast<char*>(state);

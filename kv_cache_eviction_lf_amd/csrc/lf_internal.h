@@ -80,6 +80,12 @@ struct StepArgs {
   int32_t recent;
   float scale_log2;  // softmax scale * log2(e)
   int32_t vl1;
+  // Equal budgets: item i is chunk i % u_nchunk of pair i / u_nchunk, rows
+  // [c * u_chunk, min((c + 1) * u_chunk, u_budget)); the kernel computes it
+  // instead of loading items[i].  u_budget = 0 otherwise.
+  int32_t u_budget;
+  int32_t u_chunk;
+  int32_t u_nchunk;
 };
 
 // Tile height (rows per workgroup per pass) of the kernel for a shape; chunk

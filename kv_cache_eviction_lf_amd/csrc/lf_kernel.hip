@@ -103,6 +103,11 @@ struct Shape {
   // get registers to match.
   static constexpr int kBlocksByLds = (160 * 1024) / (kSmemFloats * 4);
   static constexpr int kMinWavesPerSimd = kEpl != 8 ? 1 : kBlocksByLds >= 3 ? 3 : kBlocksByLds < 1 ? 1 : kBlocksByLds;
+  // K/V groups in flight per wave in the streaming loop (current one
+  // included).  A third where one wave per SIMD leaves the registers for it
+  // and it was measured to pay: with G = 4 it does (2 % at 4096-slot pairs),
+  // with G = 5 (and 4 stages for G = 4) it cost about 1 %.
+  static constexpr int kStages = kMinWavesPerSimd == 1 && G <= 4 ? 3 : 2;
   // The tail's scratch fits in the merge and staging areas, so the logit
   // buffers survive into the tail (see resident pairs in the kernel).
   static_assert(kEpl != 8 || kTailFloats <= kMergeFloats + kStageFloats, "tail scratch overlaps logit buffers");
@@ -193,6 +198,10 @@ __device__ __forceinline__ float wave_sum(float x) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Non-temporal (streaming) 16- and 8-byte loads.
+// The wave's index in the workgroup, in a scalar register: loop bounds
+// derived from it then stay scalar and their loops use scalar branches.
+__device__ __forceinline__ int wave_index() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
 __device__ __forceinline__ uint4 load_nt(const uint4* p) {
   typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
   const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
@@ -311,14 +320,6 @@ __device__ __forceinline__ void argmin_merge(float& s, int& i, float so, int io)
 // workgroup, at its start): q of the group [G][D], then the k_new and v_new
 // rows, in 16-byte cells; then ring entries (4-byte cells).  Lanes past the
 // end load a clamped valid cell into padding that nobody reads.
-// Whether wave 0 has no row of the item to stream (then it waits for its
-// prefetch explicitly).
-template <int D>
-__device__ __forceinline__ bool start_wave_empty(int start, int row_end) {
-  const int quarter = ((row_end - start + kWaves - 1) / kWaves + 15) & ~15;
-  return min(start + quarter, row_end) <= start;
-}
-
 template <int D, int G>
 __device__ void prefetch_tail(const StepArgs& a, int pair, float* s_pre) {
   using S = Shape<BF16T, D, G>;
@@ -383,7 +384,7 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
   // float4 logit cells per head preloaded (more when the register budget is
   // not sized for 3 waves per SIMD)
   constexpr int kPre = Shape<T, D, G>::kMinWavesPerSimd == 1 ? 32 / G : (G <= 2 ? 8 : 16 / G);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
   PairMeta* meta = a.meta + pair;
   const int b = pair / a.n_kv_heads, g = pair - b * a.n_kv_heads;
   const int t = pm.t, len = pm.len, budget = pm.budget;
@@ -592,9 +593,9 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
   if (resident) {
     // Every logit of the pair is still in the streaming waves' LDS buffers:
     // slot s of wave w = s / quarter sits at row s - w * quarter of its buffer
-    // (the wave ranges of the stream: start 0, end len).
+    // (the wave ranges of the stream: the item is [0, budget)).
     constexpr int LR = Shape<T, D, G>::kLogitRows;
-    const int quarter = ((len + kWaves - 1) / kWaves + 15) & ~15;
+    const int quarter = ((budget + kWaves - 1) / kWaves + 15) & ~15;
 #pragma unroll 4
     for (int base = 4 * tid; base < len; base += 4 * kThreads) {
       const int w = base / quarter;
@@ -667,7 +668,7 @@ __device__ void stream_valu(const StepArgs& a, int pair, int start, int row_end,
   using S = Shape<T, D, G>;
   constexpr int EPL = S::kEpl, LPR = S::kLpr, RPL = S::kRpl, U = S::kU, TILE = S::kTile;
   using elem = typename T::elem;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
   const int r = lane / LPR, c = lane % LPR;
   const int b = pair / a.n_kv_heads, g = pair - b * a.n_kv_heads;
   QReg<T, G> q;
@@ -825,8 +826,8 @@ __device__ void stream_valu(const StepArgs& a, int pair, int start, int row_end,
 //    equal the eager form up to rounding.
 // Leaves the wave's partial in s_merge[wave][G][D + 2] like stream_valu.
 template <int D, int G>
-__device__ void stream_mfma(const StepArgs& a, int pair, int start, int row_end, float* lg, float* vn, int lstride,
-                            float* s_merge, unsigned char* s_stage, float* s_logit, bool keep_last) {
+__device__ void stream_mfma(const StepArgs& a, int pair, int start, int count, PairMeta& pm, bool& keep_last,
+                            float* s_merge, unsigned char* s_stage, float* s_logit) {
   constexpr int KB = D / 32;  // q.k MFMAs per row group
   constexpr int EV = D / 16;  // value dims per lane per row = P.V MFMAs per value row
   constexpr float kLazy = 8.0f;
@@ -837,19 +838,35 @@ __device__ void stream_mfma(const StepArgs& a, int pair, int start, int row_end,
   typedef float f32x4_t __attribute__((ext_vector_type(4)));
   constexpr int RS = D * 2 + 32;  // staged row stride in bytes
   constexpr int NB = D / 16;      // value-dim blocks
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
   const int n = lane & 15, j = lane >> 4;
   const int b = pair / a.n_kv_heads, g = pair - b * a.n_kv_heads;
   const size_t pair_off = (size_t)pair * a.max_budget * D;
   const uint16_t* Kp = static_cast<const uint16_t*>(a.k_cache) + pair_off;
   const uint16_t* Vp = static_cast<const uint16_t*>(a.v_cache) + pair_off;
 
+  // The pair's metadata comes in by vector loads issued first, so that waiting
+  // for it (below, after the first K/V rows are requested) covers nothing else;
+  // a scalar load would be waited for with every other scalar load, before any
+  // K/V row is requested.
+  int4 m0, m1;
+  {
+    int z;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(z));  // address looks per-lane: a vector load
+    const int4* mp = reinterpret_cast<const int4*>(a.meta + pair) + z;
+    m0 = mp[0];
+    m1 = mp[1];
+  }
+
   uint4 qb[KB];
   {
-    const uint16_t* qh = static_cast<const uint16_t*>(a.q) + ((size_t)b * a.n_q_heads + (size_t)g * G + n) * D + 8 * j;
+    // Lanes past the group's heads load head 0's row (always valid) and never
+    // use it: an unconditional load is not waited for at once.
+    const int hq = n < G ? n : 0;
+    const uint16_t* qh = static_cast<const uint16_t*>(a.q) + ((size_t)b * a.n_q_heads + (size_t)g * G + hq) * D + 8 * j;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
-      qb[kb] = n < G ? *reinterpret_cast<const uint4*>(qh + 32 * kb) : make_uint4(0, 0, 0, 0);
+      qb[kb] = *reinterpret_cast<const uint4*>(qh + 32 * kb);
   }
   f32x4_t acc[NB];
 #pragma unroll
@@ -873,16 +890,21 @@ __device__ void stream_mfma(const StepArgs& a, int pair, int start, int row_end,
   // ranges fit the buffers) nothing is written: the tail reads the buffers.
   constexpr int LR = Shape<BF16T, D, G>::kLogitRows;  // rows per logit flush
   const float scale = a.scale_log2;
-  const int quarter = ((row_end - start + kWaves - 1) / kWaves + 15) & ~15;
+  // Wave ranges split the item's rows [start, start + count), not the filled
+  // ones: they do not depend on the fill level, so the first group's loads can
+  // be issued before the pair's metadata arrives (rows past the fill level are
+  // inside the cache allocation and simply not used).
+  const int quarter = ((count + kWaves - 1) / kWaves + 15) & ~15;
   const int R0 = start + wave * quarter;
-  const int Rend = min(R0 + quarter, row_end);
-  const int nfull = Rend - R0 >= 16 ? (Rend - R0) / 16 : 0;
-  const int Rp = R0 + 16 * nfull;  // first row of the ragged group, if any
   const uint16_t* kp = Kp + (size_t)(R0 + n) * D + 8 * j;
   const uint16_t* vp = Vp + (size_t)(R0 + 4 * j) * D + EV * n;
   float* lbuf = s_logit + wave * G * LR;  // [G][LR]
   int flushed = R0;                       // rows below this are already in HBM
-  const __amdgpu_buffer_rsrc_t lrs = wt_rsrc(lg, G * lstride * 4);
+  // Known once the metadata has arrived (see below).
+  int row_end = 0, Rend = 0, nfull = 0, Rp = 0, lstride = 0;
+  float* lg = nullptr;
+  float* vn = nullptr;
+  __amdgpu_buffer_rsrc_t lrs;
 
   auto flush = [&](int upto) {  // write buffered logits of rows [flushed, upto)
     // Fixed trip count (no data-dependent loop): the compiler can then count
@@ -904,11 +926,32 @@ __device__ void stream_mfma(const StepArgs& a, int pair, int start, int row_end,
   };
   // K/V are read once per step: non-temporal loads keep them from displacing
   // the workspace (logits, partials) in L2 and the Infinity Cache.
-  auto load_full = [&](uint4(&kk)[KB], VLoad(&vv)[4]) {
+  // A group past the wave's full groups is still "loaded", from one line at
+  // the pair's start that every lane shares, and never used: the loads are
+  // issued unconditionally, since a load under a branch makes the wait before
+  // the next group cover every buffer, which drains the pipeline.
+  auto load_grp = [&](uint4(&kk)[KB], VLoad(&vv)[4], bool live) {
+    const uint16_t* k = live ? kp : Kp;
+    const uint16_t* v = live ? vp : Vp;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) kk[kb] = load_nt(reinterpret_cast<const uint4*>(kp + 32 * kb));
+    for (int kb = 0; kb < KB; ++kb) kk[kb] = load_nt(reinterpret_cast<const uint4*>(k + 32 * kb));
 #pragma unroll
-    for (int u = 0; u < 4; ++u) vv[u] = load_nt(reinterpret_cast<const VLoad*>(vp + u * D));
+    for (int u = 0; u < 4; ++u) vv[u] = load_nt(reinterpret_cast<const VLoad*>(v + u * D));
+    kp += 16 * D;
+    vp += 16 * D;
+  };
+  // The first group is loaded before the fill level is known, always (so the
+  // number of loads in flight is fixed when the metadata is waited for), with
+  // rows clamped into the pair's allocation; it is used only if the filled
+  // rows make a full group there.
+  auto load_first = [&](uint4(&kk)[KB], VLoad(&vv)[4]) {
+    const int mb1 = a.max_budget - 1;
+    const uint16_t* k0 = Kp + (size_t)min(R0 + n, mb1) * D + 8 * j;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) kk[kb] = load_nt(reinterpret_cast<const uint4*>(k0 + 32 * kb));
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      vv[u] = load_nt(reinterpret_cast<const VLoad*>(Vp + (size_t)min(R0 + 4 * j + u, mb1) * D + EV * n));
     kp += 16 * D;
     vp += 16 * D;
   };
@@ -982,30 +1025,64 @@ __device__ void stream_mfma(const StepArgs& a, int pair, int start, int row_end,
     }
   };
   {
-    uint4 ka[KB], kb2[KB];
-    VLoad va[4], vb[4];
+    // Ring of NS group buffers: while group g is processed, groups up to
+    // g + NS - 1 are in flight.
+    constexpr int NS = Shape<BF16T, D, G>::kStages;
+    uint4 kbuf[NS][KB];
+    VLoad vbuf[NS][4];
     int g = 0;
-    if (nfull > 0) load_full(ka, va);
-    while (g < nfull) {
-      if (g + 1 < nfull) load_full(kb2, vb);
-      process(std::true_type{}, ka, va, R0 + 16 * g);
+    load_first(kbuf[0], vbuf[0]);
+    // Keeps the compiler from sinking those loads into the branch that uses
+    // them, which would put them behind the wait for the metadata.
+    asm volatile("" ::: "memory");
+    pm.t = __builtin_amdgcn_readfirstlane(m0.x);
+    pm.len = __builtin_amdgcn_readfirstlane(m0.y);
+    pm.budget = __builtin_amdgcn_readfirstlane(m0.z);
+    pm.nchunk = __builtin_amdgcn_readfirstlane(m0.w);
+    pm.item0 = __builtin_amdgcn_readfirstlane(m1.x);
+    pm.slot0 = __builtin_amdgcn_readfirstlane(m1.y);
+    pm.ticket = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(m1.z));
+    pm.lstride = __builtin_amdgcn_readfirstlane(m1.w);
+    row_end = min(start + count, pm.len);
+    Rend = min(R0 + quarter, row_end);
+    nfull = Rend - R0 >= 16 ? (Rend - R0) / 16 : 0;
+    Rp = R0 + 16 * nfull;  // first row of the ragged group, if any
+    lstride = pm.lstride;
+    lg = a.logits + (size_t)pm.slot0 * G;  // [G][lstride]
+    vn = a.vnorm + pm.slot0;                // [lstride]
+    lrs = wt_rsrc(lg, G * lstride * 4);
+    // An unsplit pair whose wave ranges fit the buffers keeps its logits here.
+    keep_last = pm.nchunk == 1 && quarter <= LR;
+#pragma unroll
+    for (int s = 1; s < NS - 1; ++s) load_grp(kbuf[s], vbuf[s], s < nfull);
+    auto step = [&](const uint4(&kk)[KB], const VLoad(&vv)[4]) {
+      process(std::true_type{}, kk, vv, R0 + 16 * g);
       ++g;
       if ((g & (LR / 16 - 1)) == 0) flush(R0 + 16 * g);
-      if (g >= nfull) break;
-      if (g + 1 < nfull) load_full(ka, va);
-      process(std::true_type{}, kb2, vb, R0 + 16 * g);
-      ++g;
-      if ((g & (LR / 16 - 1)) == 0) flush(R0 + 16 * g);
+    };
+    // One exit only (at the top): a second exit is merged with it by the
+    // compiler, and the merged path makes the loop's first wait a full drain.
+    while (g + NS <= nfull) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        // kbuf[s] holds group g; the buffer of group g - 1 takes group g + NS - 1.
+        load_grp(kbuf[(s + NS - 1) % NS], vbuf[(s + NS - 1) % NS], g + NS - 1 < nfull);
+        step(kbuf[s], vbuf[s]);
+      }
     }
+    // Fewer than NS full groups are left, all of them already loaded.
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s)
+      if (g < nfull) step(kbuf[s], vbuf[s]);
     if (Rp < Rend) {
       const int last = row_end - 1;
       const uint16_t* kr = Kp + (size_t)min(Rp + n, last) * D + 8 * j;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) ka[kb] = *reinterpret_cast<const uint4*>(kr + 32 * kb);
+      for (int kb = 0; kb < KB; ++kb) kbuf[0][kb] = *reinterpret_cast<const uint4*>(kr + 32 * kb);
 #pragma unroll
       for (int u = 0; u < 4; ++u)
-        va[u] = *reinterpret_cast<const VLoad*>(Vp + (size_t)min(Rp + 4 * j + u, last) * D + EV * n);
-      process(std::false_type{}, ka, va, Rp);
+        vbuf[0][u] = *reinterpret_cast<const VLoad*>(Vp + (size_t)min(Rp + 4 * j + u, last) * D + EV * n);
+      process(std::false_type{}, kbuf[0], vbuf[0], Rp);
     }
     if (flushed < Rend && !keep_last) flush(Rend);
   }
@@ -1027,7 +1104,7 @@ __device__ void stream_mfma(const StepArgs& a, int pair, int start, int row_end,
   }
 }
 
-template <class T, int D, int G>
+template <class T, int D, int G, bool U>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Shape<T, D, G>::kMinWavesPerSimd, 8))) void lf_step_kernel(StepArgs a) {
   using S = Shape<T, D, G>;
   __shared__ float smem[S::kSmemFloats];
@@ -1036,36 +1113,37 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Shape<
   float* s_work = smem + S::kPartFloats;  // cross-wave merge, then tail scratch
 
   const int tid = threadIdx.x;
-  const WorkItem it = a.items[blockIdx.x];
+  // U (equal budgets): the item follows from the block index, so the first
+  // K/V loads wait for no load of the work list.  A separate instantiation:
+  // a run-time branch would make every scalar load of the prologue wait.
+  WorkItem it;
+  if constexpr (U) {
+    it.pair = blockIdx.x / a.u_nchunk;
+    it.chunk = blockIdx.x - it.pair * a.u_nchunk;
+    it.start = it.chunk * a.u_chunk;
+    it.count = min(a.u_chunk, a.u_budget - it.start);
+  } else {
+    it = a.items[blockIdx.x];
+  }
   const int pair = it.pair;
-  PairMeta* meta = a.meta + pair;
-  const PairMeta pm = *meta;  // written only by this pair's tail, after every chunk is done
-  const int len = pm.len;
-  const int lstride = pm.lstride;
-  const int nchunk = pm.nchunk;
-  float* lg = a.logits + (size_t)pm.slot0 * G;  // [G][lstride]
-  float* vn = a.vnorm + pm.slot0;                // [lstride]
-  const int row_end = min(it.start + it.count, len);
-
-  // An unsplit bf16 pair whose wave ranges fit the logit buffers keeps its
-  // logits in LDS: the tail runs in this workgroup and reads them there.
+  PairMeta* meta = a.meta + pair;  // written only by this pair's tail, after every chunk is done
   float* s_logit = s_work + S::kMergeFloats + S::kStageFloats;
   float* s_pre = smem + S::kSmemFloats - S::kPreFloats;  // prefetched tail inputs
+  PairMeta pm;
+  bool resident = false;  // an unsplit bf16 pair whose logits stay in LDS for its tail
   if constexpr (T::kEpl == 8) {
-    if (tid < 64) {
-      prefetch_tail<D, G>(a, pair, s_pre);
-      // Completion is implied by this wave's first stream wait (loads return in
-      // order); a wave with nothing to stream waits for it here.
-      if (start_wave_empty<D>(it.start, row_end)) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
+    if (tid < 64) prefetch_tail<D, G>(a, pair, s_pre);
+    stream_mfma<D, G>(a, pair, it.start, it.count, pm, resident, s_work,
+                      reinterpret_cast<unsigned char*>(s_work + S::kMergeFloats), s_logit);
+    // The prefetch completed before wave 0's first stream wait (loads return in
+    // order); without a row to stream, wave 0 waits for it here.
+    if (tid < 64 && min(it.start + it.count, pm.len) <= it.start) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  } else {
+    pm = *meta;
+    stream_valu<T, D, G>(a, pair, it.start, min(it.start + it.count, pm.len), a.logits + (size_t)pm.slot0 * G,
+                         a.vnorm + pm.slot0, pm.lstride, s_work);
   }
-  const int quarter = ((row_end - it.start + kWaves - 1) / kWaves + 15) & ~15;
-  const bool resident = T::kEpl == 8 && nchunk == 1 && quarter <= S::kLogitRows;
-  if constexpr (T::kEpl == 8)
-    stream_mfma<D, G>(a, pair, it.start, row_end, lg, vn, lstride, s_work,
-                      reinterpret_cast<unsigned char*>(s_work + S::kMergeFloats), s_logit, resident);
-  else
-    stream_valu<T, D, G>(a, pair, it.start, row_end, lg, vn, lstride, s_work);
+  const int nchunk = pm.nchunk;
   __syncthreads();
 
   // Merge the waves' partials into this chunk's partial.
@@ -1115,7 +1193,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Shape<
 
 template <class T, int D, int G>
 void launch_one(const StepArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((lf_step_kernel<T, D, G>), dim3(a.n_items), dim3(kThreads), 0, s, a);
+  if (a.u_budget > 0)
+    hipLaunchKernelGGL((lf_step_kernel<T, D, G, true>), dim3(a.n_items), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((lf_step_kernel<T, D, G, false>), dim3(a.n_items), dim3(kThreads), 0, s, a);
 }
 
 using LaunchFn = void (*)(const StepArgs&, hipStream_t);
