@@ -10,7 +10,7 @@ namespace lf {
 constexpr uint32_t kStateMagic = 0x4C46535Au;  // "LFSZ"
 constexpr uint64_t kHandleMagic = 0x4C46434143484531ull;
 constexpr int kMaxBudget = 65536;  // LDS bitmap of protected slots: kMaxBudget bits
-constexpr int kMaxChunks = 256;    // chunks per (sequence, KV head): one tail thread each
+constexpr int kMaxChunks = 64;     // chunks per (sequence, KV head): one tail lane each
 constexpr int kMaxGroup = 8;
 constexpr int kThreads = 256;      // threads per workgroup (4 wave64)
 constexpr size_t kAlign = 256;

@@ -74,7 +74,10 @@ struct Shape {
   // buffers, and later by the tail.
   static constexpr int kPartFloats = G * (D + 2);
   static constexpr int kMergeFloats = kWaves * G * (D + 2);
-  static constexpr int kTailFloats = kMaxChunks * G + 2 * kWaves * G + kMaxBudget / 32 + 2 * kWaves;
+  // Tail scratch after the merge area: bitmap of protected slots, then the
+  // per-wave argmin candidates (bf16: inside the V staging area).
+  static constexpr int kBitsOffset = kMergeFloats;
+  static constexpr int kTailFloats = kBitsOffset + kMaxBudget / 32 + 2 * kWaves;
   // bf16: per-wave tile of 16 value rows, rows padded by 32 bytes against LDS bank conflicts.
   static constexpr int kStageRowBytes = D * 2 + 32;
   static constexpr int kStageFloats = kEpl == 8 ? kWaves * 16 * kStageRowBytes / 4 : 0;
@@ -240,22 +243,24 @@ __device__ __forceinline__ void store_wt4(__amdgpu_buffer_rsrc_t r, int byte_off
   const u32x4_t x = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)};
   __builtin_amdgcn_raw_buffer_store_b128(x, r, byte_off, 0, 16 /* sc1 */);
 }
-__device__ __forceinline__ float load_x(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Device-scope loads through a buffer resource over [base, base + bytes)
+// ("sc1", the policy of a relaxed agent-scope atomic load, as wide as needed).
+// A load outside the range returns 0 and touches no memory, so the tail issues
+// its loads unconditionally (a load under a branch makes later waits drain
+// every load in flight) and gives an empty range where the data is not needed.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coh_rsrc(const float* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, bytes, 0x00020000);
 }
-__device__ __forceinline__ float2 load_x(const float2* p) {
-  const unsigned long long x =
-      __hip_atomic_load(reinterpret_cast<const unsigned long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return make_float2(__uint_as_float(static_cast<unsigned>(x)), __uint_as_float(static_cast<unsigned>(x >> 32)));
+__device__ __forceinline__ float load_c1(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 16 /* sc1 */));
 }
-__device__ __forceinline__ float4 load_x(const float4* p) {
-  const float2 lo = load_x(reinterpret_cast<const float2*>(p)), hi = load_x(reinterpret_cast<const float2*>(p) + 1);
-  return make_float4(lo.x, lo.y, hi.x, hi.y);
+__device__ __forceinline__ float2 load_c2(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  const auto x = __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 16 /* sc1 */);
+  return make_float2(__uint_as_float(x[0]), __uint_as_float(x[1]));
 }
-// Workspace read in the tail: written by other workgroups when the pair is
-// split, else by this one (then a plain load, which may hit in L2).
-__device__ __forceinline__ float4 load_ws(const float* p, bool split) {
-  return split ? load_x(reinterpret_cast<const float4*>(p)) : *reinterpret_cast<const float4*>(p);
+__device__ __forceinline__ float4 load_c4(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  const auto x = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 16 /* sc1 */);
+  return make_float4(__uint_as_float(x[0]), __uint_as_float(x[1]), __uint_as_float(x[2]), __uint_as_float(x[3]));
 }
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
@@ -348,6 +353,29 @@ __device__ void prefetch_tail(const StepArgs& a, int pair, float* s_pre) {
   }
 }
 
+// LDS bitmap of the pair's protected recent slots (the ring's entries) over
+// its budget, built before the tail: cleared while the chunk partials merge,
+// then set during the ticket's round trip (a barrier between the two).
+__device__ __forceinline__ void clear_protect_bits(uint32_t* bits, int budget) {
+  for (int i = threadIdx.x; i < (budget + 31) >> 5; i += kThreads) bits[i] = 0u;
+}
+template <class T, int D, int G>
+__device__ void set_protect_bits(const StepArgs& a, int pair, int budget, uint32_t* bits, const float* s_pre) {
+  const int R = a.recent, tid = threadIdx.x;
+  const int32_t* ring = a.ring + (size_t)pair * R;
+  // bf16: the first entries were copied to LDS when the workgroup started.
+  const int32_t* first =
+      T::kEpl == 8 ? reinterpret_cast<const int32_t*>(s_pre + Shape<T, D, G>::kPreBlocks * 256) : ring;
+  if (tid < R) {
+    const int sl = first[tid];
+    if (sl >= 0 && sl < budget) atomicOr(&bits[sl >> 5], 1u << (sl & 31));
+  }
+  for (int j = tid + kThreads; j < R; j += kThreads) {
+    const int sl = ring[j];
+    if (sl >= 0 && sl < budget) atomicOr(&bits[sl >> 5], 1u << (sl & 31));
+  }
+}
+
 // Wave-wide lexicographic (score, slot) minimum; every lane gets the result.
 __device__ __forceinline__ void wave_argmin(float& s, int& i) {
   auto step = [&](float so, int io) { argmin_merge(s, i, so, io); };
@@ -393,10 +421,8 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
   const bool split = nchunk > 1;
   const size_t pair_off = (size_t)pair * a.max_budget * D;
 
-  float* s_w = s_tail;                                                     // [kMaxChunks][G] chunk weights
-  float* s_red = s_w + kMaxChunks * G;                                     // [2][kWaves][G]
-  uint32_t* s_bits = reinterpret_cast<uint32_t*>(s_red + 2 * kWaves * G);  // protected slots
-  float* s_arg = reinterpret_cast<float*>(s_bits + kMaxBudget / 32);       // [kWaves] score, [kWaves] slot
+  const uint32_t* s_bits = reinterpret_cast<const uint32_t*>(s_tail + Shape<T, D, G>::kBitsOffset);  // protected slots
+  float* s_arg = s_tail + Shape<T, D, G>::kBitsOffset + kMaxBudget / 32;  // [kWaves] score, [kWaves] slot
 
   // ---- loads that depend on nothing computed here.  Addresses are clamped to
   // valid memory and nothing is branched around, so the loads issue back to
@@ -417,60 +443,62 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
     load_q<T, G>(q, qsrc + c * EPL, D, a.scale_log2);
     kn = *reinterpret_cast<const uint4*>(knsrc + c * EPL);
   }
-  float2 ml[G];
-  if (split) {
-    const float2* src = reinterpret_cast<const float2*>(a.part_ml) + (size_t)(item0 + min(tid, nchunk - 1)) * G;
-#pragma unroll
-    for (int h = 0; h < G; ++h) ml[h] = load_x(&src[h]);
-  }
-  const int32_t* ring = a.ring + (size_t)pair * R;
-  const int32_t* ring_src =
-      kPre16 ? reinterpret_cast<const int32_t*>(s_pre + Shape<T, D, G>::kPreBlocks * 256) : ring;  // first kThreads
-  const int ring_raw = R > 0 ? ring_src[min(tid, R - 1)] : -1;
+  // Chunk partials exist only for a split pair; logits and |v| norms are read
+  // from memory unless the pair is resident (norms only when they are used).
+  const auto ml_rs = coh_rsrc(a.part_ml + (size_t)item0 * G * 2, split ? nchunk * G * 8 : 0);
+  const auto pa_rs = coh_rsrc(a.part_acc + (size_t)item0 * G * D, split ? nchunk * G * D * 4 : 0);
+  const auto lg_rs = coh_rsrc(a.logits + (size_t)pm.slot0 * G, resident ? 0 : G * lstride * 4);  // [G][lstride]
+  const auto vn_rs = coh_rsrc(a.vnorm + pm.slot0, a.vl1 ? lstride * 4 : 0);                     // [lstride]
   uint4 ins;
   {
     const int c = min(tid, 2 * kVec - 1), which = c / kVec, part = c - which * kVec;
     ins = reinterpret_cast<const uint4*>(which ? vnsrc : knsrc)[part];
   }
   const elem* vnp = vnsrc;
-  const float* pacc = a.part_acc + (size_t)item0 * G * D;
-  float vnv[kOut], pa[kOut][kCB];
+  float vnv[kOut];
 #pragma unroll
-  for (int o = 0; o < kOut; ++o) {
-    const int idx = min(tid + o * kThreads, G * D - 1);
-    vnv[o] = load_elem<T>(vnp, idx % D);
-    if (split) {
-#pragma unroll
-      for (int k = 0; k < kCB; ++k) pa[o][k] = load_x(&pacc[(size_t)min(k, nchunk - 1) * G * D + idx]);
-    }
-  }
-  const float* lg = a.logits + (size_t)pm.slot0 * G;  // [G][lstride]
-  const float* vn = a.vnorm + pm.slot0;                // [lstride]
+  for (int o = 0; o < kOut; ++o) vnv[o] = load_elem<T>(vnp, min(tid + o * kThreads, G * D - 1) % D);
   // bf16 streaming stores raw q.k; fp32 streaming stores log2-domain logits.
   const float ls = T::kEpl == 8 ? a.scale_log2 : 1.0f;
-  auto logit4 = [&](int h, int base) { return load_ws(lg + (size_t)h * lstride + base, split); };
-  // The first kPre * 4 * kThreads slots' logits (all of them for budgets up to
-  // that) are in flight together with everything above.
+  auto logit4 = [&](int h, int base) { return load_c4(lg_rs, (h * lstride + base) * 4); };
+  // Norms in the loops below are loaded only when used (no wait otherwise).
+  auto vnorm4 = [&](int base) { return a.vl1 ? load_c4(vn_rs, base * 4) : make_float4(1.f, 1.f, 1.f, 1.f); };
+  // Every workspace value the tail needs first is requested here at once: the
+  // chunk partials and the first kPre * 4 * kThreads slots' logits (all of
+  // them for budgets up to that).  A resident pair needs none of them: it
+  // skips the block, which leaves its waits below with nothing to wait for.
+  float2 ml[G];
+  float pa[kOut][kCB];
   float4 lvp[kPre][G];
   float4 v1p[kPre];
   if (!resident) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) ml[h] = load_c2(ml_rs, (lane * G + h) * 8);  // lane c: chunk c
+#pragma unroll
+    for (int o = 0; o < kOut; ++o) {
+      const int idx = min(tid + o * kThreads, G * D - 1);
+#pragma unroll
+      for (int k = 0; k < kCB; ++k) pa[o][k] = load_c1(pa_rs, (k * G * D + idx) * 4);
+    }
 #pragma unroll
     for (int p = 0; p < kPre; ++p) {
       const int base = min(4 * (tid + p * kThreads), lstride - 4);
 #pragma unroll
       for (int h = 0; h < G; ++h) lvp[p][h] = logit4(h, base);
-      v1p[p] = a.vl1 ? load_ws(vn + base, split) : make_float4(1.f, 1.f, 1.f, 1.f);
+      v1p[p] = load_c4(vn_rs, base * 4);  // empty range unless used (selected at use)
     }
-  }
-  const int ring_sl = tid < R ? ring_raw : -1;
-  float mc[G], lc[G];
+  } else {
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    mc[h] = split && tid < nchunk ? ml[h].x : kNegBig;
-    lc[h] = split && tid < nchunk ? ml[h].y : 0.f;
+    for (int h = 0; h < G; ++h) ml[h] = make_float2(0.f, 0.f);
+#pragma unroll
+    for (int o = 0; o < kOut; ++o)
+#pragma unroll
+      for (int k = 0; k < kCB; ++k) pa[o][k] = 0.f;
   }
-
-  // ---- global max and normaliser over the chunks and the incoming token
+  // ---- global max and normaliser over the chunks and the incoming token.
+  // Every wave computes them itself, lane c holding chunk c (the own merged
+  // partial in lane 0 for an unsplit pair): no LDS exchange, no barrier.  The
+  // reductions give every lane, and every wave, the same bits.
   // Logit of the incoming token (every lane of a row lineage holds it).
   float snew[G];
   {
@@ -478,46 +506,16 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
 #pragma unroll
     for (int h = 0; h < G; ++h) snew[h] = row_sum<LPR>(qk_part<T, G>(q, h, kn)) * post_scale;
   }
-  const int nwords = (budget + 31) >> 5;
-  for (int i = tid; i < nwords; i += kThreads) s_bits[i] = 0u;
-  if (!split && tid == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      mc[h] = s_part[h * (D + 2) + D];
-      lc[h] = s_part[h * (D + 2) + D + 1];
-    }
-  }
+  float M[G], invL[G], en[G], wc[G];  // wc: lane c's chunk weight exp2(m_c - M)
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const float x = wave_max(mc[h]);
-    if (lane == 0) s_red[wave * G + h] = x;
-  }
-  __syncthreads();  // bitmap zeroed, per-wave maxima visible
-  if (ring_sl >= 0 && ring_sl < budget) atomicOr(&s_bits[ring_sl >> 5], 1u << (ring_sl & 31));
-  for (int j = tid + kThreads; j < R; j += kThreads) {
-    const int sl = ring[j];
-    if (sl >= 0 && sl < budget) atomicOr(&s_bits[sl >> 5], 1u << (sl & 31));
-  }
-  float M[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float x = snew[h];
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) x = fmaxf(x, s_red[w * G + h]);
-    M[h] = x;
-    const float wgt = fast_exp2(mc[h] - M[h]);
-    if (tid < nchunk) s_w[tid * G + h] = wgt;
-    const float y = wave_sum(lc[h] * wgt);
-    if (lane == 0) s_red[(kWaves + wave) * G + h] = y;
-  }
-  __syncthreads();  // chunk weights, per-wave sums and the bitmap complete
-  float invL[G], en[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
+    const bool own = split ? lane < nchunk : lane == 0;
+    const float mc = own ? (split ? ml[h].x : s_part[h * (D + 2) + D]) : kNegBig;
+    const float lc = own ? (split ? ml[h].y : s_part[h * (D + 2) + D + 1]) : 0.f;
+    M[h] = fmaxf(wave_max(mc), snew[h]);
+    wc[h] = fast_exp2(mc - M[h]);  // 0 without a chunk
     en[h] = fast_exp2(snew[h] - M[h]);
-    float L = en[h];
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) L += s_red[(kWaves + w) * G + h];
+    const float L = wave_sum(lc * wc[h]) + en[h];
     invL[h] = 1.0f / L;
     if (tid == 0 && a.dbg_lse)
       a.dbg_lse[(size_t)b * a.n_q_heads + g * G + h] = (M[h] + __log2f(L)) * 0.6931471805599453f;
@@ -529,26 +527,30 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
     const int idx = tid + o * kThreads;
     if (idx < G * D) {
       const int h = idx / D;
-      float enh = en[0], il = invL[0];
+      // h is the same on the whole wave (D is a multiple of 64), so lane c's
+      // weight for head h is chunk c's, read with readlane.
+      float enh = en[0], il = invL[0], w = wc[0];
 #pragma unroll
       for (int hh = 1; hh < G; ++hh) {
         enh = h == hh ? en[hh] : enh;
         il = h == hh ? invL[hh] : il;
+        w = h == hh ? wc[hh] : w;
       }
+      auto wchunk = [&](int c) { return __builtin_amdgcn_readlane(__float_as_int(w), c); };
       float acc = enh * vnv[o];
       if (!split) {
-        acc = fmaf(s_part[h * (D + 2) + idx - h * D], s_w[h], acc);
+        acc = fmaf(s_part[h * (D + 2) + idx - h * D], __int_as_float(wchunk(0)), acc);
       } else {
 #pragma unroll
         for (int k = 0; k < kCB; ++k)
-          if (k < nchunk) acc = fmaf(pa[o][k], s_w[k * G + h], acc);
+          if (k < nchunk) acc = fmaf(pa[o][k], __int_as_float(wchunk(k)), acc);
         for (int ci = kCB; ci < nchunk; ci += kCB) {
           float x[kCB];
 #pragma unroll
-          for (int k = 0; k < kCB; ++k) x[k] = ci + k < nchunk ? load_x(&pacc[(size_t)(ci + k) * G * D + idx]) : 0.f;
+          for (int k = 0; k < kCB; ++k) x[k] = load_c1(pa_rs, ((ci + k) * G * D + idx) * 4);
 #pragma unroll
           for (int k = 0; k < kCB; ++k)
-            if (ci + k < nchunk) acc = fmaf(x[k], s_w[(ci + k) * G + h], acc);
+            if (ci + k < nchunk) acc = fmaf(x[k], __int_as_float(wchunk(ci + k)), acc);
         }
       }
       store_elem<T>(a.out, ((size_t)b * a.n_q_heads + g * G + h) * D + idx - h * D, acc * il);
@@ -603,22 +605,19 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
       float4 lv[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) lv[h] = *reinterpret_cast<const float4*>(src + h * LR);
-      float4 v1 = make_float4(1.f, 1.f, 1.f, 1.f);
-      if (a.vl1) v1 = load_ws(vn + base, split);
-      score4(base, lv, v1);
+      score4(base, lv, vnorm4(base));
     }
   } else {
 #pragma unroll
     for (int p = 0; p < kPre; ++p)
-      if (4 * (tid + p * kThreads) < len) score4(4 * (tid + p * kThreads), lvp[p], v1p[p]);
+      if (4 * (tid + p * kThreads) < len)
+        score4(4 * (tid + p * kThreads), lvp[p], a.vl1 ? v1p[p] : make_float4(1.f, 1.f, 1.f, 1.f));
 #pragma unroll 2
     for (int base = 4 * (tid + kPre * kThreads); base < len; base += 4 * kThreads) {
       float4 lv[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) lv[h] = logit4(h, base);
-      float4 v1 = make_float4(1.f, 1.f, 1.f, 1.f);
-      if (a.vl1) v1 = load_ws(vn + base, split);
-      score4(base, lv, v1);
+      score4(base, lv, vnorm4(base));
     }
   }
   wave_argmin(best, besti);
@@ -1145,6 +1144,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Shape<
   }
   const int nchunk = pm.nchunk;
   __syncthreads();
+  uint32_t* s_bits = reinterpret_cast<uint32_t*>(s_work + S::kBitsOffset);
+  clear_protect_bits(s_bits, pm.budget);
 
   // Merge the waves' partials into this chunk's partial.
   const size_t item = blockIdx.x;
@@ -1174,7 +1175,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Shape<
   }
 
   if (nchunk == 1) {
-    __syncthreads();  // merged partial complete
+    __syncthreads();  // merged partial complete, bitmap cleared
+    set_protect_bits<T, D, G>(a, pair, pm.budget, s_bits, s_pre);
+    __syncthreads();
   } else {
     // Ticket (the hand-over protocol is described at store_wt): every wave
     // drains its device-scope stores, the barrier orders that before thread
@@ -1185,6 +1188,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Shape<
       const unsigned prev = __hip_atomic_fetch_add(&meta->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       s_last = prev + 1 == static_cast<unsigned>(nchunk);
     }
+    set_protect_bits<T, D, G>(a, pair, pm.budget, s_bits, s_pre);  // while the ticket is in flight
     __syncthreads();
     if (!s_last) return;
   }

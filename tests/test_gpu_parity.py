@@ -111,6 +111,17 @@ def test_small_chunks_and_cache_stride():
     parity_run(w, 80, chunk_slots=128, max_budget=512, dbg_every=5)
 
 
+@pytest.mark.parametrize("kw,chunk", [
+    (dict(budget_lo=1000, budget_hi=1000, batch=2), 64),                         # 16 chunks, ragged last
+    (dict(budget_lo=4096, budget_hi=4096, batch=1, prefill="full"), 64),         # 64 chunks, the most allowed
+    (dict(budget_lo=900, budget_hi=900, batch=2, n_q_heads=14, n_kv_heads=2), 64),  # G = 7: 15 chunks
+])
+def test_many_chunks(kw, chunk):
+    # more chunks than the tail takes per batch of partial loads, up to the limit
+    w = _small(**kw)
+    parity_run(w, 40, chunk_slots=chunk, dbg_every=4, tag=f" {kw} chunk={chunk}")
+
+
 def test_vl1_on_ragged_small():
     w = _small(budget_lo=150, budget_hi=400, prefill="ragged", batch=4, n_q_heads=14, n_kv_heads=2)
     parity_run(w, 100, score="vl1", dbg_every=9)
