@@ -179,23 +179,13 @@ __device__ __forceinline__ float row_sum(float x) {
   return x;
 }
 
-// Reductions over the 64 lanes of a wave with DPP and lane swaps (no LDS
-// round trips); every lane gets the result.
+// Reduction within each row of 16 lanes (every lane of the row gets it).
 template <class Op>
-__device__ __forceinline__ float wave_reduce(float x, Op op) {
+__device__ __forceinline__ float row_reduce16(float x, Op op) {
   x = op(x, dpp<0xB1>(x));
   x = op(x, dpp<0x4E>(x));
   x = op(x, dpp<0x141>(x));
-  x = op(x, dpp<0x140>(x));
-  x = op(x, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F)));  // lane ^ 16
-  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return op(__uint_as_float(sw[0]), __uint_as_float(sw[1]));  // lane ^ 32
-}
-__device__ __forceinline__ float wave_max(float x) {
-  return wave_reduce(x, [](float u, float v) { return fmaxf(u, v); });
-}
-__device__ __forceinline__ float wave_sum(float x) {
-  return wave_reduce(x, [](float u, float v) { return u + v; });
+  return op(x, dpp<0x140>(x));
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -467,13 +457,19 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
   // chunk partials and the first kPre * 4 * kThreads slots' logits (all of
   // them for budgets up to that).  A resident pair needs none of them: it
   // skips the block, which leaves its waits below with nothing to wait for.
-  float2 ml[G];
+  // Chunk statistics, packed: lane 16 r + c holds, for pass k, head 4 k + r of
+  // chunks c, c + 16, c + 32, c + 48 (j = 0..3).
+  constexpr int KP = (G + 3) / 4;
+  const int prow = lane >> 4, pcol = lane & 15;
+  float2 ml[KP][4];
   float pa[kOut][kCB];
   float4 lvp[kPre][G];
   float4 v1p[kPre];
   if (!resident) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) ml[h] = load_c2(ml_rs, (lane * G + h) * 8);  // lane c: chunk c
+    for (int k = 0; k < KP; ++k)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ml[k][j] = load_c2(ml_rs, ((pcol + 16 * j) * G + min(4 * k + prow, G - 1)) * 8);
 #pragma unroll
     for (int o = 0; o < kOut; ++o) {
       const int idx = min(tid + o * kThreads, G * D - 1);
@@ -489,7 +485,9 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
     }
   } else {
 #pragma unroll
-    for (int h = 0; h < G; ++h) ml[h] = make_float2(0.f, 0.f);
+    for (int k = 0; k < KP; ++k)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ml[k][j] = make_float2(0.f, 0.f);
 #pragma unroll
     for (int o = 0; o < kOut; ++o)
 #pragma unroll
@@ -506,19 +504,47 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
 #pragma unroll
     for (int h = 0; h < G; ++h) snew[h] = row_sum<LPR>(qk_part<T, G>(q, h, kn)) * post_scale;
   }
-  float M[G], invL[G], en[G], wc[G];  // wc: lane c's chunk weight exp2(m_c - M)
+  // Row reductions (16 lanes) over the packed chunk statistics: one pass
+  // serves four heads.  Results are read back per head with readlane, so every
+  // wave holds the same values.
+  float M[G], invL[G], en[G];
+  float wp[KP][4];  // lane (r, c), slot j: weight exp2(m - M) of chunk c + 16 j for head 4 k + r
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const bool own = split ? lane < nchunk : lane == 0;
-    const float mc = own ? (split ? ml[h].x : s_part[h * (D + 2) + D]) : kNegBig;
-    const float lc = own ? (split ? ml[h].y : s_part[h * (D + 2) + D + 1]) : 0.f;
-    M[h] = fmaxf(wave_max(mc), snew[h]);
-    wc[h] = fast_exp2(mc - M[h]);  // 0 without a chunk
-    en[h] = fast_exp2(snew[h] - M[h]);
-    const float L = wave_sum(lc * wc[h]) + en[h];
-    invL[h] = 1.0f / L;
-    if (tid == 0 && a.dbg_lse)
-      a.dbg_lse[(size_t)b * a.n_q_heads + g * G + h] = (M[h] + __log2f(L)) * 0.6931471805599453f;
+  for (int k = 0; k < KP; ++k) {
+    const int h = 4 * k + prow;
+    float sn = snew[0];
+#pragma unroll
+    for (int hh = 1; hh < G; ++hh) sn = h == hh ? snew[hh] : sn;
+    float mcj[4], lcj[4];
+    float mx = kNegBig;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = pcol + 16 * j;
+      const bool own = h < G && (split ? c < nchunk : c == 0);
+      mcj[j] = own ? (split ? ml[k][j].x : s_part[min(h, G - 1) * (D + 2) + D]) : kNegBig;
+      lcj[j] = own ? (split ? ml[k][j].y : s_part[min(h, G - 1) * (D + 2) + D + 1]) : 0.f;
+      mx = fmaxf(mx, mcj[j]);
+    }
+    const float Mh = fmaxf(row_reduce16(mx, [](float u, float v) { return fmaxf(u, v); }), sn);
+    float ls4 = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      wp[k][j] = fast_exp2(mcj[j] - Mh);  // 0 without a chunk
+      ls4 = fmaf(lcj[j], wp[k][j], ls4);
+    }
+    const float enh = fast_exp2(sn - Mh);
+    const float Lh = row_reduce16(ls4, [](float u, float v) { return u + v; }) + enh;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (4 * k + r < G) {
+        M[4 * k + r] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Mh), 16 * r));
+        en[4 * k + r] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(enh), 16 * r));
+        const float L = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Lh), 16 * r));
+        invL[4 * k + r] = 1.0f / L;
+        if (tid == 0 && a.dbg_lse)
+          a.dbg_lse[(size_t)b * a.n_q_heads + g * G + 4 * k + r] = (M[4 * k + r] + __log2f(L)) * 0.6931471805599453f;
+      }
+    }
   }
 
   // ---- output: chunk partials in chunk order + the new token, normalised
@@ -529,14 +555,25 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
       const int h = idx / D;
       // h is the same on the whole wave (D is a multiple of 64), so lane c's
       // weight for head h is chunk c's, read with readlane.
-      float enh = en[0], il = invL[0], w = wc[0];
+      float enh = en[0], il = invL[0];
 #pragma unroll
       for (int hh = 1; hh < G; ++hh) {
         enh = h == hh ? en[hh] : enh;
         il = h == hh ? invL[hh] : il;
-        w = h == hh ? wc[hh] : w;
       }
-      auto wchunk = [&](int c) { return __builtin_amdgcn_readlane(__float_as_int(w), c); };
+      // Chunk c's weight for head h: lane 16 (h % 4) + c % 16, slot c / 16, pass h / 4.
+      float wj[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        wj[j] = wp[0][j];
+#pragma unroll
+        for (int k = 1; k < KP; ++k) wj[j] = (h >> 2) == k ? wp[k][j] : wj[j];
+      }
+      const int wbase = 16 * (h & 3);
+      auto wchunk = [&](int c) {
+        const float w = (c >> 4) == 0 ? wj[0] : (c >> 4) == 1 ? wj[1] : (c >> 4) == 2 ? wj[2] : wj[3];
+        return __builtin_amdgcn_readlane(__float_as_int(w), wbase + (c & 15));
+      };
       float acc = enh * vnv[o];
       if (!split) {
         acc = fmaf(s_part[h * (D + 2) + idx - h * D], __int_as_float(wchunk(0)), acc);
