@@ -229,6 +229,24 @@ def main():
             torch.cuda.synchronize()
             t = a.elapsed_time(b) / 10 * 1e-3
             res[name + "_GBps"] = round((n if name == "read" else 2 * n) / t / 1e9, 1)
+        # Launch floor: a graph of empty 256-workgroup launches, replayed the
+        # way the steps are (per-node cost before any byte moves).
+        nodes = 512
+        g = torch.cuda.CUDAGraph()
+        cs = torch.cuda.Stream()
+        with torch.cuda.graph(g, stream=cs):
+            sh = torch.cuda.current_stream().cuda_stream
+            for _ in range(nodes):
+                _lib.lf_probe_empty(256, sh)
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(cur)
+        for _ in range(4):
+            g.replay()
+        b.record(cur)
+        torch.cuda.synchronize()
+        res["launch_floor_us"] = round(a.elapsed_time(b) * 1e3 / (4 * nodes), 2)
         probe = res
 
     base = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_seconds)

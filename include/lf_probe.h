@@ -2,8 +2,9 @@
  * lf_probe.h - HBM bandwidth probes that sit beside the decode step.
  *
  * They are measuring tools, not part of the decode path: a plain streaming
- * copy (the reference traffic that hardware byte counters are scaled against)
- * and a streaming read (the achievable read bandwidth of the device).  Both
+ * copy (the reference traffic that hardware byte counters are scaled against),
+ * a streaming read (the achievable read bandwidth of the device) and an empty
+ * launch (the per-step floor).  Both
  * use the same 16-byte-per-lane coalesced access pattern as the decode kernel.
  * Device pointers, caller-owned; asynchronous on `stream` (hipStream_t as void*).
  */
@@ -27,6 +28,11 @@ lf_status lf_probe_copy(const void* src, void* dst, size_t bytes, void* stream);
  * into sink, which must hold at least lf_probe_read_sink_words() entries. */
 lf_status lf_probe_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
 int32_t lf_probe_read_sink_words(void);
+
+/* Launch `n_blocks` (>= 1) workgroups of 256 threads that do nothing.  Timed
+ * in a graph of many such nodes it gives the launch floor a decode step of the
+ * same grid pays before moving any byte. */
+lf_status lf_probe_empty(int32_t n_blocks, void* stream);
 
 #ifdef __cplusplus
 }

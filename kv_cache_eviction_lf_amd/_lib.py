@@ -59,6 +59,7 @@ PROTOTYPES = {
     "lf_probe_copy": (c_int32, [c_void_p, c_void_p, c_size_t, c_void_p]),
     "lf_probe_read": (c_int32, [c_void_p, c_size_t, c_void_p, c_void_p]),
     "lf_probe_read_sink_words": (c_int32, []),
+    "lf_probe_empty": (c_int32, [c_int32, c_void_p]),
 }
 
 _lib = None
@@ -156,6 +157,10 @@ def lf_probe_copy(src: int, dst: int, nbytes: int, stream: int = 0) -> None:
 def lf_probe_read(src: int, nbytes: int, sink: int, stream: int = 0) -> None:
     _check(load_library().lf_probe_read(c_void_p(src), c_size_t(nbytes), c_void_p(sink), c_void_p(stream)),
            "lf_probe_read")
+
+
+def lf_probe_empty(n_blocks: int, stream: int = 0) -> None:
+    _check(load_library().lf_probe_empty(c_int32(n_blocks), c_void_p(stream)), "lf_probe_empty")
 
 
 def lf_probe_read_sink_words() -> int:

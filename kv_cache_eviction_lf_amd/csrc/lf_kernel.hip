@@ -305,10 +305,9 @@ __device__ __forceinline__ float qk_part(const QReg<T, G>& q, int h, const uint4
 
 // (score, slot) lexicographic minimum of two candidates.
 __device__ __forceinline__ void argmin_merge(float& s, int& i, float so, int io) {
-  if (so < s || (so == s && io < i)) {
-    s = so;
-    i = io;
-  }
+  const bool lt = so < s || (so == s && io < i);  // selects, no branch
+  s = lt ? so : s;
+  i = lt ? io : i;
 }
 
 // Copies a pair's tail inputs to s_pre with LDS DMA (wave 0 of a bf16
@@ -408,6 +407,7 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
   const int t = pm.t, len = pm.len, budget = pm.budget;
   const int nchunk = pm.nchunk, item0 = pm.item0, lstride = pm.lstride;
   const int R = a.recent;
+  const int ring_pos = R > 0 ? t % R : 0;  // ring entry the incoming token takes
   const bool split = nchunk > 1;
   const size_t pair_off = (size_t)pair * a.max_budget * D;
 
@@ -663,8 +663,17 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
     reinterpret_cast<int*>(s_arg)[kWaves + wave] = besti;
   }
   __syncthreads();
+  {
+    float sw[kWaves];
+    int iw[kWaves];
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) argmin_merge(best, besti, s_arg[w], reinterpret_cast<int*>(s_arg)[kWaves + w]);
+    for (int w = 0; w < kWaves; ++w) {  // all reads first, one wait
+      sw[w] = s_arg[w];
+      iw[w] = reinterpret_cast<int*>(s_arg)[kWaves + w];
+    }
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) argmin_merge(best, besti, sw[w], iw[w]);
+  }
 
   // ---- insert the incoming token: append while filling, else overwrite the victim
   int e, ev;
@@ -685,7 +694,7 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
   }
   if (tid == 0) {
     if (e >= 0) {
-      if (R > 0) a.ring[(size_t)pair * R + (t % R)] = e;
+      if (R > 0) a.ring[(size_t)pair * R + ring_pos] = e;
       meta->t = t + 1;
       meta->len = len < budget ? len + 1 : budget;
     }

@@ -63,6 +63,10 @@ __global__ __launch_bounds__(kProbeThreads) void probe_read_kernel(const uint4* 
   if (threadIdx.x == 0) sink[blockIdx.x] = s[0] ^ s[1] ^ s[2] ^ s[3];
 }
 
+// A workgroup that does nothing: a graph of these measures the per-launch
+// floor (dispatch, workgroup start and retirement, the gap between nodes).
+__global__ __launch_bounds__(kProbeThreads) void probe_empty_kernel() {}
+
 bool bad(const void* p) { return !p || reinterpret_cast<uintptr_t>(p) % 16; }
 
 }  // namespace
@@ -85,6 +89,12 @@ lf_status lf_probe_read(const void* src, size_t bytes, uint32_t* sink, void* str
   if (!bytes) return LF_OK;
   hipLaunchKernelGGL(probe_read_kernel, dim3(kProbeBlocks), dim3(kProbeThreads), 0,
                      static_cast<hipStream_t>(stream), static_cast<const uint4*>(src), bytes / 16, sink);
+  return hipGetLastError() == hipSuccess ? LF_OK : LF_ERR_HIP;
+}
+
+lf_status lf_probe_empty(int32_t n_blocks, void* stream) {
+  if (n_blocks < 1) return LF_ERR_ARG;
+  hipLaunchKernelGGL(probe_empty_kernel, dim3(n_blocks), dim3(kProbeThreads), 0, static_cast<hipStream_t>(stream));
   return hipGetLastError() == hipSuccess ? LF_OK : LF_ERR_HIP;
 }
 

@@ -34,7 +34,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
     assert {"lf_init_cache", "lf_decode_step", "lf_free", "lf_state_bytes", "lf_last_error",
-            "lf_decode_step_dbg", "lf_probe_copy", "lf_probe_read"} <= names
+            "lf_decode_step_dbg", "lf_probe_copy", "lf_probe_read", "lf_probe_empty"} <= names
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True,
                          check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}

@@ -30,3 +30,14 @@ def test_probe_copy_and_read(nbytes):
     want = np.bitwise_xor.reduce(words) if words.size else np.uint32(0)
     got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
     assert got == want
+
+
+def test_probe_empty_launch():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    stream = torch.cuda.current_stream().cuda_stream
+    for n in (1, 256, 4096):
+        _lib.lf_probe_empty(n, stream)
+    torch.cuda.synchronize()
+    with pytest.raises(_lib.LFError):
+        _lib.lf_probe_empty(0, stream)
