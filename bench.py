@@ -40,7 +40,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="llama8b_b8")
     ap.add_argument("--layers", type=int, default=0, help="rotating layer caches (0 = enough to exceed 2x MALL)")
-    ap.add_argument("--score", default="attn", choices=["attn", "vl1"])
+    ap.add_argument("--score", default="attn", choices=["attn", "vl1", "none"],
+                    help="none: the full-cache comparator (attention only, the cache is full and keeps its tokens)")
+    ap.add_argument("--budget", type=int, default=0,
+                    help="override the workload's budget (equal for every sequence, prefill filling it)")
     ap.add_argument("--chunk", type=int, default=0, help="split-KV chunk slots (0 = library default)")
     ap.add_argument("--eager", action="store_true", help="launch step by step instead of replaying HIP graphs")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle baseline")
@@ -49,12 +52,13 @@ def parse():
     return ap.parse_args()
 
 
-def algorithmic_bytes(w, bud) -> int:
+def algorithmic_bytes(w, bud, stored: bool = True) -> int:
     """Bytes one step must move: every cached K and V row read, k_new/v_new read
-    and written into the victim slot, q read and the output written."""
+    and (unless a full comparator cache keeps its tokens) written into the victim
+    slot, q read and the output written."""
     s = 2 if w.dtype == "bf16" else 4
     kv = int(np.sum(bud)) * w.n_kv_heads * w.head_dim * 2 * s
-    new = 2 * w.batch * w.n_kv_heads * w.head_dim * 2 * s
+    new = (2 if stored else 1) * w.batch * w.n_kv_heads * w.head_dim * 2 * s
     qo = 2 * w.batch * w.n_q_heads * w.head_dim * s
     return kv + new + qo
 
@@ -72,17 +76,18 @@ def profiled_traffic(workload: str):
     return rec.get("traffic_bytes_per_launch") if rec.get("kernel_source_sha256") == sha else None
 
 
-def cpu_baseline(w, seconds: float) -> dict:
+def cpu_baseline(w, seconds: float, score: str = "attn") -> dict:
     """Time the float64 oracle as it stands, single-threaded, on the same
     workload (full batch of the first layer) for about `seconds`."""
     from threadpoolctl import threadpool_limits
 
-    from oracle import OracleCache
+    from oracle import SCORE_ATTN, SCORE_NONE, SCORE_VL1, OracleCache
     from workloads import budgets, initial_cache, step_inputs
 
     with threadpool_limits(1):
         ks, vs, ps, ts = initial_cache(w)
-        oc = OracleCache(ks, vs, ps, ts, budgets(w), w.n_q_heads, w.sink, w.recent)
+        oc = OracleCache(ks, vs, ps, ts, budgets(w), w.n_q_heads, w.sink, w.recent,
+                         score={"vl1": SCORE_VL1, "none": SCORE_NONE}.get(score, SCORE_ATTN))
         inputs = [step_inputs(w, s) for s in range(4)]
         oc.step(*inputs[0])  # warm-up
         n, t0 = 0, time.perf_counter()
@@ -116,8 +121,10 @@ def main():
     lib = _lib.load_library()
     dev = torch.device("cuda:0")
     w = get_workload(args.workload)
+    if args.budget:
+        w = w.with_(budget_lo=args.budget, budget_hi=args.budget, prefill="full")
     bud = budgets(w)
-    step_bytes = algorithmic_bytes(w, bud)
+    step_bytes = algorithmic_bytes(w, bud, stored=args.score != "none")
     layer_kv = int(np.sum(bud)) * w.n_kv_heads * w.head_dim * 2 * (2 if w.dtype == "bf16" else 4)
     L = args.layers or max(1, math.ceil(2 * MALL_BYTES / layer_kv))
 
@@ -249,9 +256,13 @@ def main():
         res["launch_floor_us"] = round(a.elapsed_time(b) * 1e3 / (4 * nodes), 2)
         probe = res
 
-    base = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_seconds)
+    base = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_seconds, args.score)
+    # counters were taken on the default step of the named workload only
+    profiled = profiled_traffic(w.name) if args.score == "attn" and not args.budget else None
     line = {
-        "metric": "decode steps/s (one fused attention+score+evict step over the batch of one layer)",
+        "metric": ("decode steps/s (full-cache attention step over the batch of one layer, no eviction)"
+                   if args.score == "none" else
+                   "decode steps/s (one fused attention+score+evict step over the batch of one layer)"),
         "value": round(steps_per_s, 1),
         "unit": "steps/s",
         "n_gpus": 1,
@@ -285,7 +296,7 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": profiled_traffic(w.name),
+            "traffic": profiled,
             "bytes_per_launch": step_bytes,
             "kernel": "lf_step_kernel",
         },

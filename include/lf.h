@@ -53,7 +53,14 @@ typedef enum lf_dtype { LF_F32 = 0, LF_BF16 = 1 } lf_dtype;
 
 typedef enum lf_score {
   LF_SCORE_ATTN = 0, /* I_i = sum over the group's query heads of alpha_{h,i} */
-  LF_SCORE_VL1 = 1   /* I_i = (sum_h alpha_{h,i}) * sum_l |v_i[l]|            */
+  LF_SCORE_VL1 = 1,  /* I_i = (sum_h alpha_{h,i}) * sum_l |v_i[l]|            */
+  LF_SCORE_NONE = 2  /* full-cache comparator: attention (a) only, no importance
+                      * and no eviction.  The incoming token is appended while
+                      * the cache has room; once it is full the token is
+                      * attended but not stored (evict_idx = -2).  This is the
+                      * uncompressed cache the pages compare LongFlow against
+                      * (LongFlow summary, section 3), run by the same streaming
+                      * kernel; size max_budget for the longest context.      */
 } lf_score;
 
 typedef struct lf_config {
@@ -123,7 +130,8 @@ lf_status lf_init_cache(const lf_config* cfg, const int32_t* budgets, const int6
  *   out        device [B][Hq][d]    attention output over cache + new token,
  *              rounded to nearest-even when dtype is bf16
  *   evict_idx  device int32 [B][Hkv]: slot overwritten by the new token, or -1
- *              when the cache was not yet full and the token was appended.
+ *              when the cache was not yet full and the token was appended,
+ *              or -2 when the token was not stored (LF_SCORE_NONE, full).
  * Asynchronous and stream-ordered; no host synchronisation, no allocation.
  * Calls on one handle must be ordered on one stream.  Validation is limited to
  * null pointers and the handle; errors: LF_ERR_ARG, LF_ERR_STATE, LF_ERR_HIP.
@@ -135,7 +143,7 @@ lf_status lf_decode_step(const void* q, const void* k_new, const void* v_new, lf
  * lf_decode_step_dbg - lf_decode_step that also exports its intermediates.
  *   scores  device float [B][Hkv][max_budget] or NULL: importance of every
  *           cached slot i < fill level, before the window mask (other entries
- *           are left untouched).
+ *           are left untouched; nothing is written under LF_SCORE_NONE).
  *   lse     device float [B][Hq] or NULL: natural-log softmax normaliser
  *           log(sum_i exp(scale q.k_i)) over cache + new token.
  * Same semantics and errors as lf_decode_step otherwise.

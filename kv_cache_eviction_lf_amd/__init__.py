@@ -8,6 +8,7 @@ from ._lib import (
     LF_F32,
     LF_INIT_ATTACH,
     LF_SCORE_ATTN,
+    LF_SCORE_NONE,
     LF_SCORE_VL1,
     LFError,
     lf_abi_version,
@@ -37,6 +38,7 @@ __all__ = [
     "LF_F32",
     "LF_INIT_ATTACH",
     "LF_SCORE_ATTN",
+    "LF_SCORE_NONE",
     "LF_SCORE_VL1",
     "LFError",
     "LongFlowCache",

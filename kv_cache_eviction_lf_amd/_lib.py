@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblf.so")
 
 LF_OK, LF_ERR_ARG, LF_ERR_UNSUPPORTED, LF_ERR_STATE, LF_ERR_HIP = range(5)
 LF_F32, LF_BF16 = 0, 1
-LF_SCORE_ATTN, LF_SCORE_VL1 = 0, 1
+LF_SCORE_ATTN, LF_SCORE_VL1, LF_SCORE_NONE = 0, 1, 2
 LF_INIT_ATTACH = 1
 STATUS_NAMES = {0: "LF_OK", 1: "LF_ERR_ARG", 2: "LF_ERR_UNSUPPORTED", 3: "LF_ERR_STATE", 4: "LF_ERR_HIP"}
 

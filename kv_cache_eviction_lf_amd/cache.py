@@ -8,10 +8,10 @@ from __future__ import annotations
 import torch
 
 from . import _lib
-from ._lib import LF_BF16, LF_F32, LF_INIT_ATTACH, LF_SCORE_ATTN, LF_SCORE_VL1
+from ._lib import LF_BF16, LF_F32, LF_INIT_ATTACH, LF_SCORE_ATTN, LF_SCORE_NONE, LF_SCORE_VL1
 
 _DTYPES = {torch.bfloat16: LF_BF16, torch.float32: LF_F32}
-_SCORES = {"attn": LF_SCORE_ATTN, "vl1": LF_SCORE_VL1}
+_SCORES = {"attn": LF_SCORE_ATTN, "vl1": LF_SCORE_VL1, "none": LF_SCORE_NONE}
 
 
 def _stream_handle(device) -> int:

@@ -57,8 +57,8 @@ lf_status validate_config(const lf_config* cfg) {
     return fail(LF_ERR_UNSUPPORTED, "head_dim %d; supported 64 and 128", cfg->head_dim);
   if (cfg->dtype != LF_F32 && cfg->dtype != LF_BF16)
     return fail(LF_ERR_UNSUPPORTED, "dtype %d; supported LF_F32 and LF_BF16", cfg->dtype);
-  if (cfg->score != LF_SCORE_ATTN && cfg->score != LF_SCORE_VL1)
-    return fail(LF_ERR_ARG, "score mode %d; expected LF_SCORE_ATTN or LF_SCORE_VL1", cfg->score);
+  if (cfg->score != LF_SCORE_ATTN && cfg->score != LF_SCORE_VL1 && cfg->score != LF_SCORE_NONE)
+    return fail(LF_ERR_ARG, "score mode %d; expected LF_SCORE_ATTN, LF_SCORE_VL1 or LF_SCORE_NONE", cfg->score);
   if (cfg->max_budget < 1 || cfg->max_budget > lf::kMaxBudget)
     return fail(LF_ERR_ARG, "max_budget %d outside [1, %d]", cfg->max_budget, lf::kMaxBudget);
   if (cfg->sink < 0 || cfg->recent < 0) return fail(LF_ERR_ARG, "sink and recent must be >= 0");
@@ -140,8 +140,8 @@ lf_status make_layout(const lf_config* cfg, const std::vector<int32_t>& bud, lf:
   off = align_up(off + sizeof(float) * 2 * group * W);
   L.part_acc = off;
   off = align_up(off + sizeof(float) * (size_t)group * cfg->head_dim * W);
-  L.logits = off;
-  off = align_up(off + sizeof(float) * (size_t)group * S);
+  L.logits = off;  // none without importance (LF_SCORE_NONE)
+  if (cfg->score != LF_SCORE_NONE) off = align_up(off + sizeof(float) * (size_t)group * S);
   L.vnorm = off;
   if (cfg->score == LF_SCORE_VL1) off = align_up(off + sizeof(float) * S);
   L.total = off;
@@ -227,6 +227,7 @@ lf_status step_impl(const void* q, const void* k_new, const void* v_new, lf_cach
   a.recent = cfg.recent;
   a.scale_log2 = cache->scale_log2;
   a.vl1 = cfg.score == LF_SCORE_VL1;
+  a.score_none = cfg.score == LF_SCORE_NONE;
   a.u_budget = cache->u_budget;
   a.u_chunk = L.chunk;
   a.u_nchunk = cache->u_budget > 0 ? (cache->u_budget + L.chunk - 1) / L.chunk : 0;

@@ -80,6 +80,7 @@ struct StepArgs {
   int32_t recent;
   float scale_log2;  // softmax scale * log2(e)
   int32_t vl1;
+  int32_t score_none;  // attention only: no logits, importance or eviction
   // Equal budgets: item i is chunk i % u_nchunk of pair i / u_nchunk, rows
   // [c * u_chunk, min((c + 1) * u_chunk, u_budget)); the kernel computes it
   // instead of loading items[i].  u_budget = 0 otherwise.

@@ -437,7 +437,7 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
   // from memory unless the pair is resident (norms only when they are used).
   const auto ml_rs = coh_rsrc(a.part_ml + (size_t)item0 * G * 2, split ? nchunk * G * 8 : 0);
   const auto pa_rs = coh_rsrc(a.part_acc + (size_t)item0 * G * D, split ? nchunk * G * D * 4 : 0);
-  const auto lg_rs = coh_rsrc(a.logits + (size_t)pm.slot0 * G, resident ? 0 : G * lstride * 4);  // [G][lstride]
+  const auto lg_rs = coh_rsrc(a.logits + (size_t)pm.slot0 * G, resident || a.score_none ? 0 : G * lstride * 4);
   const auto vn_rs = coh_rsrc(a.vnorm + pm.slot0, a.vl1 ? lstride * 4 : 0);                     // [lstride]
   uint4 ins;
   {
@@ -597,82 +597,86 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
   // ---- importance of every filled slot and the masked first-index argmin
   float best = INFINITY;
   int besti = 0x7FFFFFFF;
-  float* dbg = a.dbg_scores ? a.dbg_scores + (size_t)pair * a.max_budget : nullptr;
-  auto score4 = [&](int base, const float4(&lv)[G], const float4& v1) {
-    const uint32_t bits = s_bits[base >> 5] >> (base & 31);
-    float sc[4] = {0.f, 0.f, 0.f, 0.f};
+  // Without importance (score_none) there is no candidate: besti stays past
+  // every slot, so a full cache stores nothing.
+  if (!a.score_none) {
+    float* dbg = a.dbg_scores ? a.dbg_scores + (size_t)pair * a.max_budget : nullptr;
+    auto score4 = [&](int base, const float4(&lv)[G], const float4& v1) {
+      const uint32_t bits = s_bits[base >> 5] >> (base & 31);
+      float sc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      sc[0] = fmaf(fast_exp2(fmaf(lv[h].x, ls, -M[h])), invL[h], sc[0]);
-      sc[1] = fmaf(fast_exp2(fmaf(lv[h].y, ls, -M[h])), invL[h], sc[1]);
-      sc[2] = fmaf(fast_exp2(fmaf(lv[h].z, ls, -M[h])), invL[h], sc[2]);
-      sc[3] = fmaf(fast_exp2(fmaf(lv[h].w, ls, -M[h])), invL[h], sc[3]);
-    }
-    sc[0] *= v1.x;
-    sc[1] *= v1.y;
-    sc[2] *= v1.z;
-    sc[3] *= v1.w;
-    if (dbg) {
+      for (int h = 0; h < G; ++h) {
+        sc[0] = fmaf(fast_exp2(fmaf(lv[h].x, ls, -M[h])), invL[h], sc[0]);
+        sc[1] = fmaf(fast_exp2(fmaf(lv[h].y, ls, -M[h])), invL[h], sc[1]);
+        sc[2] = fmaf(fast_exp2(fmaf(lv[h].z, ls, -M[h])), invL[h], sc[2]);
+        sc[3] = fmaf(fast_exp2(fmaf(lv[h].w, ls, -M[h])), invL[h], sc[3]);
+      }
+      sc[0] *= v1.x;
+      sc[1] *= v1.y;
+      sc[2] *= v1.z;
+      sc[3] *= v1.w;
+      if (dbg) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (base + j < len) dbg[base + j] = sc[j];
-    }
-    // Branch-free masked minimum; i increases per thread, so the strict
-    // comparison keeps the first index on ties.
+        for (int j = 0; j < 4; ++j)
+          if (base + j < len) dbg[base + j] = sc[j];
+      }
+      // Branch-free masked minimum; i increases per thread, so the strict
+      // comparison keeps the first index on ties.
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int i = base + j;
-      const bool ok = i < len && i >= a.sink && !((bits >> j) & 1u);
-      const float v = ok ? sc[j] : INFINITY;
-      const bool lt = v < best;
-      best = lt ? v : best;
-      besti = lt ? i : besti;
-    }
-  };
-  if (resident) {
-    // Every logit of the pair is still in the streaming waves' LDS buffers:
-    // slot s of wave w = s / quarter sits at row s - w * quarter of its buffer
-    // (the wave ranges of the stream: the item is [0, budget)).
-    constexpr int LR = Shape<T, D, G>::kLogitRows;
-    const int quarter = ((budget + kWaves - 1) / kWaves + 15) & ~15;
+      for (int j = 0; j < 4; ++j) {
+        const int i = base + j;
+        const bool ok = i < len && i >= a.sink && !((bits >> j) & 1u);
+        const float v = ok ? sc[j] : INFINITY;
+        const bool lt = v < best;
+        best = lt ? v : best;
+        besti = lt ? i : besti;
+      }
+    };
+    if (resident) {
+      // Every logit of the pair is still in the streaming waves' LDS buffers:
+      // slot s of wave w = s / quarter sits at row s - w * quarter of its buffer
+      // (the wave ranges of the stream: the item is [0, budget)).
+      constexpr int LR = Shape<T, D, G>::kLogitRows;
+      const int quarter = ((budget + kWaves - 1) / kWaves + 15) & ~15;
 #pragma unroll 4
-    for (int base = 4 * tid; base < len; base += 4 * kThreads) {
-      const int w = base / quarter;
-      const float* src = s_logit + w * G * LR + (base - w * quarter);
-      float4 lv[G];
+      for (int base = 4 * tid; base < len; base += 4 * kThreads) {
+        const int w = base / quarter;
+        const float* src = s_logit + w * G * LR + (base - w * quarter);
+        float4 lv[G];
 #pragma unroll
-      for (int h = 0; h < G; ++h) lv[h] = *reinterpret_cast<const float4*>(src + h * LR);
-      score4(base, lv, vnorm4(base));
-    }
-  } else {
+        for (int h = 0; h < G; ++h) lv[h] = *reinterpret_cast<const float4*>(src + h * LR);
+        score4(base, lv, vnorm4(base));
+      }
+    } else {
 #pragma unroll
-    for (int p = 0; p < kPre; ++p)
-      if (4 * (tid + p * kThreads) < len)
-        score4(4 * (tid + p * kThreads), lvp[p], a.vl1 ? v1p[p] : make_float4(1.f, 1.f, 1.f, 1.f));
+      for (int p = 0; p < kPre; ++p)
+        if (4 * (tid + p * kThreads) < len)
+          score4(4 * (tid + p * kThreads), lvp[p], a.vl1 ? v1p[p] : make_float4(1.f, 1.f, 1.f, 1.f));
 #pragma unroll 2
-    for (int base = 4 * (tid + kPre * kThreads); base < len; base += 4 * kThreads) {
-      float4 lv[G];
+      for (int base = 4 * (tid + kPre * kThreads); base < len; base += 4 * kThreads) {
+        float4 lv[G];
 #pragma unroll
-      for (int h = 0; h < G; ++h) lv[h] = logit4(h, base);
-      score4(base, lv, vnorm4(base));
+        for (int h = 0; h < G; ++h) lv[h] = logit4(h, base);
+        score4(base, lv, vnorm4(base));
+      }
     }
-  }
-  wave_argmin(best, besti);
-  if (lane == 0) {
-    s_arg[wave] = best;
-    reinterpret_cast<int*>(s_arg)[kWaves + wave] = besti;
-  }
-  __syncthreads();
-  {
-    float sw[kWaves];
-    int iw[kWaves];
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {  // all reads first, one wait
-      sw[w] = s_arg[w];
-      iw[w] = reinterpret_cast<int*>(s_arg)[kWaves + w];
+    wave_argmin(best, besti);
+    if (lane == 0) {
+      s_arg[wave] = best;
+      reinterpret_cast<int*>(s_arg)[kWaves + wave] = besti;
     }
+    __syncthreads();
+    {
+      float sw[kWaves];
+      int iw[kWaves];
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) argmin_merge(best, besti, sw[w], iw[w]);
+      for (int w = 0; w < kWaves; ++w) {  // all reads first, one wait
+        sw[w] = s_arg[w];
+        iw[w] = reinterpret_cast<int*>(s_arg)[kWaves + w];
+      }
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) argmin_merge(best, besti, sw[w], iw[w]);
+    }
   }
 
   // ---- insert the incoming token: append while filling, else overwrite the victim
@@ -684,7 +688,7 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
     e = besti;
     ev = besti;
   } else {
-    e = -1;  // no evictable slot (prevented by init-time validation)
+    e = -1;  // not stored: score_none on a full cache (no evictable slot is prevented by validation)
     ev = -2;
   }
   if (e >= 0 && tid < 2 * kVec) {
@@ -755,7 +759,7 @@ __device__ void stream_valu(const StepArgs& a, int pair, int start, int row_end,
 #pragma unroll
       for (int h = 0; h < G; ++h) s[u][h] = row_sum<LPR>(qk_part<T, G>(q, h, kk[u])) * post_scale;
       if (row < row_end) {
-        if (c < G) {
+        if (c < G && !a.score_none) {
           float mine = s[u][0];
 #pragma unroll
           for (int h = 1; h < G; ++h) mine = c == h ? s[u][h] : mine;
@@ -954,8 +958,9 @@ __device__ void stream_mfma(const StepArgs& a, int pair, int start, int count, P
   auto flush = [&](int upto) {  // write buffered logits of rows [flushed, upto)
     // Fixed trip count (no data-dependent loop): the compiler can then count
     // the outstanding stores exactly and never waits for them to complete.
+    // Without importance (score_none) nothing is written.
     constexpr int NV = G * LR / 4;  // float4 cells of the buffer
-    const int nrows = upto - flushed;
+    const int nrows = a.score_none ? 0 : upto - flushed;
 #pragma unroll
     for (int it = 0; it < (NV + 63) / 64; ++it) {
       const int idx = lane + 64 * it;
@@ -1095,7 +1100,7 @@ __device__ void stream_mfma(const StepArgs& a, int pair, int start, int count, P
     lstride = pm.lstride;
     lg = a.logits + (size_t)pm.slot0 * G;  // [G][lstride]
     vn = a.vnorm + pm.slot0;                // [lstride]
-    lrs = wt_rsrc(lg, G * lstride * 4);
+    lrs = wt_rsrc(lg, a.score_none ? 0 : G * lstride * 4);
     // An unsplit pair whose wave ranges fit the buffers keeps its logits here.
     keep_last = pm.nchunk == 1 && quarter <= LR;
 #pragma unroll
@@ -1150,7 +1155,8 @@ __device__ void stream_mfma(const StepArgs& a, int pair, int start, int count, P
 }
 
 template <class T, int D, int G, bool U>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Shape<T, D, G>::kMinWavesPerSimd, 8))) void lf_step_kernel(StepArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Shape<T, D, G>::kMinWavesPerSimd, 8)))
+void lf_step_kernel(StepArgs a) {
   using S = Shape<T, D, G>;
   __shared__ float smem[S::kSmemFloats];
   __shared__ int s_last;

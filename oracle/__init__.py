@@ -4,10 +4,11 @@ Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
 this package.  It shares no code with the HIP library."""
 from .longflow_oracle import (
     SCORE_ATTN,
+    SCORE_NONE,
     SCORE_VL1,
     OracleCache,
     StepDecision,
     attention_step,
 )
 
-__all__ = ["SCORE_ATTN", "SCORE_VL1", "OracleCache", "StepDecision", "attention_step"]
+__all__ = ["SCORE_ATTN", "SCORE_NONE", "SCORE_VL1", "OracleCache", "StepDecision", "attention_step"]

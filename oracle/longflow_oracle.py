@@ -58,6 +58,11 @@ import numpy as np
 
 SCORE_ATTN = 0
 SCORE_VL1 = 1
+# Full-cache comparator (the uncompressed cache the LongFlow summary, section
+# 3, compares against): attention only, no importance and no eviction.  The
+# incoming token is appended while there is room; once the cache is full it is
+# attended but not stored (a reading: the pages' full cache never fills).
+SCORE_NONE = 2
 
 
 def attention_step(keys: np.ndarray, values: np.ndarray, q_heads: np.ndarray, scale: float):
@@ -153,6 +158,12 @@ class OracleCache:
                 out[b, heads] = o
                 lse[b, heads] = l
                 alpha_new[b, heads] = alpha[:, n]
+                if self.score == SCORE_NONE:
+                    if n < self.budget[b]:
+                        slot[b, g], evict[b, g] = n, -1
+                    else:
+                        slot[b, g], evict[b, g] = -1, -2  # attended, not stored
+                    continue
                 imp = alpha[:, :n].sum(axis=0)
                 if self.score == SCORE_VL1:
                     imp = imp * np.abs(vals[:n]).sum(axis=1)
@@ -183,6 +194,8 @@ class OracleCache:
             n, t = self.n[b], self.t[b]
             for g in range(self.Hkv):
                 s = int(slot[b, g])
+                if s == -1 and self.score == SCORE_NONE and n >= self.budget[b]:
+                    continue  # full comparator cache: the token is not stored
                 if n < self.budget[b]:
                     if s != n:
                         raise ValueError("a cache that is not full appends at its next free slot")

@@ -16,7 +16,7 @@ import numpy as np
 import torch
 
 from kv_cache_eviction_lf_amd import LongFlowCache
-from oracle import SCORE_ATTN, SCORE_VL1, OracleCache
+from oracle import SCORE_ATTN, SCORE_NONE, SCORE_VL1, OracleCache
 from workloads import Workload, initial_sequence
 from workloads.device import device_cache, device_step
 
@@ -58,7 +58,7 @@ def parity_run(w: Workload, steps: int, check=None, score: str = "attn", chunk_s
     init = [initial_sequence(w, b) for b in check]
     oc = OracleCache([x[0] for x in init], [x[1] for x in init], [x[2] for x in init], [x[3] for x in init],
                      bud[check], w.n_q_heads, w.sink, w.recent,
-                     score=SCORE_VL1 if score == "vl1" else SCORE_ATTN)
+                     score={"vl1": SCORE_VL1, "none": SCORE_NONE}.get(score, SCORE_ATTN))
     tol = out_tolerance(w)
     rep = ParityReport()
     idx = torch.tensor(check, device=device)

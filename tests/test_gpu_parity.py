@@ -122,6 +122,18 @@ def test_many_chunks(kw, chunk):
     parity_run(w, 40, chunk_slots=chunk, dbg_every=4, tag=f" {kw} chunk={chunk}")
 
 
+@pytest.mark.parametrize("kw", [
+    dict(prefill="short", prefill_short=250),                           # appends, fills, then stores nothing
+    dict(prefill="short", prefill_short=250, dtype="f32", n_q_heads=10, n_kv_heads=2),  # fp32, G = 5
+    dict(budget_lo=200, budget_hi=700, prefill="ragged", batch=5),      # full from the start, split and not
+])
+def test_full_cache_comparator(kw):
+    # attention only (no importance, no eviction): textbook attention over every
+    # stored token plus the incoming one; a full cache stays as it is
+    w = _small(**kw)
+    parity_run(w, 90, score="none", dbg_every=9, tag=f" none {kw}")
+
+
 def test_vl1_on_ragged_small():
     w = _small(budget_lo=150, budget_hi=400, prefill="ragged", batch=4, n_q_heads=14, n_kv_heads=2)
     parity_run(w, 100, score="vl1", dbg_every=9)

@@ -13,7 +13,7 @@ import pytest
 import torch
 from hypothesis import given, settings, strategies as st
 
-from oracle import SCORE_ATTN, SCORE_VL1, OracleCache
+from oracle import SCORE_ATTN, SCORE_NONE, SCORE_VL1, OracleCache
 from tests.brute import BruteCache
 from workloads import get_workload, initial_cache, step_inputs
 
@@ -325,3 +325,37 @@ def test_rejects_budget_not_above_windows_and_protected_commit():
     oc = OracleCache([k], [k], [np.arange(4)], [4], 4, 1, sink=1, recent=1)
     with pytest.raises(ValueError):
         oc.commit(np.array([[0]]), np.zeros((1, 1, 2)), np.zeros((1, 1, 2)))
+
+
+# ---------------------------------------------------------------- full-cache comparator (SCORE_NONE)
+
+@pytest.mark.parametrize("hq,hkv,d", [(8, 2, 16), (7, 1, 4)])
+def test_none_mode_is_textbook_attention_then_stops_storing(hq, hkv, d):
+    # While there is room every token is kept: SDPA over all of them.  Once the
+    # cache is full the token is still attended (SDPA over the stored tokens plus
+    # it) but not stored: the cache stays bit-identical and evict is -2.
+    rng = np.random.default_rng(40 + hq + d)
+    n0, budget, steps = 5, 12, 12
+    k0 = rng.standard_normal((hkv, n0, d)).astype(np.float32)
+    v0 = rng.standard_normal((hkv, n0, d)).astype(np.float32)
+    oc = OracleCache([k0], [v0], [np.arange(n0)], [n0], budget, hq, sink=2, recent=3, score=SCORE_NONE)
+    allk, allv = [k0.astype(np.float64)], [v0.astype(np.float64)]
+    for step in range(steps):
+        q = rng.standard_normal((1, hq, d)).astype(np.float32)
+        kn = rng.standard_normal((1, hkv, d)).astype(np.float32)
+        vn = rng.standard_normal((1, hkv, d)).astype(np.float32)
+        stored_k = np.concatenate(allk, axis=1)
+        stored_v = np.concatenate(allv, axis=1)
+        before_k = [x.copy() for x in oc.k]
+        dec = oc.step(q, kn, vn)
+        K = np.concatenate([stored_k, kn[0][:, None].astype(np.float64)], axis=1)
+        V = np.concatenate([stored_v, vn[0][:, None].astype(np.float64)], axis=1)
+        np.testing.assert_allclose(dec.out[0], _sdpa_reference(K, V, q[0], 1.0 / math.sqrt(d)), rtol=0, atol=1e-12)
+        if n0 + step < budget:
+            assert (dec.evict == -1).all() and (dec.slot == n0 + step).all()
+            allk.append(kn[0][:, None].astype(np.float64))
+            allv.append(vn[0][:, None].astype(np.float64))
+        else:
+            assert (dec.evict == -2).all()
+            assert all(np.array_equal(a, b) for a, b in zip(before_k, oc.k))
+        assert oc.n[0] == min(n0 + step + 1, budget)
