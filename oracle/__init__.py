@@ -9,6 +9,8 @@ from .longflow_oracle import (
     OracleCache,
     StepDecision,
     attention_step,
+    prefill_keep,
 )
 
-__all__ = ["SCORE_ATTN", "SCORE_NONE", "SCORE_VL1", "OracleCache", "StepDecision", "attention_step"]
+__all__ = ["SCORE_ATTN", "SCORE_NONE", "SCORE_VL1", "OracleCache", "StepDecision", "attention_step",
+           "prefill_keep"]

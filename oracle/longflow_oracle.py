@@ -213,3 +213,39 @@ class OracleCache:
         dec = self.decide(q, k_new, v_new)
         self.commit(dec.slot, k_new, v_new)
         return dec
+
+
+def prefill_keep(keys, q_last, budget: int, sink: int, recent: int, scale=None):
+    """One-shot, history-free compression of a prefill longer than the budget.
+
+    The same importance as the decode step (LongFlow summary, section 2.A: from
+    the current query only, a by-product of its attention; the summary's
+    section 5 leaves long prefill to other methods, so this is a reading): the
+    last prefill query attends over all P prefill tokens, and a token's
+    importance is the softmax weight it gets, summed over the query heads of its
+    KV group.  Kept per KV head: positions [0, sink), the `recent` last
+    positions [P - recent, P), and the budget - sink - recent middle positions
+    of largest importance (equal importance: the lower position first).
+
+    keys: float [Hkv][P][d]; q_last: float [Hq][d] (query heads grouped
+    contiguously).  Returns (kept int64 [Hkv][min(P, budget)] in increasing
+    position order, importance float64 [Hkv][P])."""
+    keys = np.asarray(keys, dtype=np.float64)
+    q_last = np.asarray(q_last, dtype=np.float64)
+    Hkv, P, d = keys.shape
+    G = q_last.shape[0] // Hkv
+    scale = float(1.0 / np.sqrt(d) if scale is None else scale)
+    if budget <= sink + recent:
+        raise ValueError("budget must exceed sink + recent")
+    imp = np.zeros((Hkv, P))
+    kept = []
+    for g in range(Hkv):
+        alpha, _, _ = attention_step(keys[g], keys[g], q_last[g * G:(g + 1) * G], scale)
+        imp[g] = alpha.sum(axis=0)
+        if P <= budget:
+            kept.append(np.arange(P))
+            continue
+        middle = list(range(sink, P - recent))
+        ranked = sorted(middle, key=lambda i: (-imp[g, i], i))[: budget - sink - recent]
+        kept.append(np.array(sorted(list(range(sink)) + ranked + list(range(P - recent, P)))))
+    return np.stack(kept).astype(np.int64), imp

@@ -13,7 +13,7 @@ import pytest
 import torch
 from hypothesis import given, settings, strategies as st
 
-from oracle import SCORE_ATTN, SCORE_NONE, SCORE_VL1, OracleCache
+from oracle import SCORE_ATTN, SCORE_NONE, SCORE_VL1, OracleCache, prefill_keep
 from tests.brute import BruteCache
 from workloads import get_workload, initial_cache, step_inputs
 
@@ -359,3 +359,67 @@ def test_none_mode_is_textbook_attention_then_stops_storing(hq, hkv, d):
             assert (dec.evict == -2).all()
             assert all(np.array_equal(a, b) for a, b in zip(before_k, oc.k))
         assert oc.n[0] == min(n0 + step + 1, budget)
+
+
+# ---------------------------------------------------------------- one-shot prefill compression
+
+def _brute_prefill_keep(keys, q, budget, sink, recent):
+    """Pure-Python loops: softmax weights with math.exp, importance summed over
+    the group's heads, then the middle positions taken one at a time by largest
+    importance (first position on equal importance)."""
+    Hkv, P, d = len(keys), len(keys[0]), len(keys[0][0])
+    G = len(q) // Hkv
+    scale = 1.0 / math.sqrt(d)
+    out = []
+    for g in range(Hkv):
+        imp = [0.0] * P
+        for j in range(G):
+            qh = q[g * G + j]
+            s = [scale * sum(qh[x] * keys[g][i][x] for x in range(d)) for i in range(P)]
+            m = max(s)
+            e = [math.exp(v - m) for v in s]
+            z = sum(e)
+            for i in range(P):
+                imp[i] += e[i] / z
+        if P <= budget:
+            out.append(list(range(P)))
+            continue
+        left = list(range(sink, P - recent))
+        chosen = []
+        for _ in range(budget - sink - recent):
+            best = left[0]
+            for i in left[1:]:
+                if imp[i] > imp[best]:
+                    best = i
+            chosen.append(best)
+            left.remove(best)
+        out.append(sorted(list(range(sink)) + chosen + list(range(P - recent, P))))
+    return out
+
+
+@pytest.mark.parametrize("seed,Hkv,G,P,budget,sink,recent", [
+    (0, 1, 1, 9, 6, 1, 2), (1, 2, 3, 17, 8, 2, 3), (2, 2, 2, 12, 12, 2, 2), (3, 1, 4, 30, 7, 0, 1),
+    (4, 3, 1, 25, 10, 3, 0),
+])
+def test_prefill_keep_matches_brute_force(seed, Hkv, G, P, budget, sink, recent):
+    rng = np.random.default_rng(seed)
+    d = 5
+    keys = rng.standard_normal((Hkv, P, d))
+    q = rng.standard_normal((Hkv * G, d))
+    kept, imp = prefill_keep(keys, q, budget, sink, recent)
+    assert kept.tolist() == _brute_prefill_keep(keys.tolist(), q.tolist(), budget, sink, recent)
+    np.testing.assert_allclose(imp.sum(axis=1), G, rtol=0, atol=1e-12)  # weights of each head sum to 1
+
+
+def test_prefill_keep_integer_logits_and_ties():
+    # G = 1, small-integer q and k: logits are exact integers, so the kept middle
+    # positions are the largest logits, the lower position first on equal ones
+    rng = np.random.default_rng(5)
+    P, d, budget, sink, recent = 40, 3, 16, 2, 4
+    keys = rng.integers(-2, 3, size=(1, P, d)).astype(np.float32)
+    q = np.array([[1.0, -1.0, 2.0]], dtype=np.float32)
+    kept, _ = prefill_keep(keys, q, budget, sink, recent)
+    logit = keys[0] @ q[0]
+    middle = sorted(range(sink, P - recent), key=lambda i: (-logit[i], i))[: budget - sink - recent]
+    assert kept[0].tolist() == sorted(list(range(sink)) + middle + list(range(P - recent, P)))
+    assert len(set(logit[sink:P - recent].tolist())) < P - sink - recent  # ties present and decided by position
