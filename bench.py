@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--layers", type=int, default=0, help="rotating layer caches (0 = enough to exceed 2x MALL)")
     ap.add_argument("--score", default="attn", choices=["attn", "vl1", "none"],
                     help="none: the full-cache comparator (attention only, the cache is full and keeps its tokens)")
+    ap.add_argument("--compress", action="store_true",
+                    help="time the one-shot prefill compression (lf_prefill_compress) of the workload's shape "
+                         "instead of decode steps (prefill lengths: the ragged draw, else twice the budget)")
     ap.add_argument("--budget", type=int, default=0,
                     help="override the workload's budget (equal for every sequence, prefill filling it)")
     ap.add_argument("--chunk", type=int, default=0, help="split-KV chunk slots (0 = library default)")
@@ -102,6 +105,64 @@ def cpu_baseline(w, seconds: float, score: str = "attn") -> dict:
                       f"{el:.1f} s, numpy with BLAS limited to 1 thread"}
 
 
+def bench_compress(args, w, torch, dev):
+    """Time lf_prefill_compress over the workload's batch: every sequence's
+    prefill (longer than its budget) reduced to its budget."""
+    from kv_cache_eviction_lf_amd import _lib
+    from workloads import budgets, prefill_lengths
+
+    bud = budgets(w)
+    pre = prefill_lengths(w) if w.prefill == "ragged" else 2 * bud.astype(np.int64)
+    max_prefill, max_budget = int(pre.max()), int(bud.max())
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    gen = torch.Generator(device=dev).manual_seed(w.seed)
+    q = torch.randn((w.batch, w.n_q_heads, w.head_dim), generator=gen, device=dev).to(tdt)
+    k_pre = torch.randn((w.batch, w.n_kv_heads, max_prefill, w.head_dim), generator=gen, device=dev).to(tdt)
+    v_pre = torch.randn_like(k_pre, dtype=torch.float32).to(tdt)
+    k_cache = torch.empty((w.batch, w.n_kv_heads, max_budget, w.head_dim), dtype=tdt, device=dev)
+    v_cache = torch.empty_like(k_cache)
+    kept = torch.empty((w.batch, w.n_kv_heads, max_budget), dtype=torch.int32, device=dev)
+    cfg = _lib.make_config(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, max_budget, w.sink, w.recent,
+                           _lib.LF_BF16 if w.dtype == "bf16" else _lib.LF_F32)
+    wb = _lib.lf_prefill_work_bytes(cfg, max_prefill)
+    work = torch.empty(wb, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    prel, budl = [int(x) for x in pre], [int(x) for x in bud]
+
+    def once():
+        _lib.lf_prefill_compress(cfg, budl, prel, max_prefill, q.data_ptr(), k_pre.data_ptr(), v_pre.data_ptr(),
+                                 k_cache.data_ptr(), v_cache.data_ptr(), kept.data_ptr(), work.data_ptr(), wb, stream)
+
+    n = max(3, min(args.steps, 50))
+    for _ in range(2):
+        once()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(n):
+        once()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / n
+    s = 2 if w.dtype == "bf16" else 4
+    nkeep = np.minimum(pre, bud).astype(np.int64)
+    # every prefill K row read, the kept K and V rows read and written
+    nbytes = int((pre.sum() + 4 * nkeep.sum()) * w.n_kv_heads * w.head_dim * s)
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "prefill compressions/s (one-shot, the whole batch to its budgets)",
+        "value": round(1e3 / ms, 2), "unit": "compressions/s", "n_gpus": 1, "steps": n, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded torch normal on the device)",
+        "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
+                   "head_dim": w.head_dim, "prefill": [int(pre.min()), int(pre.max())],
+                   "budget": [int(bud.min()), int(bud.max())], "sink": w.sink, "recent": w.recent},
+        "kv_GBps": round(gbps, 1), "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+        "bytes_per_call": nbytes,
+        "note": "the score pass reads the prefill K rows twice (maxima, then importance); bytes count them once",
+    }), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -123,6 +184,9 @@ def main():
     w = get_workload(args.workload)
     if args.budget:
         w = w.with_(budget_lo=args.budget, budget_hi=args.budget, prefill="full")
+    if args.compress:
+        bench_compress(args, w, torch, dev)
+        return
     bud = budgets(w)
     step_bytes = algorithmic_bytes(w, bud, stored=args.score != "none")
     layer_kv = int(np.sum(bud)) * w.n_kv_heads * w.head_dim * 2 * (2 if w.dtype == "bf16" else 4)

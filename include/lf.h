@@ -151,6 +151,47 @@ lf_status lf_decode_step(const void* q, const void* k_new, const void* v_new, lf
 lf_status lf_decode_step_dbg(const void* q, const void* k_new, const void* v_new, lf_cache* cache,
                              void* out, int32_t* evict_idx, float* scores, float* lse, void* stream);
 
+/*
+ * lf_prefill_work_bytes - size of the device scratch lf_prefill_compress needs
+ * (importance of every prefill position of every (sequence, KV head), plus the
+ * prefill lengths and budgets).  cfg validated as in lf_init_cache.
+ */
+lf_status lf_prefill_work_bytes(const lf_config* cfg, int32_t max_prefill, size_t* bytes);
+
+/*
+ * lf_prefill_compress - one-shot compression of a prefill longer than the
+ * budget, run once before decoding (the step before the decode path).  For
+ * every sequence b and KV head g the last prefill query attends over all P_b
+ * prefill tokens; a token's importance is the softmax weight it receives
+ * summed over the group's query heads (the decode step's LF_SCORE_ATTN
+ * importance: from the current query only, LongFlow summary, section 2.A).
+ * Kept: positions [0, sink), the `recent` last positions [P_b - recent, P_b),
+ * and the budget_b - sink - recent middle positions of largest importance
+ * (equal importance: the lower position).  The pages leave long prefill to
+ * other methods (summary, section 5); this selection is a reading.  When
+ * P_b <= budget_b every token is kept.
+ *   cfg          host; shapes, dtype, sink, recent, softmax_scale as for
+ *                lf_init_cache (score and chunk_slots are not used).
+ *   budgets      host int32[B] or NULL (max_budget), validated as in lf_init_cache.
+ *   prefill      host int32[B]: P_b in [1, max_prefill].
+ *   q_last       device [B][Hq][d]: the query of each sequence's last prefill token.
+ *   k_pre, v_pre device [B][Hkv][max_prefill][d]: prefill K/V, position p in row p.
+ *   k_cache, v_cache  device [B][Hkv][max_budget][d]: slots 0 .. min(P_b, budget_b)-1
+ *                receive the kept tokens in increasing position order; other
+ *                slots are untouched.  Then call lf_init_cache with
+ *                seq_len[b] = P_b (the recent window is the last slots).
+ *   kept         device int32 [B][Hkv][max_budget]: the kept positions, same order.
+ *   work         device scratch of work_bytes >= lf_prefill_work_bytes(); on
+ *                return it holds the importance [B][Hkv][max_prefill] (float).
+ * All device pointers 16-byte aligned; k_pre/v_pre must not overlap k_cache/v_cache.
+ * Asynchronous on `stream` after a small synchronous upload of the lengths.
+ * Errors: LF_ERR_ARG, LF_ERR_UNSUPPORTED, LF_ERR_HIP.
+ */
+lf_status lf_prefill_compress(const lf_config* cfg, const int32_t* budgets, const int32_t* prefill,
+                              int32_t max_prefill, const void* q_last, const void* k_pre, const void* v_pre,
+                              void* k_cache, void* v_cache, int32_t* kept, void* work, size_t work_bytes,
+                              void* stream);
+
 /* lf_free - release the host handle (NULL-safe).  Device buffers stay the caller's. */
 void lf_free(lf_cache* cache);
 

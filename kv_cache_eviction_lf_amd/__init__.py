@@ -18,6 +18,8 @@ from ._lib import (
     lf_init_cache,
     lf_last_error,
     lf_probe_copy,
+    lf_prefill_compress,
+    lf_prefill_work_bytes,
     lf_probe_read,
     lf_state_bytes,
     load_library,
@@ -26,10 +28,10 @@ from ._lib import (
 
 
 def __getattr__(name):
-    if name == "LongFlowCache":
-        from .cache import LongFlowCache
+    if name in ("LongFlowCache", "compress_prefill"):
+        from . import cache
 
-        return LongFlowCache
+        return getattr(cache, name)
     raise AttributeError(name)
 
 
@@ -42,6 +44,7 @@ __all__ = [
     "LF_SCORE_VL1",
     "LFError",
     "LongFlowCache",
+    "compress_prefill",
     "lf_abi_version",
     "lf_decode_step",
     "lf_decode_step_dbg",
@@ -49,6 +52,8 @@ __all__ = [
     "lf_init_cache",
     "lf_last_error",
     "lf_probe_copy",
+    "lf_prefill_compress",
+    "lf_prefill_work_bytes",
     "lf_probe_read",
     "lf_state_bytes",
     "load_library",

@@ -60,6 +60,12 @@ PROTOTYPES = {
     "lf_probe_read": (c_int32, [c_void_p, c_size_t, c_void_p, c_void_p]),
     "lf_probe_read_sink_words": (c_int32, []),
     "lf_probe_empty": (c_int32, [c_int32, c_void_p]),
+    "lf_prefill_work_bytes": (c_int32, [POINTER(lf_config), c_int32, POINTER(c_size_t)]),
+    "lf_prefill_compress": (
+        c_int32,
+        [POINTER(lf_config), POINTER(c_int32), POINTER(c_int32), c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
+         c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
+    ),
 }
 
 _lib = None
@@ -131,6 +137,21 @@ def lf_init_cache(cfg: lf_config, budgets, seq_len, k_cache: int, v_cache: int, 
                                         c_void_p(v_cache), c_void_p(state), c_size_t(state_bytes), c_int32(flags),
                                         c_void_p(stream), ctypes.byref(handle)), "lf_init_cache")
     return int(handle.value)
+
+
+def lf_prefill_work_bytes(cfg: lf_config, max_prefill: int) -> int:
+    out = c_size_t(0)
+    _check(load_library().lf_prefill_work_bytes(ctypes.byref(cfg), c_int32(max_prefill), ctypes.byref(out)),
+           "lf_prefill_work_bytes")
+    return int(out.value)
+
+
+def lf_prefill_compress(cfg: lf_config, budgets, prefill, max_prefill: int, q_last: int, k_pre: int, v_pre: int,
+                        k_cache: int, v_cache: int, kept: int, work: int, work_bytes: int, stream: int = 0) -> None:
+    _check(load_library().lf_prefill_compress(
+        ctypes.byref(cfg), _i32_array(budgets), _i32_array(prefill), c_int32(max_prefill), c_void_p(q_last),
+        c_void_p(k_pre), c_void_p(v_pre), c_void_p(k_cache), c_void_p(v_cache), c_void_p(kept), c_void_p(work),
+        c_size_t(work_bytes), c_void_p(stream)), "lf_prefill_compress")
 
 
 def lf_decode_step(q: int, k_new: int, v_new: int, cache: int, out: int, evict_idx: int, stream: int = 0) -> None:

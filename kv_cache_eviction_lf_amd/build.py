@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "liblf.so")
 ARCH = "gfx950"
 
-SOURCES = ["lf_host.cpp", "lf_kernel.hip", "lf_probe.hip"]
+SOURCES = ["lf_host.cpp", "lf_kernel.hip", "lf_prefill.hip", "lf_probe.hip"]
 
 # Packed fp32 VALU forms are kept off (every HIP translation unit).
 HIP_FLAGS = [
@@ -47,15 +47,19 @@ def build(verbose: bool = False) -> str:
     os.makedirs(objdir, exist_ok=True)
     objs = []
     t0 = time.time()
-    for src in SOURCES:
+    procs = []
+    for src in SOURCES:  # compiled concurrently
         path = os.path.join(CSRC, src)
         obj = os.path.join(objdir, src + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
         cmd = [cc, *HIP_FLAGS, *lang, "-c", path, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
-        subprocess.run(cmd, check=True)
+        procs.append((subprocess.Popen(cmd), cmd))
         objs.append(obj)
+    for proc, cmd in procs:
+        if proc.wait() != 0:
+            raise subprocess.CalledProcessError(proc.returncode, cmd)
     tmp = LIB + ".tmp"
     cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:

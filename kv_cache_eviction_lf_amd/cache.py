@@ -105,3 +105,36 @@ class LongFlowCache:
             self.close()
         except Exception:
             pass
+
+
+def compress_prefill(q_last: torch.Tensor, k_pre: torch.Tensor, v_pre: torch.Tensor, prefill, max_budget: int,
+                     sink: int, recent: int, budgets=None, softmax_scale: float = 0.0):
+    """One-shot compression of prefills longer than their budgets (lf_prefill_compress).
+
+    q_last [B][Hq][d]: query of each sequence's last prefill token; k_pre/v_pre
+    [B][Hkv][max_prefill][d]: prefill K/V; prefill: per-sequence prefill length.
+    Returns (k_cache, v_cache, kept, importance): caches [B][Hkv][max_budget][d]
+    holding the kept tokens in position order in slots 0..min(P_b, budget_b)-1
+    (zeros after), kept int32 [B][Hkv][max_budget] positions, importance fp32
+    [B][Hkv][max_prefill].  Pass seq_len = prefill to LongFlowCache afterwards."""
+    B, Hkv, max_prefill, d = k_pre.shape
+    dtype, dev = k_pre.dtype, k_pre.device
+    _need(v_pre, "v_pre", k_pre.shape, dtype, dev)
+    _need(k_pre, "k_pre", k_pre.shape, dtype, dev)
+    if q_last.dim() != 3 or q_last.shape[0] != B or q_last.shape[2] != d:
+        raise ValueError(f"q_last has shape {tuple(q_last.shape)}, expected [{B}][Hq][{d}]")
+    _need(q_last, "q_last", q_last.shape, dtype, dev)
+    if dtype not in _DTYPES:
+        raise ValueError("dtype must be bfloat16 or float32")
+    cfg = _lib.make_config(B, q_last.shape[1], Hkv, d, max_budget, sink, recent, _DTYPES[dtype], LF_SCORE_ATTN,
+                           softmax_scale, 0)
+    wb = _lib.lf_prefill_work_bytes(cfg, max_prefill)
+    work = torch.empty(wb, dtype=torch.uint8, device=dev)
+    k_cache = torch.zeros((B, Hkv, max_budget, d), dtype=dtype, device=dev)
+    v_cache = torch.zeros_like(k_cache)
+    kept = torch.full((B, Hkv, max_budget), -1, dtype=torch.int32, device=dev)
+    _lib.lf_prefill_compress(cfg, budgets, [int(x) for x in prefill], max_prefill, q_last.data_ptr(),
+                             k_pre.data_ptr(), v_pre.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                             kept.data_ptr(), work.data_ptr(), wb, _stream_handle(dev))
+    imp = work[: 4 * B * Hkv * max_prefill].view(torch.float32).view(B, Hkv, max_prefill)
+    return k_cache, v_cache, kept, imp

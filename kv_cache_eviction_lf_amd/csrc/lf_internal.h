@@ -93,8 +93,34 @@ struct StepArgs {
 // lengths are multiples of it.  Defined next to the kernels.
 int tile_rows(int dtype, int head_dim, int group);
 
-// Kernel launch and runtime helpers, implemented in lf_kernel.hip.
+// Arguments of the one-shot prefill compression (lf_prefill.hip).  Pair p =
+// b * n_kv_heads + g; work holds [pairs][max_prefill] importances followed by
+// the device copies of the prefill lengths and budgets.
+struct PrefillArgs {
+  const void* q_last;  // [B][Hq][d]
+  const void* k_pre;   // [B][Hkv][max_prefill][d]
+  const void* v_pre;
+  void* k_cache;       // [B][Hkv][max_budget][d]
+  void* v_cache;
+  int32_t* kept;       // [B][Hkv][max_budget]: kept positions, increasing
+  float* work;         // [pairs][max_prefill]
+  const int32_t* prefill;  // device [B]
+  const int32_t* budget;   // device [B]
+  int32_t n_kv_heads;
+  int32_t n_q_heads;
+  int32_t group;
+  int32_t max_prefill;
+  int32_t max_budget;
+  int32_t sink;
+  int32_t recent;
+  float scale_log2;
+};
+
+// Kernel launch and runtime helpers, implemented in lf_kernel.hip (step) and
+// lf_prefill.hip (prefill compression).
 int launch_step(int dtype, int head_dim, int group, const StepArgs& a, void* stream, char* err, size_t errlen);
+int launch_prefill(int dtype, int head_dim, const PrefillArgs& a, int n_pairs, void* stream, char* err,
+                   size_t errlen);
 int upload_and_wait(void* dst, const void* src, size_t bytes, void* stream, char* err, size_t errlen);
 
 }  // namespace lf

@@ -125,3 +125,27 @@ def test_step_rejects_bad_handles_without_launching():
     assert ei.value.status == LF_ERR_STATE
     _lib.lf_free(0)  # NULL-safe
     _lib.lf_free(ctypes.addressof(fake))  # wrong magic: ignored
+
+
+def test_prefill_compress_validates_before_any_device_call():
+    cfg = _cfg()
+    wb = _lib.lf_prefill_work_bytes(cfg, 1024)
+    assert wb >= 4 * 2 * 2 * 1024 + 16
+    good = dict(budgets=None, prefill=[1000, 700], max_prefill=1024, q_last=4096, k_pre=8192, v_pre=12288,
+                k_cache=16384, v_cache=20480, kept=24576, work=28672, work_bytes=wb)
+    bad = [
+        dict(prefill=[1025, 700]),        # longer than max_prefill
+        dict(prefill=[0, 700]),           # empty prefill
+        dict(q_last=0),                   # NULL
+        dict(k_cache=16384 + 8),          # misaligned
+        dict(work_bytes=wb - 1),          # scratch too small
+        dict(budgets=[20, 512]),          # budget <= sink + recent
+        dict(max_prefill=0),
+    ]
+    for change in bad:
+        args = dict(good, **change)
+        with pytest.raises(LFError) as ei:
+            _lib.lf_prefill_compress(cfg, args["budgets"], args["prefill"], args["max_prefill"], args["q_last"],
+                                     args["k_pre"], args["v_pre"], args["k_cache"], args["v_cache"], args["kept"],
+                                     args["work"], args["work_bytes"])
+        assert ei.value.status == LF_ERR_ARG, change

@@ -1,0 +1,101 @@
+"""GPU parity of the one-shot prefill compression (lf_prefill_compress) with
+the oracle's prefill_keep: the importance of every prefill position within
+float32 rounding, the kept positions exactly (where the importance at the
+selection threshold is closer than 1e-6 to its neighbour, the GPU's choice is
+accepted if every position it swapped lies within 1e-6 of the threshold), the
+kept K/V rows bit-exactly, and then decode steps from the compressed cache
+against the oracle started from the same kept positions."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import OracleCache, prefill_keep
+from workloads import Workload, prefill_inputs
+
+pytestmark = pytest.mark.gpu
+
+TIE = 1e-6
+
+
+def _case(name, B, Hq, Hkv, d, dtype, budgets, prefill, sink, recent, max_prefill, seed):
+    w = Workload(name, B, Hq, Hkv, d, dtype, min(budgets), max(budgets), sink, recent, 0, seed=seed)
+    return w, list(budgets), list(prefill), max_prefill
+
+
+CASES = [
+    _case("pf_bf16_g4", 3, 8, 2, 128, "bf16", [300, 512, 512], [700, 512, 1000], 4, 16, 1024, 21),
+    _case("pf_f32_g5", 2, 10, 2, 128, "f32", [200, 250], [600, 100], 4, 8, 640, 22),
+    _case("pf_bf16_g8_d64", 2, 16, 2, 64, "bf16", [128, 128], [4000, 129], 2, 8, 4096, 23),
+    _case("pf_bf16_g1_nowin", 1, 4, 4, 128, "bf16", [1000], [3000], 0, 0, 3072, 24),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0].name for c in CASES])
+def test_prefill_compress_matches_oracle(case):
+    from kv_cache_eviction_lf_amd import LongFlowCache, compress_prefill
+
+    w, bud, pre, max_prefill = case
+    print(f"[prefill] {w.name}: B={w.batch} Hq={w.n_q_heads} Hkv={w.n_kv_heads} d={w.head_dim} {w.dtype} "
+          f"budgets={bud} prefill={pre} sink={w.sink} recent={w.recent}", flush=True)
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    q, k, v = prefill_inputs(w, max_prefill)
+    qd, kd, vd = (torch.from_numpy(x).to(dev, tdt) for x in (q, k, v))
+    max_budget = max(bud)
+    kc, vc, kept, imp = compress_prefill(qd, kd, vd, pre, max_budget, w.sink, w.recent, budgets=bud)
+    torch.cuda.synchronize()
+    kept_h, imp_h = kept.cpu().numpy(), imp.cpu().numpy().astype(np.float64)
+    kc_h, vc_h = kc.float().cpu().numpy(), vc.float().cpu().numpy()
+    swapped = 0
+    for b in range(w.batch):
+        P, nb = pre[b], min(pre[b], bud[b])
+        want, imp_o = prefill_keep(k[b, :, :P], q[b], bud[b], w.sink, w.recent)
+        err = np.abs(imp_h[b, :, :P] - imp_o) / np.maximum(1e-3, imp_o)
+        assert float(err.max()) < 1e-4, f"seq {b}: importance differs by {err.max():.2e} (relative)"
+        for g in range(w.n_kv_heads):
+            got = kept_h[b, g, :nb]
+            assert np.all(kept_h[b, g, nb:] == -1)
+            assert np.all(np.diff(got) > 0) and got[0] >= 0 and got[-1] < P
+            if not np.array_equal(got, want[g]):
+                # near-ties at the threshold only
+                mid = imp_o[g, w.sink:P - w.recent]
+                thr = np.sort(mid)[::-1][bud[b] - w.sink - w.recent - 1]
+                diff = set(got.tolist()) ^ set(want[g].tolist())
+                assert all(abs(imp_o[g, p] - thr) < TIE for p in diff), (b, g, sorted(diff)[:8])
+                assert set(range(w.sink)) <= set(got.tolist())
+                assert set(range(P - w.recent, P)) <= set(got.tolist())
+                swapped += 1
+            assert np.array_equal(kc_h[b, g, :nb], k[b, g, got]), f"K rows of ({b},{g})"
+            assert np.array_equal(vc_h[b, g, :nb], v[b, g, got]), f"V rows of ({b},{g})"
+            assert not kc_h[b, g, nb:].any() and not vc_h[b, g, nb:].any()
+    print(f"[prefill] ok, {swapped} near-tie swaps", flush=True)
+
+    # Decode from the compressed cache: positions of the kept tokens are known,
+    # the next token's position is P.
+    cache = LongFlowCache(kc, vc, w.n_q_heads, w.sink, w.recent, pre, budgets=bud)
+    oc = OracleCache([kc_h[b][:, : min(pre[b], bud[b])] for b in range(w.batch)],
+                     [vc_h[b][:, : min(pre[b], bud[b])] for b in range(w.batch)],
+                     [kept_h[b][:, : min(pre[b], bud[b])] for b in range(w.batch)], pre, bud, w.n_q_heads,
+                     w.sink, w.recent)
+    rng = np.random.default_rng(w.seed + 1000)
+    tol = 2e-2 if w.dtype == "bf16" else 1e-5
+    for s in range(12):
+        qs = rng.standard_normal((w.batch, w.n_q_heads, w.head_dim)).astype(np.float32)
+        ks = rng.standard_normal((w.batch, w.n_kv_heads, w.head_dim)).astype(np.float32)
+        vs = rng.standard_normal((w.batch, w.n_kv_heads, w.head_dim)).astype(np.float32)
+        qt, kt, vt = (torch.from_numpy(x).to(dev, tdt) for x in (qs, ks, vs))
+        qs, ks, vs = (x.float().cpu().numpy() for x in (qt, kt, vt))  # the dtype-rounded values both sides see
+        out, ev = cache.step(qt, kt, vt)
+        dec = oc.decide(qs, ks, vs)
+        assert float(np.abs(out.float().cpu().numpy() - dec.out).max()) <= tol
+        ev_h = ev.cpu().numpy()
+        slots = dec.slot.copy()
+        for b in range(w.batch):
+            for g in range(w.n_kv_heads):
+                if ev_h[b, g] != dec.evict[b, g]:
+                    assert dec.gap[b, g] < TIE and dec.eligible[b][g, ev_h[b, g]], (s, b, g)
+                    slots[b, g] = ev_h[b, g]
+        oc.commit(slots, ks, vs)
+    cache.close()

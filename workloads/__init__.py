@@ -9,6 +9,7 @@ from .generate import (
     round_to_bf16,
     budgets,
     prefill_lengths,
+    prefill_inputs,
     initial_sequence,
     initial_cache,
     step_inputs,
@@ -23,6 +24,7 @@ __all__ = [
     "round_to_bf16",
     "budgets",
     "prefill_lengths",
+    "prefill_inputs",
     "initial_sequence",
     "initial_cache",
     "step_inputs",

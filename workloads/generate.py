@@ -21,6 +21,7 @@ _T_CACHE = 4
 _T_STEP = 5
 _T_OUTLIER = 6
 _T_ANCHOR = 7
+_T_PREFILL_ROWS = 8
 
 
 def _rng(w: Workload, tag: int, *ids: int) -> np.random.Generator:
@@ -166,3 +167,16 @@ def step_inputs(w: Workload, step: int, seqs=None):
         ks.append(k)
         vs.append(v)
     return _finish(w, np.stack(qs)), _finish(w, np.stack(ks)), _finish(w, np.stack(vs))
+
+
+
+def prefill_inputs(w: Workload, max_prefill: int):
+    """Full-length prefill of every sequence, for the one-shot compression:
+    q_last [B][Hq][d] (the last prefill token's query), k_pre and v_pre
+    [B][Hkv][max_prefill][d], N(0,1) draws rounded to the workload's dtype
+    (positions past a sequence's prefill length hold draws that are not read)."""
+    rng = _rng(w, _T_PREFILL_ROWS)
+    q = _finish(w, rng.standard_normal((w.batch, w.n_q_heads, w.head_dim), dtype=np.float32))
+    k = _finish(w, rng.standard_normal((w.batch, w.n_kv_heads, max_prefill, w.head_dim), dtype=np.float32))
+    v = _finish(w, rng.standard_normal((w.batch, w.n_kv_heads, max_prefill, w.head_dim), dtype=np.float32))
+    return q, k, v
