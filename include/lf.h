@@ -173,7 +173,7 @@ lf_status lf_prefill_work_bytes(const lf_config* cfg, int32_t max_prefill, size_
  *   cfg          host; shapes, dtype, sink, recent, softmax_scale as for
  *                lf_init_cache (score and chunk_slots are not used).
  *   budgets      host int32[B] or NULL (max_budget), validated as in lf_init_cache.
- *   prefill      host int32[B]: P_b in [1, max_prefill].
+ *   prefill      host int32[B]: P_b in [1, max_prefill]; max_prefill <= 65536.
  *   q_last       device [B][Hq][d]: the query of each sequence's last prefill token.
  *   k_pre, v_pre device [B][Hkv][max_prefill][d]: prefill K/V, position p in row p.
  *   k_cache, v_cache  device [B][Hkv][max_budget][d]: slots 0 .. min(P_b, budget_b)-1

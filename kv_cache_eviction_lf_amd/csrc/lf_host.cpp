@@ -352,9 +352,12 @@ lf_status lf_prefill_work_bytes(const lf_config* cfg, int32_t max_prefill, size_
   lf_status st = validate_config(cfg);
   if (st != LF_OK) return st;
   if (!bytes) return fail(LF_ERR_ARG, "bytes is NULL");
-  if (max_prefill < 1) return fail(LF_ERR_ARG, "max_prefill must be >= 1 (got %d)", max_prefill);
+  if (max_prefill < 1 || max_prefill > lf::kMaxPrefill)
+    return fail(LF_ERR_ARG, "max_prefill %d outside [1, %d]", max_prefill, lf::kMaxPrefill);
   const size_t pairs = (size_t)cfg->batch * cfg->n_kv_heads;
-  *bytes = align_up(sizeof(float) * pairs * (size_t)max_prefill) + align_up(sizeof(int32_t) * 2 * cfg->batch);
+  const size_t nck = (max_prefill + lf::kPrefillChunk - 1) / lf::kPrefillChunk;
+  *bytes = align_up(sizeof(float) * pairs * (size_t)max_prefill) + align_up(sizeof(float) * pairs * nck * 16) +
+           align_up(sizeof(int32_t) * 2 * cfg->batch);
   g_err[0] = 0;
   return LF_OK;
 }
@@ -381,8 +384,10 @@ lf_status lf_prefill_compress(const lf_config* cfg, const int32_t* budgets, cons
   }
   if (work_bytes < need) return fail(LF_ERR_ARG, "work_bytes %zu < %zu (lf_prefill_work_bytes)", work_bytes, need);
   const size_t pairs = (size_t)cfg->batch * cfg->n_kv_heads;
+  const int nck = (max_prefill + lf::kPrefillChunk - 1) / lf::kPrefillChunk;
   char* w = static_cast<char*>(work);
-  int32_t* dlen = reinterpret_cast<int32_t*>(w + align_up(sizeof(float) * pairs * (size_t)max_prefill));
+  float* stats = reinterpret_cast<float*>(w + align_up(sizeof(float) * pairs * (size_t)max_prefill));
+  int32_t* dlen = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(stats) + align_up(sizeof(float) * pairs * nck * 16));
   std::vector<int32_t> host(2 * cfg->batch);
   for (int b = 0; b < cfg->batch; ++b) {
     host[b] = prefill[b];
@@ -399,6 +404,9 @@ lf_status lf_prefill_compress(const lf_config* cfg, const int32_t* budgets, cons
   a.v_cache = v_cache;
   a.kept = kept;
   a.work = reinterpret_cast<float*>(w);
+  a.stats = stats;
+  a.n_chunks = nck;
+  a.n_copy = (cfg->max_budget + lf::kPrefillCopyRows - 1) / lf::kPrefillCopyRows;
   a.prefill = dlen;
   a.budget = dlen + cfg->batch;
   a.n_kv_heads = cfg->n_kv_heads;

@@ -16,6 +16,9 @@ constexpr int kThreads = 256;      // threads per workgroup (4 wave64)
 constexpr size_t kAlign = 256;
 constexpr int kSlotPad = 64;        // per-pair workspace rows are padded to this many slots
 constexpr int kTargetItems = 256;   // split pairs into chunks until about this many work items
+constexpr int kMaxPrefill = 65536;  // prefill compression: positions fit 16 bits of the selection key
+constexpr int kPrefillChunk = 512;  // rows per workgroup of the prefill score passes
+constexpr int kPrefillCopyRows = 256;  // kept rows per workgroup of the prefill copy
 
 // Per (sequence, KV head) pair.  Written by lf_init_cache, updated in place by
 // the last-arriving workgroup of the pair at the end of every step.
@@ -94,8 +97,9 @@ struct StepArgs {
 int tile_rows(int dtype, int head_dim, int group);
 
 // Arguments of the one-shot prefill compression (lf_prefill.hip).  Pair p =
-// b * n_kv_heads + g; work holds [pairs][max_prefill] importances followed by
-// the device copies of the prefill lengths and budgets.
+// b * n_kv_heads + g; the caller's scratch holds [pairs][max_prefill]
+// importances, the per-chunk statistics, then the device copies of the prefill
+// lengths and budgets.
 struct PrefillArgs {
   const void* q_last;  // [B][Hq][d]
   const void* k_pre;   // [B][Hkv][max_prefill][d]
@@ -104,8 +108,11 @@ struct PrefillArgs {
   void* v_cache;
   int32_t* kept;       // [B][Hkv][max_budget]: kept positions, increasing
   float* work;         // [pairs][max_prefill]
+  float* stats;        // [pairs][n_chunks][8][2]: per-chunk (max, sum) per head
   const int32_t* prefill;  // device [B]
   const int32_t* budget;   // device [B]
+  int32_t n_chunks;    // score chunks per pair (max_prefill / 512, rounded up)
+  int32_t n_copy;      // copy workgroups per pair (max_budget / 256, rounded up)
   int32_t n_kv_heads;
   int32_t n_q_heads;
   int32_t group;

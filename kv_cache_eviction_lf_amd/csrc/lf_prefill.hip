@@ -9,14 +9,18 @@
 // to other methods; this selection is the plainest reading that keeps the
 // decode step's importance.
 //
-// Two launches on the caller's stream:
-//   prefill_score_kernel   one workgroup per pair: two passes over the pair's
-//                          K rows (maxima and normalisers, then importance).
-//   prefill_select_kernel  one workgroup per pair: radix selection of the
-//                          threshold over 64-bit keys (importance, then the
-//                          complement of the position, so keys are unique and
-//                          the lower position ranks first on equal importance),
-//                          position-ordered compaction, then the row copies.
+// Four launches on the caller's stream:
+//   prefill_stats_kernel       a workgroup per (pair, 512-row chunk): per-head
+//                              maximum and normaliser of the chunk's logits.
+//   prefill_importance_kernel  same grid: the pair's statistics combined in
+//                              chunk order, then every row's importance.
+//   prefill_select_kernel      a workgroup per pair: radix selection of the
+//                              threshold over 48-bit keys (importance, then the
+//                              complement of the position, so keys are unique
+//                              and the lower position ranks first on equal
+//                              importance), then position-ordered compaction.
+//   prefill_copy_kernel        a workgroup per (pair, 256 kept rows): the
+//                              kept K/V rows copied in order.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -53,11 +57,22 @@ __device__ __forceinline__ void unpack16(const uint4& r, float (&x)[8], BF16E) {
   }
 }
 
-// Sum over the LPR lanes that hold one row (lanes lane ^ 1, 2, ... within the row).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the LPR consecutive lanes that hold one row, every lane of the row
+// getting it: DPP within rows of 16 lanes (quad swaps, half-row and row
+// mirrors), a lane swizzle across 16 for 32-lane rows.
 template <int LPR>
 __device__ __forceinline__ float row_total(float x) {
-#pragma unroll
-  for (int o = 1; o < LPR; o <<= 1) x += __shfl_xor(x, o);
+  if constexpr (LPR >= 2) x += dpp_mov<0xB1>(x);
+  if constexpr (LPR >= 4) x += dpp_mov<0x4E>(x);
+  if constexpr (LPR >= 8) x += dpp_mov<0x141>(x);
+  if constexpr (LPR >= 16) x += dpp_mov<0x140>(x);
+  if constexpr (LPR >= 32) x += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
+  static_assert(LPR <= 32, "rows of at most 32 lanes");
   return x;
 }
 
@@ -68,19 +83,25 @@ __device__ __forceinline__ void ml_merge(float& m, float& l, float m2, float l2)
   m = mn;
 }
 
+// Rows of one chunk of the score passes: pairs are split so that short
+// batches still fill the device.
+constexpr int kChunkRows = kPrefillChunk;
+
 template <class E, int D>
-__global__ __launch_bounds__(kPT) void prefill_score_kernel(PrefillArgs a) {
+struct ScoreCore {
   using elem = typename E::elem;
-  constexpr int EPL = E::kEpl, LPR = D / EPL, RPW = 64 / LPR;
-  const int pair = blockIdx.x;
-  const int b = pair / a.n_kv_heads, g = pair - b * a.n_kv_heads;
-  const int G = a.group;
-  const int P = a.prefill[b];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int c = lane % LPR, rw = lane / LPR;
-  const elem* kp = static_cast<const elem*>(a.k_pre) + (size_t)pair * a.max_prefill * D + c * EPL;
+  static constexpr int EPL = E::kEpl, LPR = D / EPL, RPW = 64 / LPR;
+  static constexpr int kU = 4;  // rows per lane group per iteration (loads first)
   float q[kMaxG][EPL];
-  {
+  const elem* kp;
+  int c, rw;
+
+  __device__ ScoreCore(const PrefillArgs& a, int pair) {
+    const int b = pair / a.n_kv_heads, g = pair - b * a.n_kv_heads, G = a.group;
+    const int lane = threadIdx.x & 63;
+    c = lane % LPR;
+    rw = lane / LPR;
+    kp = static_cast<const elem*>(a.k_pre) + (size_t)pair * a.max_prefill * D + c * EPL;
     const elem* qb = static_cast<const elem*>(a.q_last) + ((size_t)b * a.n_q_heads + (size_t)g * G) * D + c * EPL;
 #pragma unroll
     for (int h = 0; h < kMaxG; ++h) {
@@ -90,35 +111,57 @@ __global__ __launch_bounds__(kPT) void prefill_score_kernel(PrefillArgs a) {
       for (int e = 0; e < EPL; ++e) q[h][e] *= a.scale_log2;
     }
   }
-  auto logits = [&](int row, float (&s)[kMaxG]) {
-    float k[EPL];
-    unpack16(*reinterpret_cast<const uint4*>(kp + (size_t)row * D), k, E{});
+  // Calls f(row, s[kMaxG]) with the log2-domain logits of every row of
+  // [r0, r1) this lane group owns; rows past r1 are loaded clamped, not used.
+  template <class F>
+  __device__ void for_rows(int r0, int r1, F f) const {
+    const int wave = threadIdx.x >> 6;
+    for (int base = r0 + wave * RPW * kU + rw; base < r1; base += kPW * RPW * kU) {
+      uint4 kr[kU];
 #pragma unroll
-    for (int h = 0; h < kMaxG; ++h) {
-      float p = 0.f;
+      for (int u = 0; u < kU; ++u)
+        kr[u] = *reinterpret_cast<const uint4*>(kp + (size_t)min(base + u * RPW, r1 - 1) * D);
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) p = fmaf(q[h][e], k[e], p);
-      s[h] = row_total<LPR>(p);
+      for (int u = 0; u < kU; ++u) {
+        float k[EPL];
+        unpack16(kr[u], k, E{});
+        float s[kMaxG];
+#pragma unroll
+        for (int h = 0; h < kMaxG; ++h) {
+          float p = 0.f;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) p = fmaf(q[h][e], k[e], p);
+          s[h] = row_total<LPR>(p);
+        }
+        if (base + u * RPW < r1) f(base + u * RPW, s);
+      }
     }
-  };
-  // Pass 1: per-head maximum and normaliser (log2 domain), one row lineage per
-  // lane group, then across lanes and waves.
+  }
+};
+
+// Pass 1: per chunk and head, the maximum and normaliser (log2 domain).
+template <class E, int D>
+__global__ __launch_bounds__(kPT) void prefill_stats_kernel(PrefillArgs a) {
+  const int pair = blockIdx.x / a.n_chunks, chunk = blockIdx.x - pair * a.n_chunks;
+  const int b = pair / a.n_kv_heads;
+  const int P = a.prefill[b];
+  const int r0 = chunk * kChunkRows, r1 = min(P, r0 + kChunkRows);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   float m[kMaxG], l[kMaxG];
 #pragma unroll
   for (int h = 0; h < kMaxG; ++h) {
     m[h] = -INFINITY;
     l[h] = 0.f;
   }
-  for (int row = wave * RPW + rw; row < P; row += kPW * RPW) {
-    float s[kMaxG];
-    logits(row, s);
+  const ScoreCore<E, D> core(a, pair);
+  core.for_rows(r0, r1, [&](int, const float(&s)[kMaxG]) {
 #pragma unroll
     for (int h = 0; h < kMaxG; ++h) ml_merge(m[h], l[h], s[h], 1.f);
-  }
+  });
   __shared__ float s_m[kPW][kMaxG], s_l[kPW][kMaxG];
 #pragma unroll
   for (int h = 0; h < kMaxG; ++h) {
-    float mm = c == 0 ? m[h] : -INFINITY, ll = c == 0 ? l[h] : 0.f;  // one lane per row lineage
+    float mm = core.c == 0 ? m[h] : -INFINITY, ll = core.c == 0 ? l[h] : 0.f;  // one lane per row lineage
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) ml_merge(mm, ll, __shfl_xor(mm, o), __shfl_xor(ll, o));
     if (lane == 0) {
@@ -127,32 +170,52 @@ __global__ __launch_bounds__(kPT) void prefill_score_kernel(PrefillArgs a) {
     }
   }
   __syncthreads();
-  float M[kMaxG], invL[kMaxG];
-#pragma unroll
-  for (int h = 0; h < kMaxG; ++h) {
+  if (threadIdx.x < kMaxG) {
+    const int h = threadIdx.x;
     float mm = s_m[0][h], ll = s_l[0][h];
 #pragma unroll
     for (int w = 1; w < kPW; ++w) ml_merge(mm, ll, s_m[w][h], s_l[w][h]);
+    float* st = a.stats + ((size_t)pair * a.n_chunks + chunk) * kMaxG * 2;
+    st[2 * h] = mm;
+    st[2 * h + 1] = ll;
+  }
+}
+
+// Pass 2: the pair's chunk statistics combined in chunk order (the same bits
+// in every chunk), then the importance of the chunk's rows.
+template <class E, int D>
+__global__ __launch_bounds__(kPT) void prefill_importance_kernel(PrefillArgs a) {
+  const int pair = blockIdx.x / a.n_chunks, chunk = blockIdx.x - pair * a.n_chunks;
+  const int b = pair / a.n_kv_heads;
+  const int P = a.prefill[b], G = a.group;
+  const int r0 = chunk * kChunkRows, r1 = min(P, r0 + kChunkRows);
+  if (r0 >= r1) return;
+  const int nck = (P + kChunkRows - 1) / kChunkRows;
+  float M[kMaxG], invL[kMaxG];
+  const float* st = a.stats + (size_t)pair * a.n_chunks * kMaxG * 2;
+#pragma unroll
+  for (int h = 0; h < kMaxG; ++h) {
+    float mm = -INFINITY, ll = 0.f;
+    for (int k = 0; k < nck; ++k) ml_merge(mm, ll, st[k * kMaxG * 2 + 2 * h], st[k * kMaxG * 2 + 2 * h + 1]);
     M[h] = mm;
     invL[h] = 1.0f / ll;
   }
-  // Pass 2: importance of every prefill position.
   float* imp = a.work + (size_t)pair * a.max_prefill;
-  for (int row = wave * RPW + rw; row < P; row += kPW * RPW) {
-    float s[kMaxG];
-    logits(row, s);
+  const ScoreCore<E, D> core(a, pair);
+  core.for_rows(r0, r1, [&](int row, const float(&s)[kMaxG]) {
     float x = 0.f;
 #pragma unroll
     for (int h = 0; h < kMaxG; ++h)
       if (h < G) x = fmaf(exp2f(s[h] - M[h]), invL[h], x);
-    if (c == 0) imp[row] = x;
-  }
+    if (core.c == 0) imp[row] = x;
+  });
 }
 
 // Key of a middle position: importance bits (non-negative floats order as
-// their bit patterns), then the complement of the position.
+// their bit patterns), then the complement of the position (positions are
+// below 65536): 48 bits, unique per position.
 __device__ __forceinline__ uint64_t rank_key(float x, int pos) {
-  return (static_cast<uint64_t>(__float_as_uint(fmaxf(x, 0.f))) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(pos));
+  return (static_cast<uint64_t>(__float_as_uint(fmaxf(x, 0.f))) << 16) | (0xFFFFu - static_cast<uint32_t>(pos));
 }
 
 template <class E, int D>
@@ -175,8 +238,8 @@ __global__ __launch_bounds__(kPT) void prefill_select_kernel(PrefillArgs a) {
     const int lo = sink, hi = P - R;
     uint64_t prefix = 0, mask = 0;
     if (tid == 0) s_want = budget - sink - R;
-    for (int pass = 0; pass < 8; ++pass) {
-      const int shift = 56 - 8 * pass;
+    for (int pass = 0; pass < 6; ++pass) {
+      const int shift = 40 - 8 * pass;
       for (int i = tid; i < 256; i += kPT) s_hist[i] = 0u;
       __syncthreads();
       for (int i = lo + tid; i < hi; i += kPT) {
@@ -243,16 +306,29 @@ __global__ __launch_bounds__(kPT) void prefill_select_kernel(PrefillArgs a) {
   for (int pos = p0; pos < p1; ++pos)
     if (keep(pos) && j < static_cast<uint32_t>(nkeep)) kept[j++] = pos;  // exactly nkeep are kept
   __syncthreads();  // kept[] of this pair complete (same workgroup)
+}
 
-  // Row copies: one row per wave at a time, 16 bytes per lane.
+// Row copies of the kept positions: a workgroup per (pair, 256 kept rows),
+// one row per 64 / pieces lanes, 16 bytes per lane.
+constexpr int kCopyRows = kPrefillCopyRows;
+
+template <class E, int D>
+__global__ __launch_bounds__(kPT) void prefill_copy_kernel(PrefillArgs a) {
+  using elem = typename E::elem;
+  const int pair = blockIdx.x / a.n_copy, part = blockIdx.x - pair * a.n_copy;
+  const int b = pair / a.n_kv_heads;
+  const int P = a.prefill[b], nkeep = min(P, a.budget[b]);
+  const int r0 = part * kCopyRows, r1 = min(nkeep, r0 + kCopyRows);
+  const int32_t* kept = a.kept + (size_t)pair * a.max_budget;
   constexpr int kPieces = D * sizeof(elem) / 16;
+  constexpr int kRowsPerWave = 64 / kPieces;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane / kPieces, piece = lane % kPieces;
   const uint4* ksrc = reinterpret_cast<const uint4*>(static_cast<const elem*>(a.k_pre) + (size_t)pair * a.max_prefill * D);
   const uint4* vsrc = reinterpret_cast<const uint4*>(static_cast<const elem*>(a.v_pre) + (size_t)pair * a.max_prefill * D);
   uint4* kdst = reinterpret_cast<uint4*>(static_cast<elem*>(a.k_cache) + (size_t)pair * a.max_budget * D);
   uint4* vdst = reinterpret_cast<uint4*>(static_cast<elem*>(a.v_cache) + (size_t)pair * a.max_budget * D);
-  constexpr int kRowsPerWave = 64 / kPieces;
-  const int sub = lane / kPieces, piece = lane % kPieces;
-  for (int r = wave * kRowsPerWave + sub; r < nkeep; r += kPW * kRowsPerWave) {
+  for (int r = r0 + wave * kRowsPerWave + sub; r < r1; r += kPW * kRowsPerWave) {
     const int pos = kept[r];
     if (pos < 0 || pos >= P) continue;  // not reached: kept[0, nkeep) holds positions below P
     kdst[(size_t)r * kPieces + piece] = ksrc[(size_t)pos * kPieces + piece];
@@ -262,8 +338,10 @@ __global__ __launch_bounds__(kPT) void prefill_select_kernel(PrefillArgs a) {
 
 template <class E, int D>
 void launch_prefill(const PrefillArgs& a, int n_pairs, hipStream_t s) {
-  hipLaunchKernelGGL((prefill_score_kernel<E, D>), dim3(n_pairs), dim3(kPT), 0, s, a);
+  hipLaunchKernelGGL((prefill_stats_kernel<E, D>), dim3(n_pairs * a.n_chunks), dim3(kPT), 0, s, a);
+  hipLaunchKernelGGL((prefill_importance_kernel<E, D>), dim3(n_pairs * a.n_chunks), dim3(kPT), 0, s, a);
   hipLaunchKernelGGL((prefill_select_kernel<E, D>), dim3(n_pairs), dim3(kPT), 0, s, a);
+  hipLaunchKernelGGL((prefill_copy_kernel<E, D>), dim3(n_pairs * a.n_copy), dim3(kPT), 0, s, a);
 }
 
 }  // namespace
