@@ -152,6 +152,27 @@ lf_status lf_decode_step_dbg(const void* q, const void* k_new, const void* v_new
                              void* out, int32_t* evict_idx, float* scores, float* lse, void* stream);
 
 /*
+ * lf_reset_sequences - restart some sequences of the batch in place (a finished
+ * request's place taken by a new one under continuous batching) while the
+ * others keep their state.  The decode step runs over a static, pre-allocated
+ * cache (LongFlow summary, section 2.C); this only re-initialises the listed
+ * sequences' position, fill level and recent-window ring, exactly as
+ * lf_init_cache does for the whole batch.
+ *   cache    live handle.
+ *   n        number of listed sequences (0: nothing to do).
+ *   seqs     host int32[n]: distinct sequence indices in [0, B).
+ *   seq_len  host int64[n]: tokens the new request has seen; its cached tokens
+ *            are already in the sequence's k_cache/v_cache rows, laid out as
+ *            lf_init_cache describes (for example by lf_prefill_compress).
+ * Budgets and the split of work stay as at init.  The metadata is written by
+ * small uploads ordered on `stream` after the steps already queued there; the
+ * call returns once they completed.  Errors: LF_ERR_ARG, LF_ERR_STATE,
+ * LF_ERR_HIP.
+ */
+lf_status lf_reset_sequences(lf_cache* cache, int32_t n, const int32_t* seqs, const int64_t* seq_len,
+                             void* stream);
+
+/*
  * lf_prefill_work_bytes - size of the device scratch lf_prefill_compress needs
  * (importance of every prefill position of every (sequence, KV head), plus the
  * prefill lengths and budgets).  cfg validated as in lf_init_cache.

@@ -21,6 +21,7 @@ from ._lib import (
     lf_prefill_compress,
     lf_prefill_work_bytes,
     lf_probe_read,
+    lf_reset_sequences,
     lf_state_bytes,
     load_library,
     make_config,
@@ -55,6 +56,7 @@ __all__ = [
     "lf_prefill_compress",
     "lf_prefill_work_bytes",
     "lf_probe_read",
+    "lf_reset_sequences",
     "lf_state_bytes",
     "load_library",
     "make_config",

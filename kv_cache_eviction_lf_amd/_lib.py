@@ -61,6 +61,7 @@ PROTOTYPES = {
     "lf_probe_read_sink_words": (c_int32, []),
     "lf_probe_empty": (c_int32, [c_int32, c_void_p]),
     "lf_prefill_work_bytes": (c_int32, [POINTER(lf_config), c_int32, POINTER(c_size_t)]),
+    "lf_reset_sequences": (c_int32, [c_void_p, c_int32, POINTER(c_int32), POINTER(c_int64), c_void_p]),
     "lf_prefill_compress": (
         c_int32,
         [POINTER(lf_config), POINTER(c_int32), POINTER(c_int32), c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
@@ -137,6 +138,16 @@ def lf_init_cache(cfg: lf_config, budgets, seq_len, k_cache: int, v_cache: int, 
                                         c_void_p(v_cache), c_void_p(state), c_size_t(state_bytes), c_int32(flags),
                                         c_void_p(stream), ctypes.byref(handle)), "lf_init_cache")
     return int(handle.value)
+
+
+def lf_reset_sequences(cache: int, seqs, seq_len, stream: int = 0) -> None:
+    s = [int(x) for x in seqs]
+    sl = [int(x) for x in seq_len]
+    if len(s) != len(sl):
+        raise ValueError("seqs and seq_len must have the same length")
+    _check(load_library().lf_reset_sequences(c_void_p(cache), c_int32(len(s)), (c_int32 * max(1, len(s)))(*s),
+                                             (c_int64 * max(1, len(sl)))(*sl), c_void_p(stream)),
+           "lf_reset_sequences")
 
 
 def lf_prefill_work_bytes(cfg: lf_config, max_prefill: int) -> int:

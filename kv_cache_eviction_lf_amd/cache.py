@@ -95,6 +95,13 @@ class LongFlowCache:
                                     0 if lse is None else lse.data_ptr(), stream)
         return out, evict_idx
 
+    def reset(self, seqs, seq_len) -> None:
+        """Restart sequences `seqs` in place (their K/V rows already hold the new
+        requests' cached tokens) with `seq_len` tokens seen; lf_reset_sequences."""
+        if not self.handle:
+            raise RuntimeError("cache is closed")
+        _lib.lf_reset_sequences(self.handle, list(seqs), list(seq_len), _stream_handle(self.device))
+
     def close(self) -> None:
         if self.handle:
             _lib.lf_free(self.handle)

@@ -27,6 +27,7 @@ struct lf_cache {
   char* state;
   float scale_log2;
   int32_t u_budget;  // the common budget when every sequence has the same one, else 0
+  std::vector<int32_t> budgets;  // per sequence, as validated at init
 };
 
 namespace {
@@ -75,6 +76,27 @@ lf_status validate_config(const lf_config* cfg) {
   const double cache_elems = (double)cfg->batch * cfg->n_kv_heads * cfg->max_budget * cfg->head_dim;
   if (cache_elems > 9.0e15) return fail(LF_ERR_ARG, "cache too large");
   return LF_OK;
+}
+
+// Metadata and ring of sequence b's pairs for a cache holding `t` tokens laid
+// out as lf_init_cache describes (meta and ring indexed by pair, the other
+// PairMeta fields already set by the layout).
+void start_sequence(const lf_config& cfg, int b, int64_t t, int32_t budget, lf::PairMeta* meta, int32_t* ring) {
+  const int R = cfg.recent;
+  const int64_t len = t < budget ? t : budget;
+  for (int g = 0; g < cfg.n_kv_heads; ++g) {
+    const int p = b * cfg.n_kv_heads + g;
+    meta[p].t = (int32_t)t;
+    meta[p].len = (int32_t)len;
+    meta[p].ticket = 0;
+    for (int j = 0; j < R; ++j) ring[(size_t)p * R + j] = -1;
+    // The R newest cached positions [t - R, t): slot = position while the
+    // prefill fits, else they are the last R slots (layout contract).
+    for (int64_t pos = t - R < 0 ? 0 : t - R; pos < t; ++pos) {
+      const int64_t slot = t <= budget ? pos : budget - (t - pos);
+      ring[(size_t)p * R + pos % R] = (int32_t)slot;
+    }
+  }
 }
 
 lf_status validate_budgets(const lf_config* cfg, const int32_t* budgets, std::vector<int32_t>& out) {
@@ -289,25 +311,8 @@ lf_status lf_init_cache(const lf_config* cfg, const int32_t* budgets, const int6
     std::vector<char> img(L.part_ml, 0);
     lf::StateHeader h{lf::kStateMagic, L.n_pairs, L.n_items, L.total_slots};
     std::memcpy(img.data() + L.header, &h, sizeof(h));
-    const int R = cfg->recent;
     int32_t* ring = reinterpret_cast<int32_t*>(img.data() + L.ring);
-    for (int b = 0; b < cfg->batch; ++b) {
-      const int64_t t = seq_len[b];
-      const int64_t len = t < bud[b] ? t : bud[b];
-      for (int g = 0; g < cfg->n_kv_heads; ++g) {
-        const int p = b * cfg->n_kv_heads + g;
-        meta[p].t = (int32_t)t;
-        meta[p].len = (int32_t)len;
-        meta[p].ticket = 0;
-        for (int j = 0; j < R; ++j) ring[(size_t)p * R + j] = -1;
-        // The R newest cached positions [t - R, t): slot = position while the
-        // prefill fits, else they are the last R slots (layout contract).
-        for (int64_t pos = t - R < 0 ? 0 : t - R; pos < t; ++pos) {
-          const int64_t slot = t <= bud[b] ? pos : bud[b] - (t - pos);
-          ring[(size_t)p * R + pos % R] = (int32_t)slot;
-        }
-      }
-    }
+    for (int b = 0; b < cfg->batch; ++b) start_sequence(*cfg, b, seq_len[b], bud[b], meta.data(), ring);
     std::memcpy(img.data() + L.meta, meta.data(), sizeof(lf::PairMeta) * meta.size());
     std::memcpy(img.data() + L.items, items.data(), sizeof(lf::WorkItem) * items.size());
     if (lf::upload_and_wait(state, img.data(), img.size(), stream, g_err, sizeof(g_err))) return LF_ERR_HIP;
@@ -322,6 +327,7 @@ lf_status lf_init_cache(const lf_config* cfg, const int32_t* budgets, const int6
   c->u_budget = bud[0];
   for (int b = 1; b < cfg->batch; ++b)
     if (bud[b] != bud[0]) c->u_budget = 0;
+  c->budgets = bud;
   c->k_cache = k_cache;
   c->v_cache = v_cache;
   c->state = static_cast<char*>(state);
@@ -346,6 +352,44 @@ void lf_free(lf_cache* cache) {
   if (!cache || cache->magic != lf::kHandleMagic) return;
   cache->magic = 0;
   delete cache;
+}
+
+lf_status lf_reset_sequences(lf_cache* cache, int32_t n, const int32_t* seqs, const int64_t* seq_len,
+                             void* stream) {
+  if (!cache) return fail(LF_ERR_ARG, "cache is NULL");
+  if (cache->magic != lf::kHandleMagic) return fail(LF_ERR_STATE, "not a live lf_cache handle");
+  if (n < 0) return fail(LF_ERR_ARG, "n must be >= 0");
+  if (n == 0) return LF_OK;
+  if (!seqs || !seq_len) return fail(LF_ERR_ARG, "seqs and seq_len must be non-NULL");
+  const lf_config& cfg = cache->cfg;
+  std::vector<char> seen(cfg.batch, 0);
+  for (int i = 0; i < n; ++i) {
+    if (seqs[i] < 0 || seqs[i] >= cfg.batch) return fail(LF_ERR_ARG, "seqs[%d] = %d outside [0, %d)", i, seqs[i], cfg.batch);
+    if (seen[seqs[i]]) return fail(LF_ERR_ARG, "sequence %d listed twice", seqs[i]);
+    seen[seqs[i]] = 1;
+    if (seq_len[i] < 0 || seq_len[i] > 0x7FFFFFFFll - 0x10000000ll)
+      return fail(LF_ERR_ARG, "seq_len[%d] = %lld out of range", i, (long long)seq_len[i]);
+  }
+  lf::StateLayout L{};
+  std::vector<lf::PairMeta> meta;
+  lf_status st = make_layout(&cfg, cache->budgets, L, nullptr, &meta);
+  if (st != LF_OK) return st;
+  const int H = cfg.n_kv_heads, R = cfg.recent;
+  std::vector<int32_t> ring((size_t)L.n_pairs * (R > 0 ? R : 1));
+  for (int i = 0; i < n; ++i) {
+    const int b = seqs[i];
+    start_sequence(cfg, b, seq_len[i], cache->budgets[b], meta.data(), ring.data());
+    // A sequence's pairs are contiguous in the metadata and in the ring.
+    if (lf::upload_and_wait(cache->state + L.meta + sizeof(lf::PairMeta) * (size_t)b * H, meta.data() + (size_t)b * H,
+                            sizeof(lf::PairMeta) * H, stream, g_err, sizeof(g_err)))
+      return LF_ERR_HIP;
+    if (R > 0 && lf::upload_and_wait(cache->state + L.ring + sizeof(int32_t) * (size_t)b * H * R,
+                                     ring.data() + (size_t)b * H * R, sizeof(int32_t) * H * R, stream, g_err,
+                                     sizeof(g_err)))
+      return LF_ERR_HIP;
+  }
+  g_err[0] = 0;
+  return LF_OK;
 }
 
 lf_status lf_prefill_work_bytes(const lf_config* cfg, int32_t max_prefill, size_t* bytes) {

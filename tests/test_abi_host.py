@@ -149,3 +149,13 @@ def test_prefill_compress_validates_before_any_device_call():
                                      args["k_pre"], args["v_pre"], args["k_cache"], args["v_cache"], args["kept"],
                                      args["work"], args["work_bytes"])
         assert ei.value.status == LF_ERR_ARG, change
+
+
+def test_reset_sequences_rejects_bad_handles_and_arguments():
+    with pytest.raises(LFError) as ei:
+        _lib.lf_reset_sequences(0, [0], [5])
+    assert ei.value.status == LF_ERR_ARG
+    fake = (ctypes.c_uint64 * 64)()  # wrong magic
+    with pytest.raises(LFError) as ei:
+        _lib.lf_reset_sequences(ctypes.addressof(fake), [0], [5])
+    assert ei.value.status == LF_ERR_STATE

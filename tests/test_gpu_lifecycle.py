@@ -1,0 +1,77 @@
+"""Continuous batching on one static cache (lf_reset_sequences): after some
+decode steps two sequences of the batch are replaced by new requests (their
+rows rewritten, their state restarted), and every sequence, replaced or not,
+stays in parity with the float64 oracle that restarts the same sequences from
+the same contents."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_harness import TIE_EXEMPTION
+from oracle import OracleCache
+from workloads import Workload, initial_sequence
+from workloads.device import device_cache, device_step
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_step(s, out, ev, dec, tol):
+    err = float(np.abs(out.float().cpu().numpy() - dec.out).max())
+    assert err <= tol, f"step {s}: output differs by {err:.3e}"
+    ev_h = ev.cpu().numpy()
+    slots = dec.slot.copy()
+    for b in range(ev_h.shape[0]):
+        for g in range(ev_h.shape[1]):
+            if ev_h[b, g] != dec.evict[b, g]:
+                ok = (dec.evict[b, g] >= 0 and ev_h[b, g] >= 0 and dec.gap[b, g] < TIE_EXEMPTION
+                      and dec.eligible[b][g, ev_h[b, g]])
+                assert ok, f"step {s} seq {b} kv {g}: GPU {ev_h[b, g]}, oracle {dec.evict[b, g]}"
+                slots[b, g] = ev_h[b, g]
+    return slots
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_reset_sequences_mid_run(dtype):
+    from kv_cache_eviction_lf_amd import LongFlowCache
+
+    w = Workload("lifecycle", 4, 8, 2, 128, dtype, 300, 300, 4, 16, 0, seed=31)
+    fresh = w.with_(seed=77, prefill="short", prefill_short=120)  # the new requests
+    dev = torch.device("cuda:0")
+    print(f"[lifecycle] {dtype}", flush=True)
+    K, V, seq_len, bud = device_cache(w, dev)
+    cache = LongFlowCache(K, V, w.n_q_heads, w.sink, w.recent, seq_len, budgets=bud)
+    init = [initial_sequence(w, b) for b in range(w.batch)]
+    oc = OracleCache([x[0] for x in init], [x[1] for x in init], [x[2] for x in init], [x[3] for x in init],
+                     bud, w.n_q_heads, w.sink, w.recent)
+    tol = 2e-2 if dtype == "bf16" else 1e-5
+    for s in range(15):
+        (qd, kd, vd), (q, kn, vn) = device_step(w, s, dev)
+        out, ev = cache.step(qd, kd, vd)
+        oc.commit(_check_step(s, out, ev, oc.decide(q, kn, vn), tol), kn, vn)
+
+    replaced = [1, 3]
+    lens = []
+    for b in replaced:
+        k, v, pos, t = initial_sequence(fresh, b)
+        n = k.shape[1]
+        K[b].zero_()
+        V[b].zero_()
+        K[b, :, :n] = torch.from_numpy(k).to(K.dtype)
+        V[b, :, :n] = torch.from_numpy(v).to(V.dtype)
+        one = OracleCache([k], [v], [pos], [t], int(bud[b]), w.n_q_heads, w.sink, w.recent)
+        oc.k[b], oc.v[b], oc.pos[b], oc.n[b], oc.t[b] = one.k[0], one.v[0], one.pos[0], one.n[0], one.t[0]
+        lens.append(t)
+    cache.reset(replaced, lens)
+
+    for s in range(15, 45):
+        (qd, kd, vd), (q, kn, vn) = device_step(w, s, dev)
+        out, ev = cache.step(qd, kd, vd)
+        oc.commit(_check_step(s, out, ev, oc.decide(q, kn, vn), tol), kn, vn)
+    assert all(oc.n[b] == 120 + 30 for b in replaced)  # appended after the restart
+    Kh, Vh = K.float().cpu().numpy(), V.float().cpu().numpy()
+    for b in range(w.batch):
+        nb = int(bud[b])
+        assert np.array_equal(Kh[b, :, :nb], oc.k[b]) and np.array_equal(Vh[b, :, :nb], oc.v[b]), f"cache of {b}"
+    cache.close()
