@@ -14,29 +14,31 @@
 //
 // Design on gfx950 (wave64, 256 CUs in 8 XCDs, HBM3E):
 //  * The step is HBM-bound: every cached K and V byte is read once, so the
-//    kernel is a streaming scan, not a contraction.  Each lane issues 16-byte
-//    loads of one row segment; a 64-lane load covers 64/LPR consecutive rows
-//    (LPR = lanes per row), one contiguous 1 KiB run per wave load.  Each lane
-//    uses exactly the bytes it loads (the group's q is held in registers), so
-//    K/V go HBM -> VGPR.  The tile loop is software-pipelined: the next tile's
-//    K/V loads are in flight while the current tile is computed.
-//  * bf16 q.k uses v_dot2c_f32_bf16 on the packed pairs as loaded (fp32
-//    accumulate); P.V and all softmax arithmetic are fp32.
+//    kernel is a streaming scan.  K and V rows are read with 16-byte
+//    non-temporal loads straight into registers; each wave walks its quarter
+//    of a chunk in 16-row groups through a ring of register buffers, every
+//    load unconditional so the compiler's waits stay precise.
+//  * bf16: q.k and P.V run on the matrix cores (the 16 rows of a group against
+//    the group's query heads; V through an LDS tile read back transposed), the
+//    online softmax in fp32 on the vector ALUs.  fp32 caches use a vector-ALU
+//    path (stream_valu).
 //  * Work is a static list of (pair, row range) chunks, pair = (sequence, KV
-//    head).  Pairs are split only when there are too few of them to fill the
+//    head); pairs are split only when there are too few of them to fill the
 //    GPU.  A chunk keeps a running max / sum / weighted value sum per head
-//    (online softmax, log2 domain) and stores its raw logits for the score pass.
+//    (log2 domain) and writes its raw logits out for the importance pass, or
+//    keeps them in LDS when its own workgroup will run the pair's tail.
 //  * A pair's tail runs in the workgroup that finishes it: directly when the
-//    pair is one chunk, else in the last-arriving chunk (device-scope ticket,
-//    one release per workgroup).  The tail merges the partials in chunk order,
-//    adds the incoming token, writes the output, computes the exact importance
-//    of every slot from the stored logits with the global max / normaliser,
-//    takes the lexicographic (score, slot) argmin outside the sink slots and the
-//    ring of recent slots, and copies k_new / v_new into the victim slot.  No
-//    other workgroup reads the pair after its ticket, so the in-place write
-//    cannot race with a reader.
-//  * Row reductions use DPP (quad_perm, row mirrors); every other reduction has
-//    a fixed order, so results are bit-reproducible.
+//    pair is one chunk, else in the chunk that takes the last ticket
+//    (device-scope stores and loads on both sides of a relaxed device-scope
+//    fetch-add; the protocol is described at store_wt).  The tail merges the
+//    partials in chunk order, adds the incoming token, writes the output,
+//    computes the exact importance of every slot from the stored logits with
+//    the global max / normaliser, takes the lexicographic (score, slot) argmin
+//    outside the sink slots and the ring of recent slots, and copies k_new /
+//    v_new into the victim slot.  No other workgroup reads the pair after its
+//    ticket, so the in-place write cannot race with a reader.
+//  * Cross-lane reductions use DPP and lane swaps; every reduction has a fixed
+//    order, so results are bit-reproducible.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -207,9 +209,10 @@ __device__ __forceinline__ uint2 load_nt(const uint2* p) {
 }
 
 // Data one workgroup hands to another in the same launch (logits, |v| norms,
-// chunk partials of a split pair) moves only through device-scope atomic
-// stores and loads (relaxed, agent scope; "sc1" on gfx950: written through the
-// non-coherent per-XCD L2 to memory, and read past it).  Each chunk drains its
+// chunk partials of a split pair) moves only through device-scope stores and
+// loads: relaxed agent-scope atomics, or buffer stores and loads with the same
+// "sc1" cache policy (on gfx950: written through the non-coherent per-XCD L2
+// to memory, and read past it).  Each chunk drains its
 // stores (s_waitcnt vmcnt(0): a device-scope store has then reached memory)
 // before its thread 0 increments the pair's ticket with a device-scope RMW, and
 // the chunk that takes the last ticket reads the others' data with
@@ -385,12 +388,13 @@ __device__ __forceinline__ void wave_argmin(float& s, int& i) {
 }
 
 // Tail of one pair: merge chunk partials, output, importance, argmin, insert.
-// Every load that does not depend on the merged statistics (chunk maxima and
-// sums, the ring, the chunk partials, the first logits, the new token) is
-// issued before the first barrier, so the tail costs about one memory round
-// trip plus arithmetic.
+// Every workspace load (chunk statistics and partials, the first logits) is
+// issued at once at the start, so the tail costs about one memory round trip
+// plus arithmetic; the new token's rows and the ring are already in LDS
+// (s_pre) and the bitmap of protected slots was built before the tail.
 // s_part: this workgroup's merged partial ([G][D + 2], used when nchunk == 1);
-// s_tail: scratch of Shape::kTailFloats floats.
+// s_tail: the region after the merge area holds the bitmap and the argmin
+// candidates (Shape::kBitsOffset).
 template <class T, int D, int G>
 __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const float* s_part, float* s_tail,
                           const float* s_logit, bool resident, const float* s_pre) {
