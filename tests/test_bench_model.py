@@ -1,0 +1,51 @@
+"""The benchmark's byte model against the per-step sizes worked out by hand
+from the configurations (K and V read once, the incoming token read and
+written into its slot, q read and the output written), and its refusal of
+more than one GPU.  CPU only."""
+from __future__ import annotations
+
+import importlib.util
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+from workloads import budgets, get_workload
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _bench():
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(ROOT, "bench.py"))
+    m = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(m)
+    return m
+
+
+def test_algorithmic_bytes_of_the_fixed_workloads():
+    m = _bench()
+    # B * Hkv * budget * d * 2 (K, V) * 2 bytes + 2 * B * Hkv * d * 2 * 2 + 2 * B * Hq * d * 2
+    want = {
+        "llama8b_b8": 8 * 8 * 2048 * 128 * 4 + 2 * 8 * 8 * 128 * 4 + 2 * 8 * 32 * 128 * 2,
+        "throughput_b64": 64 * 8 * 4096 * 128 * 4 + 2 * 64 * 8 * 128 * 4 + 2 * 64 * 32 * 128 * 2,
+        "evict_stress": 16 * 4 * 1024 * 128 * 4 + 2 * 16 * 4 * 128 * 4 + 2 * 16 * 28 * 128 * 2,
+    }
+    assert want["llama8b_b8"] == 67_305_472 and want["throughput_b64"] == 1_075_314_688
+    assert want["evict_stress"] == 33_849_344
+    for name, nbytes in want.items():
+        w = get_workload(name)
+        assert m.algorithmic_bytes(w, budgets(w)) == nbytes, name
+    w = get_workload("ragged_b128")
+    bud = budgets(w)
+    ragged = int(np.sum(bud)) * 8 * 128 * 4 + 2 * 128 * 8 * 128 * 4 + 2 * 128 * 40 * 128 * 2
+    assert m.algorithmic_bytes(w, bud) == ragged
+    # a full comparator cache keeps its tokens: the slot write drops out
+    w = get_workload("llama8b_b8")
+    assert m.algorithmic_bytes(w, budgets(w), stored=False) == 67_305_472 - 8 * 8 * 128 * 4
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
