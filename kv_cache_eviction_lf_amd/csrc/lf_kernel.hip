@@ -1112,7 +1112,9 @@ __device__ void stream_mfma(const StepArgs& a, int pair, int start, int count, P
     auto step = [&](const uint4(&kk)[KB], const VLoad(&vv)[4]) {
       process(std::true_type{}, kk, vv, R0 + 16 * g);
       ++g;
-      if ((g & (LR / 16 - 1)) == 0) flush(R0 + 16 * g);
+      // A full buffer goes out, unless the pair is resident (its wave range
+      // fits the buffer exactly, and the tail reads it there).
+      if ((g & (LR / 16 - 1)) == 0 && !keep_last) flush(R0 + 16 * g);
     };
     // One exit only (at the top): a second exit is merged with it by the
     // compiler, and the merged path makes the loop's first wait a full drain.

@@ -134,6 +134,21 @@ def test_full_cache_comparator(kw):
     parity_run(w, 90, score="none", dbg_every=9, tag=f" none {kw}")
 
 
+@pytest.mark.parametrize("kw,score", [
+    (dict(budget_lo=700, budget_hi=700, batch=2), "attn"),
+    (dict(budget_lo=700, budget_hi=700, batch=2), "vl1"),
+    # outlier key channels and planted anchors: logits jump within a pass, so
+    # the probabilities a resident pair keeps are rescaled mid-stream
+    (dict(budget_lo=1024, budget_hi=1024, batch=2, n_q_heads=28, n_kv_heads=4, outlier_channels=4,
+          outlier_scale=10.0, anchors=8, anchor_every=7), "attn"),
+])
+def test_resident_pairs(kw, score):
+    # one chunk per pair whose wave ranges fit the LDS buffers: the tail reads
+    # the stream's probabilities from LDS instead of logits from memory
+    w = _small(**kw)
+    parity_run(w, 60, score=score, chunk_slots=1024, dbg_every=5, tag=f" resident {score}")
+
+
 def test_vl1_on_ragged_small():
     w = _small(budget_lo=150, budget_hi=400, prefill="ragged", batch=4, n_q_heads=14, n_kv_heads=2)
     parity_run(w, 100, score="vl1", dbg_every=9)
