@@ -290,7 +290,6 @@ lf_status lf_init_cache(const lf_config* cfg, const int32_t* budgets, const int6
     return fail(LF_ERR_ARG, "seq_len, k_cache, v_cache and state must be non-NULL");
   if (flags & ~LF_INIT_ATTACH) return fail(LF_ERR_ARG, "unknown flags 0x%x", (unsigned)flags);
   if (reinterpret_cast<uintptr_t>(state) % lf::kAlign) return fail(LF_ERR_ARG, "state must be 256-byte aligned");
-  const size_t esz = cfg->dtype == LF_BF16 ? 2 : 4;
   if (reinterpret_cast<uintptr_t>(k_cache) % 16 || reinterpret_cast<uintptr_t>(v_cache) % 16)
     return fail(LF_ERR_ARG, "k_cache and v_cache must be 16-byte aligned");
   std::vector<int32_t> bud;
@@ -304,7 +303,6 @@ lf_status lf_init_cache(const lf_config* cfg, const int32_t* budgets, const int6
   if ((st = make_layout(cfg, bud, L, &items, &meta)) != LF_OK) return st;
   if (state_bytes < L.total)
     return fail(LF_ERR_ARG, "state_bytes %zu < required %zu (see lf_state_bytes)", state_bytes, L.total);
-  (void)esz;
 
   if (!(flags & LF_INIT_ATTACH)) {
     // Host image of header + meta + ring + work list, uploaded in one copy.
@@ -356,8 +354,8 @@ void lf_free(lf_cache* cache) {
 
 lf_status lf_reset_sequences(lf_cache* cache, int32_t n, const int32_t* seqs, const int64_t* seq_len,
                              void* stream) {
-  if (!cache) return fail(LF_ERR_ARG, "cache is NULL");
-  if (cache->magic != lf::kHandleMagic) return fail(LF_ERR_STATE, "not a live lf_cache handle");
+  lf_status st = check_handle(cache);
+  if (st != LF_OK) return st;
   if (n < 0) return fail(LF_ERR_ARG, "n must be >= 0");
   if (n == 0) return LF_OK;
   if (!seqs || !seq_len) return fail(LF_ERR_ARG, "seqs and seq_len must be non-NULL");
@@ -372,8 +370,7 @@ lf_status lf_reset_sequences(lf_cache* cache, int32_t n, const int32_t* seqs, co
   }
   lf::StateLayout L{};
   std::vector<lf::PairMeta> meta;
-  lf_status st = make_layout(&cfg, cache->budgets, L, nullptr, &meta);
-  if (st != LF_OK) return st;
+  if ((st = make_layout(&cfg, cache->budgets, L, nullptr, &meta)) != LF_OK) return st;
   const int H = cfg.n_kv_heads, R = cfg.recent;
   std::vector<int32_t> ring((size_t)L.n_pairs * (R > 0 ? R : 1));
   for (int i = 0; i < n; ++i) {

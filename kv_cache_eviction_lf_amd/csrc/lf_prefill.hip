@@ -220,7 +220,6 @@ __device__ __forceinline__ uint64_t rank_key(float x, int pos) {
 
 template <class E, int D>
 __global__ __launch_bounds__(kPT) void prefill_select_kernel(PrefillArgs a) {
-  using elem = typename E::elem;
   const int pair = blockIdx.x;
   const int b = pair / a.n_kv_heads;
   const int P = a.prefill[b], budget = a.budget[b];
