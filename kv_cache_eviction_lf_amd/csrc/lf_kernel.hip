@@ -644,7 +644,9 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
       const int quarter = ((budget + kWaves - 1) / kWaves + 15) & ~15;
 #pragma unroll 4
       for (int base = 4 * tid; base < len; base += 4 * kThreads) {
-        const int w = base / quarter;
+        int w = 0;  // base / quarter, by comparisons
+#pragma unroll
+        for (int ww = 1; ww < kWaves; ++ww) w += base >= ww * quarter;
         const float* src = s_logit + w * G * LR + (base - w * quarter);
         float4 lv[G];
 #pragma unroll
