@@ -26,14 +26,18 @@
 //    head); pairs are split only when there are too few of them to fill the
 //    GPU.  A chunk keeps a running max / sum / weighted value sum per head
 //    (log2 domain) and writes its raw logits out for the importance pass, or
-//    keeps them in LDS when its own workgroup will run the pair's tail.
+//    keeps them in LDS when its own workgroup will run the pair's tail: in
+//    fp32 when they fit, else in half precision, from which the tail bounds
+//    every slot's importance and scores exactly, from the key rows, only the
+//    slots that can still be the minimum.
 //  * A pair's tail runs in the workgroup that finishes it: directly when the
 //    pair is one chunk, else in the chunk that takes the last ticket
 //    (device-scope stores and loads on both sides of a relaxed device-scope
 //    fetch-add; the protocol is described at store_wt).  The tail merges the
 //    partials in chunk order, adds the incoming token, writes the output,
-//    computes the exact importance of every slot from the stored logits with
-//    the global max / normaliser, takes the lexicographic (score, slot) argmin
+//    computes the importance of every slot from the stored logits with the
+//    global max / normaliser (exactly; or bounded, then exact for the possible
+//    minima), takes the lexicographic (score, slot) argmin
 //    outside the sink slots and the ring of recent slots, and copies k_new /
 //    v_new into the victim slot.  No other workgroup reads the pair after its
 //    ticket, so the in-place write cannot race with a reader.
@@ -52,6 +56,14 @@ namespace {
 
 constexpr float kNegBig = -1.0e30f;  // running-max start: finite, so empty partials merge without NaN
 constexpr int kWaves = kThreads / 64;
+// Where a pair's logits are when its tail runs: written out to the workspace,
+// or kept in the streaming waves' LDS buffers (an unsplit pair, bf16), in fp32
+// when each wave's range fits kLogitRows rows, else in half precision up to
+// twice that (the tail then bounds every slot's importance from the half
+// values and recomputes the few slots that could be the minimum exactly from
+// their K rows).
+constexpr int kLogitsOut = 0, kLogitsFull = 1, kLogitsHalf = 2;
+constexpr int kCandCap = 256;  // exactly recomputed candidates per pair before the fallback
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
@@ -77,9 +89,10 @@ struct Shape {
   static constexpr int kPartFloats = G * (D + 2);
   static constexpr int kMergeFloats = kWaves * G * (D + 2);
   // Tail scratch after the merge area: bitmap of protected slots, then the
-  // per-wave argmin candidates (bf16: inside the V staging area).
+  // per-wave argmin candidates, the per-wave upper bounds, the candidate count
+  // and list of half-precision resident pairs (bf16: inside the V staging area).
   static constexpr int kBitsOffset = kMergeFloats;
-  static constexpr int kTailFloats = kBitsOffset + kMaxBudget / 32 + 2 * kWaves;
+  static constexpr int kTailFloats = kBitsOffset + kMaxBudget / 32 + 2 * kWaves + kWaves + 1 + kCandCap;
   // bf16: per-wave tile of 16 value rows, rows padded by 32 bytes against LDS bank conflicts.
   static constexpr int kStageRowBytes = D * 2 + 32;
   static constexpr int kStageFloats = kEpl == 8 ? kWaves * 16 * kStageRowBytes / 4 : 0;
@@ -114,7 +127,7 @@ struct Shape {
   // with G = 5 (and 4 stages for G = 4) it cost about 1 %.
   static constexpr int kStages = kMinWavesPerSimd == 1 && G <= 4 ? 3 : 2;
   // The tail's scratch fits in the merge and staging areas, so the logit
-  // buffers survive into the tail (see resident pairs in the kernel).
+  // buffers survive into the tail (see kLogitsFull and kLogitsHalf).
   static_assert(kEpl != 8 || kTailFloats <= kMergeFloats + kStageFloats, "tail scratch overlaps logit buffers");
 };
 
@@ -397,7 +410,7 @@ __device__ __forceinline__ void wave_argmin(float& s, int& i) {
 // candidates (Shape::kBitsOffset).
 template <class T, int D, int G>
 __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const float* s_part, float* s_tail,
-                          const float* s_logit, bool resident, const float* s_pre) {
+                          const float* s_logit, int lmode, const float* s_pre) {
   using elem = typename T::elem;
   constexpr int kOut = (G * D + kThreads - 1) / kThreads;  // output elements per thread
   constexpr int kCB = G <= 4 ? 8 : 4;                       // chunk partials loaded per batch
@@ -438,10 +451,10 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
     kn = *reinterpret_cast<const uint4*>(knsrc + c * EPL);
   }
   // Chunk partials exist only for a split pair; logits and |v| norms are read
-  // from memory unless the pair is resident (norms only when they are used).
+  // from memory unless the pair kept them in LDS (norms only when they are used).
   const auto ml_rs = coh_rsrc(a.part_ml + (size_t)item0 * G * 2, split ? nchunk * G * 8 : 0);
   const auto pa_rs = coh_rsrc(a.part_acc + (size_t)item0 * G * D, split ? nchunk * G * D * 4 : 0);
-  const auto lg_rs = coh_rsrc(a.logits + (size_t)pm.slot0 * G, resident || a.score_none ? 0 : G * lstride * 4);
+  const auto lg_rs = coh_rsrc(a.logits + (size_t)pm.slot0 * G, lmode != kLogitsOut || a.score_none ? 0 : G * lstride * 4);
   const auto vn_rs = coh_rsrc(a.vnorm + pm.slot0, a.vl1 ? lstride * 4 : 0);                     // [lstride]
   uint4 ins;
   {
@@ -459,8 +472,9 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
   auto vnorm4 = [&](int base) { return a.vl1 ? load_c4(vn_rs, base * 4) : make_float4(1.f, 1.f, 1.f, 1.f); };
   // Every workspace value the tail needs first is requested here at once: the
   // chunk partials and the first kPre * 4 * kThreads slots' logits (all of
-  // them for budgets up to that).  A resident pair needs none of them: it
-  // skips the block, which leaves its waits below with nothing to wait for.
+  // them for budgets up to that).  A pair that kept its logits in LDS needs
+  // none of them: it skips the block, which leaves its waits below with
+  // nothing to wait for.
   // Chunk statistics, packed: lane 16 r + c holds, for pass k, head 4 k + r of
   // chunks c, c + 16, c + 32, c + 48 (j = 0..3).
   constexpr int KP = (G + 3) / 4;
@@ -469,7 +483,7 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
   float pa[kOut][kCB];
   float4 lvp[kPre][G];
   float4 v1p[kPre];
-  if (!resident) {
+  if (lmode == kLogitsOut) {
 #pragma unroll
     for (int k = 0; k < KP; ++k)
 #pragma unroll
@@ -636,7 +650,20 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
         besti = lt ? i : besti;
       }
     };
-    if (resident) {
+    // Exact importance of slot i from its key row, on the LPR lanes of one row
+    // lineage (every lane of the lineage gets the same value).
+    auto exact_score = [&](int i) {
+      const int c = lane % LPR;
+      const uint4 kr = *reinterpret_cast<const uint4*>(static_cast<const elem*>(a.k_cache) + pair_off +
+                                                       (size_t)i * D + c * EPL);
+      const float post_scale = T::kEpl == 8 ? a.scale_log2 : 1.0f;
+      float sc = 0.f;
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+        sc = fmaf(fast_exp2(row_sum<LPR>(qk_part<T, G>(q, h, kr)) * post_scale - M[h]), invL[h], sc);
+      return a.vl1 ? sc * load_c1(vn_rs, i * 4) : sc;
+    };
+    if (lmode == kLogitsFull) {
       // Every logit of the pair is still in the streaming waves' LDS buffers:
       // slot s of wave w = s / quarter sits at row s - w * quarter of its buffer
       // (the wave ranges of the stream: the item is [0, budget)).
@@ -652,6 +679,105 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
 #pragma unroll
         for (int h = 0; h < G; ++h) lv[h] = *reinterpret_cast<const float4*>(src + h * LR);
         score4(base, lv, vnorm4(base));
+      }
+    } else if (lmode == kLogitsHalf) {
+      if constexpr (T::kEpl == 8) {
+        // The streaming waves kept half-precision log2-domain logits (same
+        // layout as above, 2 LR rows per head).  Pass 1 bounds every eligible
+        // slot's importance from them; the slots whose lower bound is not
+        // above the smallest upper bound are the only possible minima, and
+        // only they are scored exactly from their key rows.
+        constexpr int LR = Shape<T, D, G>::kLogitRows;
+        constexpr int kCells = 2 * LR * kWaves / (4 * kThreads);  // float4 cells per thread
+        static_assert(kCells * 4 <= 32, "eligibility mask");
+        const int quarter = ((budget + kWaves - 1) / kWaves + 15) & ~15;
+        const _Float16* lb16 = reinterpret_cast<const _Float16*>(s_logit);
+        float* s_ub = s_arg + 2 * kWaves;                           // [kWaves]
+        int* s_ncand = reinterpret_cast<int*>(s_ub + kWaves);      // [1]
+        int* s_cand = s_ncand + 1;                                 // [kCandCap]
+        typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+        // A half value x differs from the fp32 logit by at most |x| 2^-11
+        // (subnormals: 2^-25), and the exact recomputation from it by a few
+        // fp32 roundings; every exp2 argument is therefore within
+        // E = max_h |x_h| 2^-11 + 2^-12 of the exact one, and the importance
+        // within the factors 2^-E and 2^E.  Infinite or NaN logits give no bound.
+        float lo[kCells][4];
+        uint32_t okm = 0;
+        float ub = INFINITY;
+#pragma unroll
+        for (int p = 0; p < kCells; ++p) {
+          const int base = 4 * (tid + p * kThreads);
+          int w = 0;
+#pragma unroll
+          for (int ww = 1; ww < kWaves; ++ww) w += base >= ww * quarter;
+          const _Float16* src = lb16 + w * G * 2 * LR + min(base - w * quarter, 2 * LR - 4);
+          float sc[4] = {0.f, 0.f, 0.f, 0.f}, ex[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            const half4_t x = *reinterpret_cast<const half4_t*>(src + h * 2 * LR);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              const float xf = (float)x[jj];
+              sc[jj] = fmaf(fast_exp2(xf - M[h]), invL[h], sc[jj]);
+              ex[jj] = fmaxf(ex[jj], fabsf(xf));
+            }
+          }
+          const float4 v1 = base < len ? vnorm4(base) : make_float4(1.f, 1.f, 1.f, 1.f);
+          const float v1a[4] = {v1.x, v1.y, v1.z, v1.w};
+          const uint32_t bits = s_bits[min(base, kMaxBudget - 32) >> 5] >> (base & 31);
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int i = base + jj;
+            const bool ok = i < len && i >= a.sink && !((bits >> jj) & 1u);
+            const float v = sc[jj] * v1a[jj];
+            const bool wild = !(ex[jj] < 65504.f);
+            const float E = fmaf(ex[jj], 0x1p-11f, 0x1p-12f);
+            const float up = wild ? INFINITY : v * fast_exp2(E);
+            lo[p][jj] = wild ? 0.f : v * fast_exp2(-E);
+            ub = ok ? fminf(ub, up) : ub;
+            okm |= (ok ? 1u : 0u) << (4 * p + jj);
+          }
+        }
+        {
+          int dummy = 0;
+          wave_argmin(ub, dummy);
+        }
+        if (lane == 0) s_ub[wave] = ub;
+        if (tid == 0) *s_ncand = 0;
+        __syncthreads();
+        float U = s_ub[0];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) U = fminf(U, s_ub[w]);
+#pragma unroll
+        for (int p = 0; p < kCells; ++p)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+            if (((okm >> (4 * p + jj)) & 1u) && lo[p][jj] <= U) {
+              const int k = atomicAdd(s_ncand, 1);
+              if (k < kCandCap) s_cand[k] = 4 * (tid + p * kThreads) + jj;
+            }
+        __syncthreads();
+        const int ncand = *s_ncand;
+        constexpr int RPL = 64 / LPR;  // slots per wave per pass
+        const int r = lane / LPR;
+        if (ncand <= kCandCap && !dbg) {
+          for (int j0 = wave * RPL; j0 < ncand; j0 += kWaves * RPL) {
+            const int jc = j0 + r;
+            const int i = s_cand[min(jc, ncand - 1)];
+            const float v = exact_score(i);
+            argmin_merge(best, besti, jc < ncand ? v : INFINITY, jc < ncand ? i : 0x7FFFFFFF);
+          }
+        } else {
+          // Too many candidates (near-equal importances), or every score is
+          // asked for: exact scores of all filled slots.
+          for (int i0 = wave * RPL; i0 < len; i0 += kWaves * RPL) {
+            const int i = min(i0 + r, len - 1);
+            const float v = exact_score(i);
+            if (dbg && lane % LPR == 0 && i0 + r < len) dbg[i] = v;
+            const bool ok = i0 + r < len && i >= a.sink && !((s_bits[i >> 5] >> (i & 31)) & 1u);
+            argmin_merge(best, besti, ok ? v : INFINITY, ok ? i : 0x7FFFFFFF);
+          }
+        }
       }
     } else {
 #pragma unroll
@@ -881,7 +1007,7 @@ __device__ void stream_valu(const StepArgs& a, int pair, int start, int row_end,
 //    equal the eager form up to rounding.
 // Leaves the wave's partial in s_merge[wave][G][D + 2] like stream_valu.
 template <int D, int G>
-__device__ void stream_mfma(const StepArgs& a, int pair, int start, int count, PairMeta& pm, bool& keep_last,
+__device__ void stream_mfma(const StepArgs& a, int pair, int start, int count, PairMeta& pm, int& lmode,
                             float* s_merge, unsigned char* s_stage, float* s_logit) {
   constexpr int KB = D / 32;  // q.k MFMAs per row group
   constexpr int EV = D / 16;  // value dims per lane per row = P.V MFMAs per value row
@@ -941,8 +1067,9 @@ __device__ void stream_mfma(const StepArgs& a, int pair, int start, int count, P
   // rows clamped to the last valid row (their logits are masked to -inf, so
   // their probabilities are exactly 0).  The raw q.k of every row goes to a
   // per-wave LDS buffer and is written out LR rows at a time as contiguous
-  // runs (see Shape::kLogitRows).  With keep_last (an unsplit pair whose wave
-  // ranges fit the buffers) nothing is written: the tail reads the buffers.
+  // runs (see Shape::kLogitRows).  An unsplit pair whose wave ranges fit the
+  // buffers (kLogitsFull), or fit them in half precision (kLogitsHalf, log2
+  // domain), writes nothing: the tail reads the buffers.
   constexpr int LR = Shape<BF16T, D, G>::kLogitRows;  // rows per logit flush
   const float scale = a.scale_log2;
   // Wave ranges split the item's rows [start, start + count), not the filled
@@ -1024,8 +1151,17 @@ __device__ void stream_mfma(const StepArgs& a, int pair, int start, int count, P
 #pragma unroll
       for (int i = 0; i < 4; ++i) sv[i] = r0 + i < row_end ? sv[i] : -INFINITY;
     }
-    if (n < G)
-      *reinterpret_cast<float4*>(lbuf + n * LR + (r0 - flushed)) = make_float4(sv[0], sv[1], sv[2], sv[3]);
+    if (n < G) {
+      if (lmode == kLogitsHalf) {
+        // log2-domain logits in half precision, 2 LR rows per head (see kLogitsHalf)
+        typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+        const half4_t x = {(_Float16)(sv[0] * scale), (_Float16)(sv[1] * scale), (_Float16)(sv[2] * scale),
+                           (_Float16)(sv[3] * scale)};
+        *reinterpret_cast<half4_t*>(reinterpret_cast<_Float16*>(lbuf) + n * 2 * LR + (r0 - R0)) = x;
+      } else {
+        *reinterpret_cast<float4*>(lbuf + n * LR + (r0 - flushed)) = make_float4(sv[0], sv[1], sv[2], sv[3]);
+      }
+    }
 #pragma unroll
     for (int u = 0; u < 4; ++u) *reinterpret_cast<VLoad*>(wr + u * RS) = vv[u];
     // Group max per head (log2 domain): in-lane over 4 rows, then across the 4 lane groups.
@@ -1107,16 +1243,17 @@ __device__ void stream_mfma(const StepArgs& a, int pair, int start, int count, P
     lg = a.logits + (size_t)pm.slot0 * G;  // [G][lstride]
     vn = a.vnorm + pm.slot0;                // [lstride]
     lrs = wt_rsrc(lg, a.score_none ? 0 : G * lstride * 4);
-    // An unsplit pair whose wave ranges fit the buffers keeps its logits here.
-    keep_last = pm.nchunk == 1 && quarter <= LR;
+    // An unsplit pair whose wave ranges fit the buffers keeps its logits here,
+    // in fp32 up to LR rows per wave, in half precision up to 2 LR.
+    lmode = pm.nchunk != 1 ? kLogitsOut : quarter <= LR ? kLogitsFull : quarter <= 2 * LR ? kLogitsHalf : kLogitsOut;
 #pragma unroll
     for (int s = 1; s < NS - 1; ++s) load_grp(kbuf[s], vbuf[s], s < nfull);
     auto step = [&](const uint4(&kk)[KB], const VLoad(&vv)[4]) {
       process(std::true_type{}, kk, vv, R0 + 16 * g);
       ++g;
-      // A full buffer goes out, unless the pair is resident (its wave range
-      // fits the buffer exactly, and the tail reads it there).
-      if ((g & (LR / 16 - 1)) == 0 && !keep_last) flush(R0 + 16 * g);
+      // A full buffer goes out, unless the pair keeps its logits in LDS for
+      // the tail.
+      if ((g & (LR / 16 - 1)) == 0 && lmode == kLogitsOut) flush(R0 + 16 * g);
     };
     // One exit only (at the top): a second exit is merged with it by the
     // compiler, and the merged path makes the loop's first wait a full drain.
@@ -1142,7 +1279,7 @@ __device__ void stream_mfma(const StepArgs& a, int pair, int start, int count, P
         vbuf[0][u] = *reinterpret_cast<const VLoad*>(Vp + (size_t)min(Rp + 4 * j + u, last) * D + EV * n);
       process(std::false_type{}, kbuf[0], vbuf[0], Rp);
     }
-    if (flushed < Rend && !keep_last) flush(Rend);
+    if (flushed < Rend && lmode == kLogitsOut) flush(Rend);
   }
   lsum += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(lsum), 0x401F));
   {
@@ -1189,10 +1326,10 @@ void lf_step_kernel(StepArgs a) {
   float* s_logit = s_work + S::kMergeFloats + S::kStageFloats;
   float* s_pre = smem + S::kSmemFloats - S::kPreFloats;  // prefetched tail inputs
   PairMeta pm;
-  bool resident = false;  // an unsplit bf16 pair whose logits stay in LDS for its tail
+  int lmode = kLogitsOut;  // where the pair's logits are for its tail
   if constexpr (T::kEpl == 8) {
     if (tid < 64) prefetch_tail<D, G>(a, pair, s_pre);
-    stream_mfma<D, G>(a, pair, it.start, it.count, pm, resident, s_work,
+    stream_mfma<D, G>(a, pair, it.start, it.count, pm, lmode, s_work,
                       reinterpret_cast<unsigned char*>(s_work + S::kMergeFloats), s_logit);
     // The prefetch completed before wave 0's first stream wait (loads return in
     // order); without a row to stream, wave 0 waits for it here.
@@ -1252,7 +1389,7 @@ void lf_step_kernel(StepArgs a) {
     __syncthreads();
     if (!s_last) return;
   }
-  pair_tail<T, D, G>(a, pair, pm, s_part, s_work, s_logit, resident, s_pre);
+  pair_tail<T, D, G>(a, pair, pm, s_part, s_work, s_logit, lmode, s_pre);
 }
 
 template <class T, int D, int G>

@@ -149,6 +149,51 @@ def test_resident_pairs(kw, score):
     parity_run(w, 60, score=score, chunk_slots=1024, dbg_every=5, tag=f" resident {score}")
 
 
+@pytest.mark.parametrize("kw,score,chunk", [
+    (dict(budget_lo=6000, budget_hi=6000, batch=2), "attn", 8192),                 # G = 4
+    (dict(budget_lo=6000, budget_hi=6000, batch=2), "vl1", 8192),
+    (dict(budget_lo=1500, budget_hi=1500, batch=2, n_q_heads=16, n_kv_heads=2), "attn", 2048),  # G = 8
+    (dict(budget_lo=2000, budget_hi=2000, batch=2, n_q_heads=28, n_kv_heads=4, outlier_channels=4,
+          outlier_scale=10.0, anchors=8, anchor_every=7), "attn", 2048),           # G = 7, large logits
+    (dict(budget_lo=3900, budget_hi=8000, batch=4, prefill="ragged", n_q_heads=10, n_kv_heads=2), "attn",
+     8192),                                                                        # G = 5, fp32 and half pairs
+])
+def test_half_resident_pairs(kw, score, chunk):
+    # one chunk per pair whose wave ranges are up to twice the LDS buffers: the
+    # stream keeps half-precision logits, the tail bounds every importance from
+    # them and scores the possible minima exactly from their key rows
+    w = _small(**kw)
+    parity_run(w, 30, score=score, chunk_slots=chunk, dbg_every=6, tag=f" half {score}")
+
+
+def test_half_resident_equal_importances():
+    # every cached key the same: all importances tie, more slots are possible
+    # minima than the exact pass takes, and the tail scores every slot exactly;
+    # the first eligible slot (just past the sink window) must go
+    from kv_cache_eviction_lf_amd import LongFlowCache
+    from oracle import OracleCache
+
+    B, Hq, Hkv, D, bud, sink, recent = 1, 8, 2, 128, 6000, 4, 16
+    gen = torch.Generator().manual_seed(3)
+    bf = lambda *shape: torch.randn(*shape, generator=gen).to(torch.bfloat16)  # noqa: E731
+    K = bf(D).expand(B, Hkv, bud, D).contiguous()
+    V = bf(B, Hkv, bud, D)
+    q, kn, vn = bf(B, Hq, D), bf(B, Hkv, D), bf(B, Hkv, D)
+    dev = torch.device("cuda:0")
+    Kd, Vd = K.to(dev), V.to(dev)
+    cache = LongFlowCache(Kd, Vd, Hq, sink, recent, [bud] * B, budgets=[bud] * B, chunk_slots=8192)
+    out, ev = cache.step(q.to(dev), kn.to(dev), vn.to(dev))
+    torch.cuda.synchronize()
+    f64 = lambda x: x.double().numpy()  # noqa: E731
+    oc = OracleCache([f64(K[0])], [f64(V[0])], [np.arange(bud)], [bud], [bud], Hq, sink, recent)
+    dec = oc.decide(f64(q), f64(kn), f64(vn))
+    assert dec.evict.tolist() == [[sink] * Hkv]
+    assert ev.cpu().tolist() == [[sink] * Hkv]
+    err = float(np.abs(out.float().cpu().numpy() - dec.out).max())
+    assert err <= 2e-2, err
+    cache.close()
+
+
 def test_vl1_on_ragged_small():
     w = _small(budget_lo=150, budget_hi=400, prefill="ragged", batch=4, n_q_heads=14, n_kv_heads=2)
     parity_run(w, 100, score="vl1", dbg_every=9)
