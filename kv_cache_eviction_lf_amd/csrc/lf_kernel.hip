@@ -697,15 +697,19 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
         int* s_cand = s_ncand + 1;                                 // [kCandCap]
         typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
         // A half value x differs from the fp32 logit by at most |x| 2^-11
-        // (subnormals: 2^-25), and the exact recomputation from it by a few
-        // fp32 roundings; every exp2 argument is therefore within
-        // E = max_h |x_h| 2^-11 + 2^-12 of the exact one, and the importance
-        // within the factors 2^-E and 2^E.  Infinite or NaN logits give no bound.
-        float lo[kCells][4];
+        // (subnormals: 2^-25), and that logit from the exact recomputation by
+        // a few fp32 roundings; every exp2 argument is therefore within
+        // E = max_h |x_h| 2^-11 (1 + 2^-8) + 2^-10 of the exact one, and the
+        // importance v within the factors 2^-E >= 1 - E and 2^E <= 1 + E (E <= 1).
+        // Logits of magnitude 2040 and above (infinite, NaN) give no bound:
+        // the slot is always a candidate.  Cells past the filled slots are
+        // skipped (the test is the same on the whole workgroup).
+        float lo[kCells][4] = {};
         uint32_t okm = 0;
         float ub = INFINITY;
 #pragma unroll
         for (int p = 0; p < kCells; ++p) {
+          if (4 * p * kThreads >= len) continue;
           const int base = 4 * (tid + p * kThreads);
           int w = 0;
 #pragma unroll
@@ -730,10 +734,10 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
             const int i = base + jj;
             const bool ok = i < len && i >= a.sink && !((bits >> jj) & 1u);
             const float v = sc[jj] * v1a[jj];
-            const bool wild = !(ex[jj] < 65504.f);
-            const float E = fmaf(ex[jj], 0x1p-11f, 0x1p-12f);
-            const float up = wild ? INFINITY : v * fast_exp2(E);
-            lo[p][jj] = wild ? 0.f : v * fast_exp2(-E);
+            const bool wild = !(ex[jj] < 2040.f);
+            const float E = fmaf(ex[jj], 0x1.01p-11f, 0x1p-10f);
+            const float up = wild ? INFINITY : fmaf(v, E, v);
+            lo[p][jj] = wild ? 0.f : fmaf(-v, E, v);
             ub = ok ? fminf(ub, up) : ub;
             okm |= (ok ? 1u : 0u) << (4 * p + jj);
           }
@@ -760,7 +764,14 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
         const int ncand = *s_ncand;
         constexpr int RPL = 64 / LPR;  // slots per wave per pass
         const int r = lane / LPR;
-        if (ncand <= kCandCap && !dbg) {
+        if (ncand == 1 && !dbg) {
+          // The minimum is always a candidate (its lower bound is not above
+          // its score, which is not above the smallest upper bound), and an
+          // exact tie with it would be one too: a single candidate is the
+          // argmin, and its score is not needed.
+          best = 0.f;
+          besti = s_cand[0];
+        } else if (ncand <= kCandCap && !dbg) {
           for (int j0 = wave * RPL; j0 < ncand; j0 += kWaves * RPL) {
             const int jc = j0 + r;
             const int i = s_cand[min(jc, ncand - 1)];
