@@ -174,7 +174,7 @@ def main():
 
     from kv_cache_eviction_lf_amd import LongFlowCache, _lib
     from workloads import budgets, get_workload
-    from workloads.device import device_cache, device_step
+    from workloads.device import device_cache, device_step_pool
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -192,15 +192,17 @@ def main():
     layer_kv = int(np.sum(bud)) * w.n_kv_heads * w.head_dim * 2 * (2 if w.dtype == "bf16" else 4)
     L = args.layers or max(1, math.ceil(2 * MALL_BYTES / layer_kv))
 
-    # L independent layer caches (distinct seeds) and a pool of step inputs.
+    # L independent layer caches (distinct seeds) and fresh inputs for every
+    # step (a repeated input would fill the caches with copies of its tokens).
     caches = []
     for layer in range(L):
         wl = w.with_(seed=w.seed + 7919 * layer)
         K, V, seq_len, _ = device_cache(wl, dev)
         caches.append(LongFlowCache(K, V, w.n_q_heads, w.sink, w.recent, seq_len, budgets=bud,
                                     score=args.score, chunk_slots=args.chunk))
-    P = 8
-    pool = [device_step(w, s, dev)[0] for s in range(P)]
+    step_in = 2 * (w.batch * w.n_q_heads + 2 * w.batch * w.n_kv_heads) * w.head_dim * (2 if w.dtype == "bf16" else 4)
+    P = max(1, min(args.warmup + args.steps, (16 << 30) // step_in))
+    pool = device_step_pool(w, P, dev)
     outs = [torch.empty_like(pool[0][0]) for _ in range(L)]
     evs = [torch.empty((w.batch, w.n_kv_heads), dtype=torch.int32, device=dev) for _ in range(L)]
     ptrs = [(caches[i].handle, outs[i].data_ptr(), evs[i].data_ptr()) for i in range(L)]
@@ -225,7 +227,7 @@ def main():
     graphs = {}
 
     def graph_for(n, base):
-        key = (n, base % (L * P))
+        key = (n, base)
         if key not in graphs:
             g = torch.cuda.CUDAGraph()
             cs = torch.cuda.Stream()
@@ -237,35 +239,28 @@ def main():
         return graphs[key]
 
     chunk = 512 if not args.eager else 0
-    # pre-capture what the timed region replays (capture launches nothing)
+
+    def pieces(n, base):  # graphs of up to `chunk` consecutive steps
+        return [(min(chunk, n - i), base + i) for i in range(0, n, chunk)]
+
+    # pre-capture what warm-up and the timed region replay (capture launches nothing)
     if not args.eager:
-        full, rem = divmod(args.steps, chunk)
-        if full:
-            graph_for(chunk, 0)
-        if rem:
-            graph_for(rem, full * chunk)
-        wf, wr = divmod(args.warmup, chunk)
-        if wf:
-            graph_for(chunk, 0)
-        if wr:
-            graph_for(wr, wf * chunk)
+        for n, b in pieces(args.warmup, 0) + pieces(args.steps, args.warmup):
+            graph_for(n, b)
 
-    def run(n):
+    def run(n, base):
         if args.eager:
-            run_eager(n, 0)
+            run_eager(n, base)
             return
-        full, rem = divmod(n, chunk)
-        for i in range(full):
-            graph_for(chunk, 0).replay()
-        if rem:
-            graph_for(rem, full * chunk).replay()
+        for m, b in pieces(n, base):
+            graph_for(m, b).replay()
 
-    run(args.warmup)
+    run(args.warmup, 0)
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record(cur)
-    run(args.steps)
+    run(args.steps, args.warmup)
     ev1.record(cur)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0

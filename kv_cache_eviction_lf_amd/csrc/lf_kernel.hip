@@ -652,16 +652,26 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
     };
     // Exact importance of slot i from its key row, on the LPR lanes of one row
     // lineage (every lane of the lineage gets the same value).
-    auto exact_score = [&](int i) {
+    // (key_row issues the loads, exact_score takes them, so that several
+    // slots' loads can be in flight together.)
+    struct KeyRow {
+      uint4 k;
+      float vn;
+    };
+    auto key_row = [&](int i) {
       const int c = lane % LPR;
-      const uint4 kr = *reinterpret_cast<const uint4*>(static_cast<const elem*>(a.k_cache) + pair_off +
-                                                       (size_t)i * D + c * EPL);
+      KeyRow kr;
+      kr.k = *reinterpret_cast<const uint4*>(static_cast<const elem*>(a.k_cache) + pair_off + (size_t)i * D + c * EPL);
+      kr.vn = load_c1(vn_rs, i * 4);  // empty range unless VL1
+      return kr;
+    };
+    auto exact_score = [&](const KeyRow& kr) {
       const float post_scale = T::kEpl == 8 ? a.scale_log2 : 1.0f;
       float sc = 0.f;
 #pragma unroll
       for (int h = 0; h < G; ++h)
-        sc = fmaf(fast_exp2(row_sum<LPR>(qk_part<T, G>(q, h, kr)) * post_scale - M[h]), invL[h], sc);
-      return a.vl1 ? sc * load_c1(vn_rs, i * 4) : sc;
+        sc = fmaf(fast_exp2(row_sum<LPR>(qk_part<T, G>(q, h, kr.k)) * post_scale - M[h]), invL[h], sc);
+      return a.vl1 ? sc * kr.vn : sc;
     };
     if (lmode == kLogitsFull) {
       // Every logit of the pair is still in the streaming waves' LDS buffers:
@@ -775,18 +785,27 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
           for (int j0 = wave * RPL; j0 < ncand; j0 += kWaves * RPL) {
             const int jc = j0 + r;
             const int i = s_cand[min(jc, ncand - 1)];
-            const float v = exact_score(i);
+            const float v = exact_score(key_row(i));
             argmin_merge(best, besti, jc < ncand ? v : INFINITY, jc < ncand ? i : 0x7FFFFFFF);
           }
         } else {
           // Too many candidates (near-equal importances), or every score is
           // asked for: exact scores of all filled slots.
-          for (int i0 = wave * RPL; i0 < len; i0 += kWaves * RPL) {
-            const int i = min(i0 + r, len - 1);
-            const float v = exact_score(i);
-            if (dbg && lane % LPR == 0 && i0 + r < len) dbg[i] = v;
-            const bool ok = i0 + r < len && i >= a.sink && !((s_bits[i >> 5] >> (i & 31)) & 1u);
-            argmin_merge(best, besti, ok ? v : INFINITY, ok ? i : 0x7FFFFFFF);
+          // Four rows per lane lineage in flight; per lane the slots
+          // increase, but the merge keeps the first index on ties anyway.
+          constexpr int kU = 4;
+          for (int i0 = wave * RPL * kU; i0 < len; i0 += kWaves * RPL * kU) {
+            KeyRow kr[kU];
+#pragma unroll
+            for (int u = 0; u < kU; ++u) kr[u] = key_row(min(i0 + u * RPL + r, len - 1));
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+              const int i = i0 + u * RPL + r;
+              const float v = exact_score(kr[u]);
+              if (dbg && lane % LPR == 0 && i < len) dbg[i] = v;
+              const bool ok = i < len && i >= a.sink && !((s_bits[min(i, len - 1) >> 5] >> (i & 31)) & 1u);
+              argmin_merge(best, besti, ok ? v : INFINITY, ok ? i : 0x7FFFFFFF);
+            }
           }
         }
       }

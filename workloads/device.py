@@ -47,3 +47,35 @@ def device_step(w: Workload, step: int, device):
     dt = torch_dtype(w)
     dev = tuple(torch.from_numpy(x).to(dt).to(device) for x in (q, k, v))
     return dev, (q, k, v)
+
+
+def device_step_pool(w: Workload, n: int, device, first_step: int = 0):
+    """Inputs of ``n`` consecutive decode steps (from ``first_step``) drawn on the
+    device, for timing runs that give every step fresh inputs: a list of
+    (q, k_new, v_new) tensors.  Same distributions and structure as
+    step_inputs (N(0,1) draws rounded to the workload's dtype, the key outlier
+    channels scaled, anchor queries on event steps), from a seeded torch
+    generator instead of the per-step numpy streams, so the values differ from
+    step_inputs'."""
+    from .generate import anchor_directions, anchor_event, outlier_channels
+
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(np.random.SeedSequence([w.seed, 0x5EED]).generate_state(1)[0]))
+    dt = torch_dtype(w)
+    ch = torch.as_tensor(outlier_channels(w), device=device)
+    z = None
+    if w.anchors:
+        z = torch.as_tensor(np.stack([anchor_directions(w, b) for b in range(w.batch)]), dtype=torch.float32,
+                            device=device)  # [B][Hkv][anchors][d]
+    pool = []
+    for s in range(first_step, first_step + n):
+        q = torch.randn((w.batch, w.n_q_heads, w.head_dim), generator=gen, device=device)
+        k = torch.randn((w.batch, w.n_kv_heads, w.head_dim), generator=gen, device=device)
+        v = torch.randn((w.batch, w.n_kv_heads, w.head_dim), generator=gen, device=device)
+        ev = anchor_event(w, s)
+        if ev is not None:
+            q = z[:, :, ev, :].repeat_interleave(w.group, dim=1) + 0.5 * q
+        if ch.numel():
+            k[..., ch] *= w.outlier_scale
+        pool.append((q.to(dt), k.to(dt), v.to(dt)))
+    return pool
