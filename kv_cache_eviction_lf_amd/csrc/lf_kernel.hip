@@ -102,8 +102,13 @@ struct Shape {
   // number of runs rather than their size: against 128-row runs, 512-row runs
   // take the throughput shape (B64, budget 4096) from 212 to 180 us per step,
   // 1024-row runs the ragged shape (budgets up to 8192) from 530 to 448 us, at
-  // the price of one workgroup per compute unit for G = 5.
-  static constexpr int kLogitRows = G <= 5 ? 1024 : 256;
+  // the price of one workgroup per compute unit for G = 5.  Unsplit pairs write
+  // nothing when their logits fit the buffers (fp32) or twice them (half
+  // precision), so for G <= 4 512 rows suffice for budgets up to 4096 and leave
+  // room for two workgroups per compute unit, one's tail overlapping the
+  // other's stream (B64 budget 4096: 165.8 -> 162.4 us; B8 budget 2048 split
+  // four ways: 19.0 -> 18.6 us).
+  static constexpr int kLogitRows = G <= 4 ? 512 : G <= 5 ? 1024 : 256;
   static constexpr int kLogitFloats = kEpl == 8 ? kWaves * G * kLogitRows : 0;
   static constexpr int kStreamFloats = kMergeFloats + kStageFloats + kLogitFloats;
   // bf16: the tail's inputs that do not depend on the stream (the group's q,

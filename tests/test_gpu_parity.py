@@ -150,8 +150,9 @@ def test_resident_pairs(kw, score):
 
 
 @pytest.mark.parametrize("kw,score,chunk", [
-    (dict(budget_lo=6000, budget_hi=6000, batch=2), "attn", 8192),                 # G = 4
-    (dict(budget_lo=6000, budget_hi=6000, batch=2), "vl1", 8192),
+    (dict(budget_lo=3000, budget_hi=3000, batch=2), "attn", 4096),                 # G = 4
+    (dict(budget_lo=3000, budget_hi=3000, batch=2), "vl1", 4096),
+    (dict(budget_lo=6000, budget_hi=6000, batch=2, n_q_heads=10, n_kv_heads=2), "vl1", 8192),  # G = 5
     (dict(budget_lo=1500, budget_hi=1500, batch=2, n_q_heads=16, n_kv_heads=2), "attn", 2048),  # G = 8
     (dict(budget_lo=2000, budget_hi=2000, batch=2, n_q_heads=28, n_kv_heads=4, outlier_channels=4,
           outlier_scale=10.0, anchors=8, anchor_every=7), "attn", 2048),           # G = 7, large logits
@@ -173,7 +174,7 @@ def test_half_resident_equal_importances():
     from kv_cache_eviction_lf_amd import LongFlowCache
     from oracle import OracleCache
 
-    B, Hq, Hkv, D, bud, sink, recent = 1, 8, 2, 128, 6000, 4, 16
+    B, Hq, Hkv, D, bud, sink, recent = 1, 8, 2, 128, 4000, 4, 16
     gen = torch.Generator().manual_seed(3)
     bf = lambda *shape: torch.randn(*shape, generator=gen).to(torch.bfloat16)  # noqa: E731
     K = bf(D).expand(B, Hkv, bud, D).contiguous()
