@@ -173,6 +173,26 @@ lf_status lf_reset_sequences(lf_cache* cache, int32_t n, const int32_t* seqs, co
                              void* stream);
 
 /*
+ * lf_reset_sequences_budget - lf_reset_sequences that also gives the listed
+ * sequences new slot budgets (a new request with another memory allowance
+ * takes a finished one's place).  Every other sequence keeps its state and
+ * budget.  The split of work and the workspace layout follow the new budgets,
+ * so the call reads the metadata and rings back from the device after the
+ * steps queued on `stream`, keeps the other sequences' positions, fill levels
+ * and rings, restarts the listed ones as lf_reset_sequences does, and writes
+ * the whole metadata and work list back; it returns once that completed.
+ *   budgets  host int32[n]: new budget of each listed sequence, in
+ *            (sink + recent, max_budget]; the listed sequence's cached tokens
+ *            (seq_len, capped at the new budget) are already laid out in its
+ *            k_cache/v_cache rows as lf_init_cache describes.
+ * The state buffer passed to lf_init_cache (its state_bytes) must hold the
+ * layout of the new budgets (lf_state_bytes with them); otherwise LF_ERR_ARG
+ * and nothing changes.  Errors: LF_ERR_ARG, LF_ERR_STATE, LF_ERR_HIP.
+ */
+lf_status lf_reset_sequences_budget(lf_cache* cache, int32_t n, const int32_t* seqs, const int64_t* seq_len,
+                                    const int32_t* budgets, void* stream);
+
+/*
  * lf_prefill_work_bytes - size of the device scratch lf_prefill_compress needs
  * (importance of every prefill position of every (sequence, KV head), plus the
  * prefill lengths and budgets).  cfg validated as in lf_init_cache.

@@ -62,6 +62,8 @@ PROTOTYPES = {
     "lf_probe_empty": (c_int32, [c_int32, c_void_p]),
     "lf_prefill_work_bytes": (c_int32, [POINTER(lf_config), c_int32, POINTER(c_size_t)]),
     "lf_reset_sequences": (c_int32, [c_void_p, c_int32, POINTER(c_int32), POINTER(c_int64), c_void_p]),
+    "lf_reset_sequences_budget": (
+        c_int32, [c_void_p, c_int32, POINTER(c_int32), POINTER(c_int64), POINTER(c_int32), c_void_p]),
     "lf_prefill_compress": (
         c_int32,
         [POINTER(lf_config), POINTER(c_int32), POINTER(c_int32), c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
@@ -148,6 +150,18 @@ def lf_reset_sequences(cache: int, seqs, seq_len, stream: int = 0) -> None:
     _check(load_library().lf_reset_sequences(c_void_p(cache), c_int32(len(s)), (c_int32 * max(1, len(s)))(*s),
                                              (c_int64 * max(1, len(sl)))(*sl), c_void_p(stream)),
            "lf_reset_sequences")
+
+
+def lf_reset_sequences_budget(cache: int, seqs, seq_len, budgets, stream: int = 0) -> None:
+    s = [int(x) for x in seqs]
+    sl = [int(x) for x in seq_len]
+    bd = [int(x) for x in budgets]
+    if not (len(s) == len(sl) == len(bd)):
+        raise ValueError("seqs, seq_len and budgets must have the same length")
+    m = max(1, len(s))
+    _check(load_library().lf_reset_sequences_budget(c_void_p(cache), c_int32(len(s)), (c_int32 * m)(*s),
+                                                    (c_int64 * m)(*sl), (c_int32 * m)(*bd), c_void_p(stream)),
+           "lf_reset_sequences_budget")
 
 
 def lf_prefill_work_bytes(cfg: lf_config, max_prefill: int) -> int:

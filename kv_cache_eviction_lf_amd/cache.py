@@ -32,11 +32,14 @@ class LongFlowCache:
 
     k_cache, v_cache: contiguous device tensors [B][Hkv][max_budget][d] (bf16 or
     fp32), filled as the C ABI's lf_init_cache describes; budgets: per-sequence
-    budgets (None = max_budget); seq_len: tokens already seen per sequence."""
+    budgets (None = max_budget); seq_len: tokens already seen per sequence.
+    state_capacity: bytes to allocate for the state buffer when none is given
+    (at least what the budgets need); a larger buffer lets reset() give
+    sequences larger budgets later."""
 
     def __init__(self, k_cache: torch.Tensor, v_cache: torch.Tensor, n_q_heads: int, sink: int, recent: int,
                  seq_len, budgets=None, score: str = "attn", softmax_scale: float = 0.0, chunk_slots: int = 0,
-                 state: torch.Tensor | None = None, attach: bool = False):
+                 state: torch.Tensor | None = None, attach: bool = False, state_capacity: int = 0):
         if k_cache.dim() != 4:
             raise ValueError("k_cache must be [B][Hkv][max_budget][d]")
         if k_cache.dtype not in _DTYPES:
@@ -56,7 +59,7 @@ class LongFlowCache:
         if state is None:
             if attach:
                 raise ValueError("attach needs the saved state tensor")
-            state = torch.empty(self.state_bytes, dtype=torch.uint8, device=self.device)
+            state = torch.empty(max(self.state_bytes, int(state_capacity)), dtype=torch.uint8, device=self.device)
         elif state.numel() < self.state_bytes or state.device != self.device:
             raise ValueError("state tensor too small or on another device")
         self.state = state
@@ -95,12 +98,21 @@ class LongFlowCache:
                                     0 if lse is None else lse.data_ptr(), stream)
         return out, evict_idx
 
-    def reset(self, seqs, seq_len) -> None:
+    def reset(self, seqs, seq_len, budgets=None) -> None:
         """Restart sequences `seqs` in place (their K/V rows already hold the new
-        requests' cached tokens) with `seq_len` tokens seen; lf_reset_sequences."""
+        requests' cached tokens) with `seq_len` tokens seen; lf_reset_sequences,
+        or lf_reset_sequences_budget when new `budgets` are given for them."""
         if not self.handle:
             raise RuntimeError("cache is closed")
-        _lib.lf_reset_sequences(self.handle, list(seqs), list(seq_len), _stream_handle(self.device))
+        if budgets is None:
+            _lib.lf_reset_sequences(self.handle, list(seqs), list(seq_len), _stream_handle(self.device))
+            return
+        _lib.lf_reset_sequences_budget(self.handle, list(seqs), list(seq_len), list(budgets),
+                                       _stream_handle(self.device))
+        full = list(self.budgets) if self.budgets is not None else [self.max_budget] * self.B
+        for b, nb in zip(seqs, budgets):
+            full[int(b)] = int(nb)
+        self.budgets = full
 
     def close(self) -> None:
         if self.handle:

@@ -25,6 +25,7 @@ struct lf_cache {
   void* k_cache;
   void* v_cache;
   char* state;
+  size_t state_bytes;  // capacity of the caller's state buffer
   float scale_log2;
   int32_t u_budget;  // the common budget when every sequence has the same one, else 0
   std::vector<int32_t> budgets;  // per sequence, as validated at init
@@ -214,6 +215,25 @@ lf_status check_handle(const lf_cache* c) {
   return LF_OK;
 }
 
+// Arguments shared by lf_reset_sequences and lf_reset_sequences_budget.
+lf_status check_reset_args(const lf_cache* cache, int32_t n, const int32_t* seqs, const int64_t* seq_len) {
+  lf_status st = check_handle(cache);
+  if (st != LF_OK) return st;
+  if (n < 0) return fail(LF_ERR_ARG, "n must be >= 0");
+  if (n == 0) return LF_OK;
+  if (!seqs || !seq_len) return fail(LF_ERR_ARG, "seqs and seq_len must be non-NULL");
+  const lf_config& cfg = cache->cfg;
+  std::vector<char> seen(cfg.batch, 0);
+  for (int i = 0; i < n; ++i) {
+    if (seqs[i] < 0 || seqs[i] >= cfg.batch) return fail(LF_ERR_ARG, "seqs[%d] = %d outside [0, %d)", i, seqs[i], cfg.batch);
+    if (seen[seqs[i]]) return fail(LF_ERR_ARG, "sequence %d listed twice", seqs[i]);
+    seen[seqs[i]] = 1;
+    if (seq_len[i] < 0 || seq_len[i] > 0x7FFFFFFFll - 0x10000000ll)
+      return fail(LF_ERR_ARG, "seq_len[%d] = %lld out of range", i, (long long)seq_len[i]);
+  }
+  return LF_OK;
+}
+
 lf_status step_impl(const void* q, const void* k_new, const void* v_new, lf_cache* cache, void* out,
                     int32_t* evict_idx, float* scores, float* lse, void* stream) {
   lf_status st = check_handle(cache);
@@ -329,6 +349,7 @@ lf_status lf_init_cache(const lf_config* cfg, const int32_t* budgets, const int6
   c->k_cache = k_cache;
   c->v_cache = v_cache;
   c->state = static_cast<char*>(state);
+  c->state_bytes = state_bytes;
   const double scale = cfg->softmax_scale > 0 ? cfg->softmax_scale : 1.0 / std::sqrt((double)cfg->head_dim);
   c->scale_log2 = (float)(scale * 1.4426950408889634);
   *out = c;
@@ -354,20 +375,9 @@ void lf_free(lf_cache* cache) {
 
 lf_status lf_reset_sequences(lf_cache* cache, int32_t n, const int32_t* seqs, const int64_t* seq_len,
                              void* stream) {
-  lf_status st = check_handle(cache);
-  if (st != LF_OK) return st;
-  if (n < 0) return fail(LF_ERR_ARG, "n must be >= 0");
-  if (n == 0) return LF_OK;
-  if (!seqs || !seq_len) return fail(LF_ERR_ARG, "seqs and seq_len must be non-NULL");
+  lf_status st = check_reset_args(cache, n, seqs, seq_len);
+  if (st != LF_OK || n == 0) return st;
   const lf_config& cfg = cache->cfg;
-  std::vector<char> seen(cfg.batch, 0);
-  for (int i = 0; i < n; ++i) {
-    if (seqs[i] < 0 || seqs[i] >= cfg.batch) return fail(LF_ERR_ARG, "seqs[%d] = %d outside [0, %d)", i, seqs[i], cfg.batch);
-    if (seen[seqs[i]]) return fail(LF_ERR_ARG, "sequence %d listed twice", seqs[i]);
-    seen[seqs[i]] = 1;
-    if (seq_len[i] < 0 || seq_len[i] > 0x7FFFFFFFll - 0x10000000ll)
-      return fail(LF_ERR_ARG, "seq_len[%d] = %lld out of range", i, (long long)seq_len[i]);
-  }
   lf::StateLayout L{};
   std::vector<lf::PairMeta> meta;
   if ((st = make_layout(&cfg, cache->budgets, L, nullptr, &meta)) != LF_OK) return st;
@@ -385,6 +395,53 @@ lf_status lf_reset_sequences(lf_cache* cache, int32_t n, const int32_t* seqs, co
                                      sizeof(g_err)))
       return LF_ERR_HIP;
   }
+  g_err[0] = 0;
+  return LF_OK;
+}
+
+lf_status lf_reset_sequences_budget(lf_cache* cache, int32_t n, const int32_t* seqs, const int64_t* seq_len,
+                                    const int32_t* budgets, void* stream) {
+  lf_status st = check_reset_args(cache, n, seqs, seq_len);
+  if (st != LF_OK || n == 0) return st;
+  if (!budgets) return fail(LF_ERR_ARG, "budgets must be non-NULL");
+  const lf_config& cfg = cache->cfg;
+  std::vector<int32_t> nb = cache->budgets;
+  for (int i = 0; i < n; ++i) nb[seqs[i]] = budgets[i];
+  std::vector<int32_t> checked;
+  if ((st = validate_budgets(&cfg, nb.data(), checked)) != LF_OK) return st;
+  lf::StateLayout L{};
+  std::vector<lf::WorkItem> items;
+  std::vector<lf::PairMeta> meta;
+  if ((st = make_layout(&cfg, nb, L, &items, &meta)) != LF_OK) return st;
+  if (L.total > cache->state_bytes)
+    return fail(LF_ERR_ARG, "the new budgets need %zu state bytes, the buffer holds %zu", L.total,
+                cache->state_bytes);
+  // Header, metadata and rings lie before the work list at offsets that depend
+  // only on the numbers of pairs and ring entries, so the old and the new
+  // layout place them alike.  Read them back (after the queued steps), keep
+  // every other sequence's position, fill level and ring, restart the listed
+  // ones, and write header, metadata, rings and the new work list back.
+  const lf::StateLayout& old = cache->lay;
+  std::vector<char> img(L.part_ml, 0);
+  if (lf::download_and_wait(img.data(), cache->state, old.items, stream, g_err, sizeof(g_err))) return LF_ERR_HIP;
+  const lf::PairMeta* cur = reinterpret_cast<const lf::PairMeta*>(img.data() + L.meta);
+  for (int p = 0; p < L.n_pairs; ++p) {
+    meta[p].t = cur[p].t;
+    meta[p].len = cur[p].len;
+    meta[p].ticket = 0;
+  }
+  int32_t* ring = reinterpret_cast<int32_t*>(img.data() + L.ring);
+  for (int i = 0; i < n; ++i) start_sequence(cfg, seqs[i], seq_len[i], nb[seqs[i]], meta.data(), ring);
+  lf::StateHeader h{lf::kStateMagic, L.n_pairs, L.n_items, L.total_slots};
+  std::memcpy(img.data() + L.header, &h, sizeof(h));
+  std::memcpy(img.data() + L.meta, meta.data(), sizeof(lf::PairMeta) * meta.size());
+  std::memcpy(img.data() + L.items, items.data(), sizeof(lf::WorkItem) * items.size());
+  if (lf::upload_and_wait(cache->state, img.data(), img.size(), stream, g_err, sizeof(g_err))) return LF_ERR_HIP;
+  cache->lay = L;
+  cache->budgets = nb;
+  cache->u_budget = nb[0];
+  for (int b = 1; b < cfg.batch; ++b)
+    if (nb[b] != nb[0]) cache->u_budget = 0;
   g_err[0] = 0;
   return LF_OK;
 }

@@ -129,5 +129,6 @@ int launch_step(int dtype, int head_dim, int group, const StepArgs& a, void* str
 int launch_prefill(int dtype, int head_dim, const PrefillArgs& a, int n_pairs, void* stream, char* err,
                    size_t errlen);
 int upload_and_wait(void* dst, const void* src, size_t bytes, void* stream, char* err, size_t errlen);
+int download_and_wait(void* dst, const void* src, size_t bytes, void* stream, char* err, size_t errlen);
 
 }  // namespace lf

@@ -1489,4 +1489,15 @@ int upload_and_wait(void* dst, const void* src, size_t bytes, void* stream, char
   return 0;
 }
 
+int download_and_wait(void* dst, const void* src, size_t bytes, void* stream, char* err, size_t errlen) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
+    snprintf(err, errlen, "state download failed: %s", hipGetErrorString(e));
+    return 1;
+  }
+  return 0;
+}
+
 }  // namespace lf

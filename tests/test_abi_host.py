@@ -159,3 +159,11 @@ def test_reset_sequences_rejects_bad_handles_and_arguments():
     with pytest.raises(LFError) as ei:
         _lib.lf_reset_sequences(ctypes.addressof(fake), [0], [5])
     assert ei.value.status == LF_ERR_STATE
+    with pytest.raises(LFError) as ei:
+        _lib.lf_reset_sequences_budget(0, [0], [5], [100])
+    assert ei.value.status == LF_ERR_ARG
+    with pytest.raises(LFError) as ei:
+        _lib.lf_reset_sequences_budget(ctypes.addressof(fake), [0], [5], [100])
+    assert ei.value.status == LF_ERR_STATE
+    with pytest.raises(ValueError):
+        _lib.lf_reset_sequences_budget(0, [0, 1], [5, 5], [100])

@@ -75,3 +75,64 @@ def test_reset_sequences_mid_run(dtype):
         nb = int(bud[b])
         assert np.array_equal(Kh[b, :, :nb], oc.k[b]) and np.array_equal(Vh[b, :, :nb], oc.v[b]), f"cache of {b}"
     cache.close()
+
+
+def test_reset_sequences_with_new_budgets():
+    # new requests with other budgets take two places (one larger, one smaller
+    # and not yet full); the work split changes (equal budgets -> ragged ->
+    # equal again) while the other sequences carry on
+    from kv_cache_eviction_lf_amd import LongFlowCache, LFError
+
+    w = Workload("rebudget", 4, 8, 2, 128, "bf16", 300, 300, 4, 16, 0, seed=41)
+    dev = torch.device("cuda:0")
+    print("[lifecycle] new budgets", flush=True)
+    K, V, seq_len, bud = device_cache(w, dev, max_budget=512)
+    bud = [int(x) for x in bud]
+    tight = LongFlowCache(K, V, w.n_q_heads, w.sink, w.recent, seq_len, budgets=bud)
+    with pytest.raises(LFError):  # its state buffer holds only the initial layout
+        tight.reset([1], [500], budgets=[500])
+    tight.close()
+    cache = LongFlowCache(K, V, w.n_q_heads, w.sink, w.recent, seq_len, budgets=bud, state_capacity=1 << 22)
+    init = [initial_sequence(w, b) for b in range(w.batch)]
+    oc = OracleCache([x[0] for x in init], [x[1] for x in init], [x[2] for x in init], [x[3] for x in init],
+                     bud, w.n_q_heads, w.sink, w.recent)
+    s = 0
+
+    def run(n):
+        nonlocal s
+        for _ in range(n):
+            (qd, kd, vd), (q, kn, vn) = device_step(w, s, dev)
+            out, ev = cache.step(qd, kd, vd)
+            oc.commit(_check_step(s, out, ev, oc.decide(q, kn, vn), 2e-2), kn, vn)
+            s += 1
+
+    def replace(seqs, requests):
+        lens, news = [], []
+        for b, req in zip(seqs, requests):
+            k, v, pos, t = initial_sequence(req, b)
+            n = k.shape[1]
+            nb = int(req.budget_lo)
+            K[b].zero_()
+            V[b].zero_()
+            K[b, :, :n] = torch.from_numpy(k).to(K.dtype)
+            V[b, :, :n] = torch.from_numpy(v).to(V.dtype)
+            one = OracleCache([k], [v], [pos], [t], nb, w.n_q_heads, w.sink, w.recent)
+            oc.k[b], oc.v[b], oc.pos[b], oc.n[b], oc.t[b] = one.k[0], one.v[0], one.pos[0], one.n[0], one.t[0]
+            oc.budget[b] = nb
+            bud[b] = nb
+            lens.append(t)
+            news.append(nb)
+        cache.reset(seqs, lens, budgets=news)
+
+    run(12)
+    replace([1, 3], [w.with_(seed=77, budget_lo=500, budget_hi=500),
+                     w.with_(seed=78, budget_lo=120, budget_hi=120, prefill="short", prefill_short=90)])
+    run(40)  # sequence 3 fills its 120 slots and starts evicting
+    assert oc.n[3] == 120
+    replace([1, 3], [w.with_(seed=79), w.with_(seed=80)])  # every budget 300 again
+    run(12)
+    Kh, Vh = K.float().cpu().numpy(), V.float().cpu().numpy()
+    for b in range(w.batch):
+        nb = bud[b]
+        assert np.array_equal(Kh[b, :, :nb], oc.k[b]) and np.array_equal(Vh[b, :, :nb], oc.v[b]), f"cache of {b}"
+    cache.close()
