@@ -83,3 +83,31 @@ def test_anchor_workload_structure():
     qq = q[0].reshape(w.n_kv_heads, w.group, -1)
     cos = (qq * z[:, None]).sum(-1) / np.linalg.norm(qq, axis=-1) / np.linalg.norm(z, axis=-1)[:, None]
     assert cos.min() > 0.8
+
+
+def test_device_step_pool_matches_the_step_recipe():
+    # the benchmark's on-device inputs: shapes, dtype, seeded reproducibility,
+    # outlier key channels and anchor queries as in step_inputs (on the CPU here)
+    from workloads import anchor_event
+    from workloads.device import device_step_pool
+    from workloads.generate import anchor_directions
+
+    w = get_workload("evict_stress").with_(batch=4)
+    ev_step = w.anchor_every  # first anchor event
+    a = device_step_pool(w, 3, "cpu", first_step=ev_step - 1)
+    b = device_step_pool(w, 3, "cpu", first_step=ev_step - 1)
+    for (q, k, v), (q2, k2, v2) in zip(a, b):
+        assert q.shape == (w.batch, w.n_q_heads, w.head_dim) and q.dtype == torch.bfloat16
+        assert k.shape == v.shape == (w.batch, w.n_kv_heads, w.head_dim)
+        assert torch.equal(q, q2) and torch.equal(k, k2) and torch.equal(v, v2)
+    ch = outlier_channels(w)
+    k = torch.stack([x[1] for x in a]).float()
+    rest = np.setdiff1d(np.arange(w.head_dim), ch)
+    assert 6.0 < float(k[..., ch].std()) / float(k[..., rest].std()) < 16.0
+    assert anchor_event(w, ev_step) is not None and anchor_event(w, ev_step - 1) is None
+    q_ev = a[1][0].double().numpy()
+    z = np.stack([anchor_directions(w, s) for s in range(w.batch)])[:, :, anchor_event(w, ev_step), :]
+    zq = np.repeat(z, w.group, axis=1)
+    resid = q_ev - zq  # 0.5 N(0, 1) plus bf16 rounding
+    assert 0.4 < resid.std() < 0.6
+    assert abs(float(a[0][0].double().std()) - 1.0) < 0.1  # no anchor on the step before
