@@ -158,6 +158,9 @@ def test_resident_pairs(kw, score):
           outlier_scale=10.0, anchors=8, anchor_every=7), "attn", 2048),           # G = 7, large logits
     (dict(budget_lo=3900, budget_hi=8000, batch=4, prefill="ragged", n_q_heads=10, n_kv_heads=2), "attn",
      8192),                                                                        # G = 5, fp32 and half pairs
+    (dict(budget_lo=3000, budget_hi=3000, batch=2, n_q_heads=6, n_kv_heads=2, head_dim=64), "vl1", 4096),  # d 64
+    (dict(budget_lo=2500, budget_hi=4000, batch=3, n_q_heads=2, n_kv_heads=2, sink=0, recent=0), "attn",
+     4096),                                                                        # G = 1, no windows
 ])
 def test_half_resident_pairs(kw, score, chunk):
     # one chunk per pair whose wave ranges are up to twice the LDS buffers: the
