@@ -165,8 +165,6 @@ lf_status make_layout(const lf_config* cfg, const std::vector<int32_t>& bud, lf:
   off = align_up(off + sizeof(float) * (size_t)group * cfg->head_dim * W);
   L.logits = off;  // none without importance (LF_SCORE_NONE)
   if (cfg->score != LF_SCORE_NONE) off = align_up(off + sizeof(float) * (size_t)group * S);
-  L.vnorm = off;
-  if (cfg->score == LF_SCORE_VL1) off = align_up(off + sizeof(float) * S);
   L.total = off;
   if (items || meta) {
     // Workspace offsets follow pair order; work items follow sequences in
@@ -259,7 +257,6 @@ lf_status step_impl(const void* q, const void* k_new, const void* v_new, lf_cach
   a.part_ml = reinterpret_cast<float*>(s + L.part_ml);
   a.part_acc = reinterpret_cast<float*>(s + L.part_acc);
   a.logits = reinterpret_cast<float*>(s + L.logits);
-  a.vnorm = reinterpret_cast<float*>(s + L.vnorm);
   a.n_items = L.n_items;
   a.n_pairs = cfg.batch * cfg.n_kv_heads;
   a.n_q_heads = cfg.n_q_heads;

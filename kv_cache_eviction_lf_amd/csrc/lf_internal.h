@@ -52,7 +52,7 @@ struct StateHeader {
 
 // Byte offsets of the regions of the caller's state buffer.
 struct StateLayout {
-  size_t header, meta, ring, items, part_ml, part_acc, logits, vnorm, total;
+  size_t header, meta, ring, items, part_ml, part_acc, logits, total;
   int32_t n_pairs, n_items, total_slots, chunk, max_nchunk;
 };
 
@@ -72,8 +72,7 @@ struct StepArgs {
   const WorkItem* items;
   float* part_ml;   // [n_items][G][2]: (max of log2-domain logits, sum of exp2)
   float* part_acc;  // [n_items][G][d]
-  float* logits;    // per pair [G][budget], log2-domain logits of this step
-  float* vnorm;     // per pair [budget], |v|_1 of every slot (VL1 only)
+  float* logits;    // per pair [G][budget], logits of this step (VL1: plus log2 |v|_1)
   int32_t n_items;
   int32_t n_pairs;  // batch * n_kv_heads
   int32_t n_q_heads;

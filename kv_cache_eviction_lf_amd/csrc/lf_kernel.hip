@@ -455,12 +455,11 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
     load_q<T, G>(q, qsrc + c * EPL, D, a.scale_log2);
     kn = *reinterpret_cast<const uint4*>(knsrc + c * EPL);
   }
-  // Chunk partials exist only for a split pair; logits and |v| norms are read
-  // from memory unless the pair kept them in LDS (norms only when they are used).
+  // Chunk partials exist only for a split pair; logits are read from memory
+  // unless the pair kept them in LDS.
   const auto ml_rs = coh_rsrc(a.part_ml + (size_t)item0 * G * 2, split ? nchunk * G * 8 : 0);
   const auto pa_rs = coh_rsrc(a.part_acc + (size_t)item0 * G * D, split ? nchunk * G * D * 4 : 0);
   const auto lg_rs = coh_rsrc(a.logits + (size_t)pm.slot0 * G, lmode != kLogitsOut || a.score_none ? 0 : G * lstride * 4);
-  const auto vn_rs = coh_rsrc(a.vnorm + pm.slot0, a.vl1 ? lstride * 4 : 0);                     // [lstride]
   uint4 ins;
   {
     const int c = min(tid, 2 * kVec - 1), which = c / kVec, part = c - which * kVec;
@@ -470,11 +469,11 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
   float vnv[kOut];
 #pragma unroll
   for (int o = 0; o < kOut; ++o) vnv[o] = load_elem<T>(vnp, min(tid + o * kThreads, G * D - 1) % D);
-  // bf16 streaming stores raw q.k; fp32 streaming stores log2-domain logits.
-  const float ls = T::kEpl == 8 ? a.scale_log2 : 1.0f;
+  // bf16 streaming stores raw q.k, fp32 streaming log2-domain logits; with VL1
+  // both store the log2-domain logit plus log2 |v|_1 of the slot, so the
+  // weight-times-norm product is one exp2.
+  const float ls = T::kEpl == 8 && !a.vl1 ? a.scale_log2 : 1.0f;
   auto logit4 = [&](int h, int base) { return load_c4(lg_rs, (h * lstride + base) * 4); };
-  // Norms in the loops below are loaded only when used (no wait otherwise).
-  auto vnorm4 = [&](int base) { return a.vl1 ? load_c4(vn_rs, base * 4) : make_float4(1.f, 1.f, 1.f, 1.f); };
   // Every workspace value the tail needs first is requested here at once: the
   // chunk partials and the first kPre * 4 * kThreads slots' logits (all of
   // them for budgets up to that).  A pair that kept its logits in LDS needs
@@ -487,7 +486,6 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
   float2 ml[KP][4];
   float pa[kOut][kCB];
   float4 lvp[kPre][G];
-  float4 v1p[kPre];
   if (lmode == kLogitsOut) {
 #pragma unroll
     for (int k = 0; k < KP; ++k)
@@ -504,7 +502,6 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
       const int base = min(4 * (tid + p * kThreads), lstride - 4);
 #pragma unroll
       for (int h = 0; h < G; ++h) lvp[p][h] = logit4(h, base);
-      v1p[p] = load_c4(vn_rs, base * 4);  // empty range unless used (selected at use)
     }
   } else {
 #pragma unroll
@@ -624,7 +621,7 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
   // every slot, so a full cache stores nothing.
   if (!a.score_none) {
     float* dbg = a.dbg_scores ? a.dbg_scores + (size_t)pair * a.max_budget : nullptr;
-    auto score4 = [&](int base, const float4(&lv)[G], const float4& v1) {
+    auto score4 = [&](int base, const float4(&lv)[G]) {
       const uint32_t bits = s_bits[base >> 5] >> (base & 31);
       float sc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -634,10 +631,6 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
         sc[2] = fmaf(fast_exp2(fmaf(lv[h].z, ls, -M[h])), invL[h], sc[2]);
         sc[3] = fmaf(fast_exp2(fmaf(lv[h].w, ls, -M[h])), invL[h], sc[3]);
       }
-      sc[0] *= v1.x;
-      sc[1] *= v1.y;
-      sc[2] *= v1.z;
-      sc[3] *= v1.w;
       if (dbg) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
@@ -659,15 +652,15 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
     // lineage (every lane of the lineage gets the same value).
     // (key_row issues the loads, exact_score takes them, so that several
     // slots' loads can be in flight together.)
+    // With VL1 the value row is loaded too and its |v|_1 taken the stream's way.
     struct KeyRow {
-      uint4 k;
-      float vn;
+      uint4 k, v;
     };
     auto key_row = [&](int i) {
-      const int c = lane % LPR;
+      const size_t off = pair_off + (size_t)i * D + (lane % LPR) * EPL;
       KeyRow kr;
-      kr.k = *reinterpret_cast<const uint4*>(static_cast<const elem*>(a.k_cache) + pair_off + (size_t)i * D + c * EPL);
-      kr.vn = load_c1(vn_rs, i * 4);  // empty range unless VL1
+      kr.k = *reinterpret_cast<const uint4*>(static_cast<const elem*>(a.k_cache) + off);
+      kr.v = *reinterpret_cast<const uint4*>(static_cast<const elem*>(a.v_cache) + off);
       return kr;
     };
     auto exact_score = [&](const KeyRow& kr) {
@@ -676,7 +669,15 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
 #pragma unroll
       for (int h = 0; h < G; ++h)
         sc = fmaf(fast_exp2(row_sum<LPR>(qk_part<T, G>(q, h, kr.k)) * post_scale - M[h]), invL[h], sc);
-      return a.vl1 ? sc * kr.vn : sc;
+      if (a.vl1) {
+        float vx[EPL];
+        unpack<T>(kr.v, vx);
+        float n1 = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) n1 += fabsf(vx[e]);
+        sc *= row_sum<LPR>(n1);
+      }
+      return sc;
     };
     if (lmode == kLogitsFull) {
       // Every logit of the pair is still in the streaming waves' LDS buffers:
@@ -693,7 +694,7 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
         float4 lv[G];
 #pragma unroll
         for (int h = 0; h < G; ++h) lv[h] = *reinterpret_cast<const float4*>(src + h * LR);
-        score4(base, lv, vnorm4(base));
+        score4(base, lv);
       }
     } else if (lmode == kLogitsHalf) {
       if constexpr (T::kEpl == 8) {
@@ -741,14 +742,12 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
               ex[jj] = fmaxf(ex[jj], fabsf(xf));
             }
           }
-          const float4 v1 = base < len ? vnorm4(base) : make_float4(1.f, 1.f, 1.f, 1.f);
-          const float v1a[4] = {v1.x, v1.y, v1.z, v1.w};
           const uint32_t bits = s_bits[min(base, kMaxBudget - 32) >> 5] >> (base & 31);
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
             const int i = base + jj;
             const bool ok = i < len && i >= a.sink && !((bits >> jj) & 1u);
-            const float v = sc[jj] * v1a[jj];
+            const float v = sc[jj];
             const bool wild = !(ex[jj] < 2040.f);
             const float E = fmaf(ex[jj], 0x1.01p-11f, 0x1p-10f);
             const float up = wild ? INFINITY : fmaf(v, E, v);
@@ -818,13 +817,13 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
 #pragma unroll
       for (int p = 0; p < kPre; ++p)
         if (4 * (tid + p * kThreads) < len)
-          score4(4 * (tid + p * kThreads), lvp[p], a.vl1 ? v1p[p] : make_float4(1.f, 1.f, 1.f, 1.f));
+          score4(4 * (tid + p * kThreads), lvp[p]);
 #pragma unroll 2
       for (int base = 4 * (tid + kPre * kThreads); base < len; base += 4 * kThreads) {
         float4 lv[G];
 #pragma unroll
         for (int h = 0; h < G; ++h) lv[h] = logit4(h, base);
-        score4(base, lv, vnorm4(base));
+        score4(base, lv);
       }
     }
     wave_argmin(best, besti);
@@ -879,7 +878,7 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
 // per row lineage, P.V by FMA.  Leaves the wave's partial (max, sum, weighted
 // value sum per head) in s_merge[wave][G][D + 2].
 template <class T, int D, int G>
-__device__ void stream_valu(const StepArgs& a, int pair, int start, int row_end, float* lg, float* vn, int lstride,
+__device__ void stream_valu(const StepArgs& a, int pair, int start, int row_end, float* lg, int lstride,
                             float* s_merge) {
   using S = Shape<T, D, G>;
   constexpr int EPL = S::kEpl, LPR = S::kLpr, RPL = S::kRpl, U = S::kU, TILE = S::kTile;
@@ -925,29 +924,27 @@ __device__ void stream_valu(const StepArgs& a, int pair, int start, int row_end,
       const int row = tb + lane_row + u * RPL;
 #pragma unroll
       for (int h = 0; h < G; ++h) s[u][h] = row_sum<LPR>(qk_part<T, G>(q, h, kk[u])) * post_scale;
-      if (row < row_end) {
-        if (c < G && !a.score_none) {
-          float mine = s[u][0];
-#pragma unroll
-          for (int h = 1; h < G; ++h) mine = c == h ? s[u][h] : mine;
-          store_wt(&lg[(size_t)c * lstride + row], mine);
-        }
-      } else {
-#pragma unroll
-        for (int h = 0; h < G; ++h) s[u][h] = -INFINITY;
-      }
-    }
-    if (a.vl1) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int row = tb + lane_row + u * RPL;
+      // With VL1 the stored logit carries log2 |v|_1 of the row (weight times
+      // norm = exp2 of the sum), so no norm is stored apart.
+      float lnorm = 0.f;
+      if (a.vl1) {
         float vx[EPL];
         unpack<T>(vv[u], vx);
         float n1 = 0.f;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) n1 += fabsf(vx[e]);
-        n1 = row_sum<LPR>(n1);
-        if (c == 0 && row < row_end) store_wt(&vn[row], n1);
+        lnorm = __log2f(row_sum<LPR>(n1));
+      }
+      if (row < row_end) {
+        if (c < G && !a.score_none) {
+          float mine = s[u][0];
+#pragma unroll
+          for (int h = 1; h < G; ++h) mine = c == h ? s[u][h] : mine;
+          store_wt(&lg[(size_t)c * lstride + row], mine + lnorm);
+        }
+      } else {
+#pragma unroll
+        for (int h = 0; h < G; ++h) s[u][h] = -INFINITY;
       }
     }
 #pragma unroll
@@ -1120,7 +1117,6 @@ __device__ void stream_mfma(const StepArgs& a, int pair, int start, int count, P
   // Known once the metadata has arrived (see below).
   int row_end = 0, Rend = 0, nfull = 0, Rp = 0, lstride = 0;
   float* lg = nullptr;
-  float* vn = nullptr;
   __amdgpu_buffer_rsrc_t lrs;
 
   auto flush = [&](int upto) {  // write buffered logits of rows [flushed, upto)
@@ -1186,15 +1182,39 @@ __device__ void stream_mfma(const StepArgs& a, int pair, int start, int count, P
 #pragma unroll
       for (int i = 0; i < 4; ++i) sv[i] = r0 + i < row_end ? sv[i] : -INFINITY;
     }
+    // What the tail scores from: the raw q.k, or with VL1 the log2-domain
+    // logit plus log2 |v|_1 of the row (weight times norm = exp2 of the sum),
+    // so no norm is stored apart.  Every lane of row group j holds the norms
+    // of rows r0 .. r0 + 3 after the 16-lane sum.
+    float st[4] = {sv[0], sv[1], sv[2], sv[3]};
+    if (a.vl1) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        float vf[EV];
+        if constexpr (EV == 8) {
+          unpack<BF16T>(vv[u], vf);
+        } else {
+          vf[0] = bf16_lo(vv[u].x);
+          vf[1] = bf16_hi(vv[u].x);
+          vf[2] = bf16_lo(vv[u].y);
+          vf[3] = bf16_hi(vv[u].y);
+        }
+        float n1 = 0.f;
+#pragma unroll
+        for (int e = 0; e < EV; ++e) n1 += fabsf(vf[e]);
+        st[u] = fmaf(sv[u], scale, __log2f(row_sum<16>(n1)));
+      }
+    }
     if (n < G) {
       if (lmode == kLogitsHalf) {
-        // log2-domain logits in half precision, 2 LR rows per head (see kLogitsHalf)
+        // log2-domain values in half precision, 2 LR rows per head (see kLogitsHalf)
         typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
-        const half4_t x = {(_Float16)(sv[0] * scale), (_Float16)(sv[1] * scale), (_Float16)(sv[2] * scale),
-                           (_Float16)(sv[3] * scale)};
+        const float f = a.vl1 ? 1.0f : scale;
+        const half4_t x = {(_Float16)(st[0] * f), (_Float16)(st[1] * f), (_Float16)(st[2] * f),
+                           (_Float16)(st[3] * f)};
         *reinterpret_cast<half4_t*>(reinterpret_cast<_Float16*>(lbuf) + n * 2 * LR + (r0 - R0)) = x;
       } else {
-        *reinterpret_cast<float4*>(lbuf + n * LR + (r0 - flushed)) = make_float4(sv[0], sv[1], sv[2], sv[3]);
+        *reinterpret_cast<float4*>(lbuf + n * LR + (r0 - flushed)) = make_float4(st[0], st[1], st[2], st[3]);
       }
     }
 #pragma unroll
@@ -1231,25 +1251,6 @@ __device__ void stream_mfma(const StepArgs& a, int pair, int start, int count, P
       acc[blk] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bhi, acc[blk], 0, 0, 0);
       acc[blk] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, blo, acc[blk], 0, 0, 0);
     }
-    if (a.vl1) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        float vf[EV];
-        if constexpr (EV == 8) {
-          unpack<BF16T>(vv[u], vf);
-        } else {
-          vf[0] = bf16_lo(vv[u].x);
-          vf[1] = bf16_hi(vv[u].x);
-          vf[2] = bf16_lo(vv[u].y);
-          vf[3] = bf16_hi(vv[u].y);
-        }
-        float n1 = 0.f;
-#pragma unroll
-        for (int e = 0; e < EV; ++e) n1 += fabsf(vf[e]);
-        n1 = row_sum<16>(n1);
-        if (n == 0 && (kFull || r0 + u < row_end)) store_wt(&vn[r0 + u], n1);
-      }
-    }
   };
   {
     // Ring of NS group buffers: while group g is processed, groups up to
@@ -1276,7 +1277,6 @@ __device__ void stream_mfma(const StepArgs& a, int pair, int start, int count, P
     Rp = R0 + 16 * nfull;  // first row of the ragged group, if any
     lstride = pm.lstride;
     lg = a.logits + (size_t)pm.slot0 * G;  // [G][lstride]
-    vn = a.vnorm + pm.slot0;                // [lstride]
     lrs = wt_rsrc(lg, a.score_none ? 0 : G * lstride * 4);
     // An unsplit pair whose wave ranges fit the buffers keeps its logits here,
     // in fp32 up to LR rows per wave, in half precision up to 2 LR.
@@ -1372,7 +1372,7 @@ void lf_step_kernel(StepArgs a) {
   } else {
     pm = *meta;
     stream_valu<T, D, G>(a, pair, it.start, min(it.start + it.count, pm.len), a.logits + (size_t)pm.slot0 * G,
-                         a.vnorm + pm.slot0, pm.lstride, s_work);
+                         pm.lstride, s_work);
   }
   const int nchunk = pm.nchunk;
   __syncthreads();
