@@ -194,8 +194,9 @@ lf_status lf_reset_sequences_budget(lf_cache* cache, int32_t n, const int32_t* s
 
 /*
  * lf_prefill_work_bytes - size of the device scratch lf_prefill_compress needs
- * (importance of every prefill position of every (sequence, KV head), plus the
- * prefill lengths and budgets).  cfg validated as in lf_init_cache.
+ * (importance and the group's logits of every prefill position of every
+ * (sequence, KV head), per-chunk statistics, plus the prefill lengths and
+ * budgets).  cfg validated as in lf_init_cache.
  */
 lf_status lf_prefill_work_bytes(const lf_config* cfg, int32_t max_prefill, size_t* bytes);
 

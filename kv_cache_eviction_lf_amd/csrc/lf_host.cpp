@@ -451,8 +451,9 @@ lf_status lf_prefill_work_bytes(const lf_config* cfg, int32_t max_prefill, size_
     return fail(LF_ERR_ARG, "max_prefill %d outside [1, %d]", max_prefill, lf::kMaxPrefill);
   const size_t pairs = (size_t)cfg->batch * cfg->n_kv_heads;
   const size_t nck = (max_prefill + lf::kPrefillChunk - 1) / lf::kPrefillChunk;
+  const size_t group = cfg->n_q_heads / cfg->n_kv_heads;
   *bytes = align_up(sizeof(float) * pairs * (size_t)max_prefill) + align_up(sizeof(float) * pairs * nck * 16) +
-           align_up(sizeof(int32_t) * 2 * cfg->batch);
+           align_up(sizeof(int32_t) * 2 * cfg->batch) + align_up(sizeof(float) * pairs * (size_t)max_prefill * group);
   g_err[0] = 0;
   return LF_OK;
 }
@@ -483,6 +484,7 @@ lf_status lf_prefill_compress(const lf_config* cfg, const int32_t* budgets, cons
   char* w = static_cast<char*>(work);
   float* stats = reinterpret_cast<float*>(w + align_up(sizeof(float) * pairs * (size_t)max_prefill));
   int32_t* dlen = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(stats) + align_up(sizeof(float) * pairs * nck * 16));
+  float* logits = reinterpret_cast<float*>(reinterpret_cast<char*>(dlen) + align_up(sizeof(int32_t) * 2 * cfg->batch));
   std::vector<int32_t> host(2 * cfg->batch);
   for (int b = 0; b < cfg->batch; ++b) {
     host[b] = prefill[b];
@@ -500,6 +502,7 @@ lf_status lf_prefill_compress(const lf_config* cfg, const int32_t* budgets, cons
   a.kept = kept;
   a.work = reinterpret_cast<float*>(w);
   a.stats = stats;
+  a.logits = logits;
   a.n_chunks = nck;
   a.n_copy = (cfg->max_budget + lf::kPrefillCopyRows - 1) / lf::kPrefillCopyRows;
   a.prefill = dlen;

@@ -97,8 +97,8 @@ int tile_rows(int dtype, int head_dim, int group);
 
 // Arguments of the one-shot prefill compression (lf_prefill.hip).  Pair p =
 // b * n_kv_heads + g; the caller's scratch holds [pairs][max_prefill]
-// importances, the per-chunk statistics, then the device copies of the prefill
-// lengths and budgets.
+// importances, the per-chunk statistics, the device copies of the prefill
+// lengths and budgets, then [pairs][max_prefill][group] logits.
 struct PrefillArgs {
   const void* q_last;  // [B][Hq][d]
   const void* k_pre;   // [B][Hkv][max_prefill][d]
@@ -108,6 +108,7 @@ struct PrefillArgs {
   int32_t* kept;       // [B][Hkv][max_budget]: kept positions, increasing
   float* work;         // [pairs][max_prefill]
   float* stats;        // [pairs][n_chunks][8][2]: per-chunk (max, sum) per head
+  float* logits;       // [pairs][max_prefill][group]: log2-domain logits of the last query
   const int32_t* prefill;  // device [B]
   const int32_t* budget;   // device [B]
   int32_t n_chunks;    // score chunks per pair (max_prefill / 512, rounded up)

@@ -10,10 +10,12 @@
 // decode step's importance.
 //
 // Four launches on the caller's stream:
-//   prefill_stats_kernel       a workgroup per (pair, 512-row chunk): per-head
-//                              maximum and normaliser of the chunk's logits.
+//   prefill_stats_kernel       a workgroup per (pair, 512-row chunk): the
+//                              chunk's logits (stored, G per position) and
+//                              their per-head maximum and normaliser.
 //   prefill_importance_kernel  same grid: the pair's statistics combined in
-//                              chunk order, then every row's importance.
+//                              chunk order, then every row's importance from
+//                              its stored logits (no second pass over K).
 //   prefill_select_kernel      a workgroup per pair: radix selection of the
 //                              threshold over 48-bit keys (importance, then the
 //                              complement of the position, so keys are unique
@@ -87,31 +89,31 @@ __device__ __forceinline__ void ml_merge(float& m, float& l, float m2, float l2)
 // batches still fill the device.
 constexpr int kChunkRows = kPrefillChunk;
 
-template <class E, int D>
+template <class E, int D, int G>
 struct ScoreCore {
   using elem = typename E::elem;
   static constexpr int EPL = E::kEpl, LPR = D / EPL, RPW = 64 / LPR;
   static constexpr int kU = 4;  // rows per lane group per iteration (loads first)
-  float q[kMaxG][EPL];
+  float q[G][EPL];
   const elem* kp;
   int c, rw;
 
   __device__ ScoreCore(const PrefillArgs& a, int pair) {
-    const int b = pair / a.n_kv_heads, g = pair - b * a.n_kv_heads, G = a.group;
+    const int b = pair / a.n_kv_heads, g = pair - b * a.n_kv_heads;
     const int lane = threadIdx.x & 63;
     c = lane % LPR;
     rw = lane / LPR;
     kp = static_cast<const elem*>(a.k_pre) + (size_t)pair * a.max_prefill * D + c * EPL;
     const elem* qb = static_cast<const elem*>(a.q_last) + ((size_t)b * a.n_q_heads + (size_t)g * G) * D + c * EPL;
 #pragma unroll
-    for (int h = 0; h < kMaxG; ++h) {
-      const uint4 r = *reinterpret_cast<const uint4*>(qb + (size_t)min(h, G - 1) * D);
+    for (int h = 0; h < G; ++h) {
+      const uint4 r = *reinterpret_cast<const uint4*>(qb + (size_t)h * D);
       unpack16(r, q[h], E{});
 #pragma unroll
       for (int e = 0; e < EPL; ++e) q[h][e] *= a.scale_log2;
     }
   }
-  // Calls f(row, s[kMaxG]) with the log2-domain logits of every row of
+  // Calls f(row, s[G]) with the log2-domain logits of every row of
   // [r0, r1) this lane group owns; rows past r1 are loaded clamped, not used.
   template <class F>
   __device__ void for_rows(int r0, int r1, F f) const {
@@ -125,9 +127,9 @@ struct ScoreCore {
       for (int u = 0; u < kU; ++u) {
         float k[EPL];
         unpack16(kr[u], k, E{});
-        float s[kMaxG];
+        float s[G];
 #pragma unroll
-        for (int h = 0; h < kMaxG; ++h) {
+        for (int h = 0; h < G; ++h) {
           float p = 0.f;
 #pragma unroll
           for (int e = 0; e < EPL; ++e) p = fmaf(q[h][e], k[e], p);
@@ -139,28 +141,43 @@ struct ScoreCore {
   }
 };
 
-// Pass 1: per chunk and head, the maximum and normaliser (log2 domain).
-template <class E, int D>
+// Pass 1: the chunk's logits, stored [position][G] (lane c of a row lineage
+// stores head c, so a wave's stores are contiguous), and per head their
+// maximum and normaliser (log2 domain).
+template <class E, int D, int G>
 __global__ __launch_bounds__(kPT) void prefill_stats_kernel(PrefillArgs a) {
   const int pair = blockIdx.x / a.n_chunks, chunk = blockIdx.x - pair * a.n_chunks;
   const int b = pair / a.n_kv_heads;
   const int P = a.prefill[b];
   const int r0 = chunk * kChunkRows, r1 = min(P, r0 + kChunkRows);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  float m[kMaxG], l[kMaxG];
+  float m[G], l[G];
 #pragma unroll
-  for (int h = 0; h < kMaxG; ++h) {
+  for (int h = 0; h < G; ++h) {
     m[h] = -INFINITY;
     l[h] = 0.f;
   }
-  const ScoreCore<E, D> core(a, pair);
-  core.for_rows(r0, r1, [&](int, const float(&s)[kMaxG]) {
+  const ScoreCore<E, D, G> core(a, pair);
+  float* lg = a.logits + (size_t)pair * a.max_prefill * G;
+  core.for_rows(r0, r1, [&](int row, const float(&s)[G]) {
+    // Running (max, sum) per head: the sum is rescaled only when the max
+    // moves (the hardware exp2; all lanes of a row lineage agree).
 #pragma unroll
-    for (int h = 0; h < kMaxG; ++h) ml_merge(m[h], l[h], s[h], 1.f);
+    for (int h = 0; h < G; ++h) {
+      if (s[h] > m[h]) {
+        l[h] *= __builtin_amdgcn_exp2f(m[h] - s[h]);
+        m[h] = s[h];
+      }
+      l[h] += __builtin_amdgcn_exp2f(s[h] - m[h]);
+    }
+    float mine = s[0];
+#pragma unroll
+    for (int h = 1; h < G; ++h) mine = core.c == h ? s[h] : mine;
+    if (core.c < G) lg[(size_t)row * G + core.c] = mine;
   });
   __shared__ float s_m[kPW][kMaxG], s_l[kPW][kMaxG];
 #pragma unroll
-  for (int h = 0; h < kMaxG; ++h) {
+  for (int h = 0; h < G; ++h) {
     float mm = core.c == 0 ? m[h] : -INFINITY, ll = core.c == 0 ? l[h] : 0.f;  // one lane per row lineage
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) ml_merge(mm, ll, __shfl_xor(mm, o), __shfl_xor(ll, o));
@@ -170,7 +187,7 @@ __global__ __launch_bounds__(kPT) void prefill_stats_kernel(PrefillArgs a) {
     }
   }
   __syncthreads();
-  if (threadIdx.x < kMaxG) {
+  if (threadIdx.x < G) {
     const int h = threadIdx.x;
     float mm = s_m[0][h], ll = s_l[0][h];
 #pragma unroll
@@ -182,33 +199,33 @@ __global__ __launch_bounds__(kPT) void prefill_stats_kernel(PrefillArgs a) {
 }
 
 // Pass 2: the pair's chunk statistics combined in chunk order (the same bits
-// in every chunk), then the importance of the chunk's rows.
-template <class E, int D>
+// in every chunk), then the importance of the chunk's rows from their stored
+// logits, one row per thread.
+template <class E, int D, int G>
 __global__ __launch_bounds__(kPT) void prefill_importance_kernel(PrefillArgs a) {
   const int pair = blockIdx.x / a.n_chunks, chunk = blockIdx.x - pair * a.n_chunks;
   const int b = pair / a.n_kv_heads;
-  const int P = a.prefill[b], G = a.group;
+  const int P = a.prefill[b];
   const int r0 = chunk * kChunkRows, r1 = min(P, r0 + kChunkRows);
   if (r0 >= r1) return;
   const int nck = (P + kChunkRows - 1) / kChunkRows;
-  float M[kMaxG], invL[kMaxG];
+  float M[G], invL[G];
   const float* st = a.stats + (size_t)pair * a.n_chunks * kMaxG * 2;
 #pragma unroll
-  for (int h = 0; h < kMaxG; ++h) {
+  for (int h = 0; h < G; ++h) {
     float mm = -INFINITY, ll = 0.f;
     for (int k = 0; k < nck; ++k) ml_merge(mm, ll, st[k * kMaxG * 2 + 2 * h], st[k * kMaxG * 2 + 2 * h + 1]);
     M[h] = mm;
     invL[h] = 1.0f / ll;
   }
   float* imp = a.work + (size_t)pair * a.max_prefill;
-  const ScoreCore<E, D> core(a, pair);
-  core.for_rows(r0, r1, [&](int row, const float(&s)[kMaxG]) {
+  const float* lg = a.logits + (size_t)pair * a.max_prefill * G;
+  for (int row = r0 + (int)threadIdx.x; row < r1; row += kPT) {
     float x = 0.f;
 #pragma unroll
-    for (int h = 0; h < kMaxG; ++h)
-      if (h < G) x = fmaf(exp2f(s[h] - M[h]), invL[h], x);
-    if (core.c == 0) imp[row] = x;
-  });
+    for (int h = 0; h < G; ++h) x = fmaf(__builtin_amdgcn_exp2f(lg[(size_t)row * G + h] - M[h]), invL[h], x);
+    imp[row] = x;
+  }
 }
 
 // Key of a middle position: importance bits (non-negative floats order as
@@ -335,10 +352,19 @@ __global__ __launch_bounds__(kPT) void prefill_copy_kernel(PrefillArgs a) {
   }
 }
 
+template <class E, int D, int G>
+void launch_scores(const PrefillArgs& a, int n_pairs, hipStream_t s) {
+  hipLaunchKernelGGL((prefill_stats_kernel<E, D, G>), dim3(n_pairs * a.n_chunks), dim3(kPT), 0, s, a);
+  hipLaunchKernelGGL((prefill_importance_kernel<E, D, G>), dim3(n_pairs * a.n_chunks), dim3(kPT), 0, s, a);
+}
+
 template <class E, int D>
 void launch_prefill(const PrefillArgs& a, int n_pairs, hipStream_t s) {
-  hipLaunchKernelGGL((prefill_stats_kernel<E, D>), dim3(n_pairs * a.n_chunks), dim3(kPT), 0, s, a);
-  hipLaunchKernelGGL((prefill_importance_kernel<E, D>), dim3(n_pairs * a.n_chunks), dim3(kPT), 0, s, a);
+  using Fn = void (*)(const PrefillArgs&, int, hipStream_t);
+  constexpr Fn kScores[kMaxG] = {launch_scores<E, D, 1>, launch_scores<E, D, 2>, launch_scores<E, D, 3>,
+                                 launch_scores<E, D, 4>, launch_scores<E, D, 5>, launch_scores<E, D, 6>,
+                                 launch_scores<E, D, 7>, launch_scores<E, D, 8>};
+  kScores[a.group - 1](a, n_pairs, s);
   hipLaunchKernelGGL((prefill_select_kernel<E, D>), dim3(n_pairs), dim3(kPT), 0, s, a);
   hipLaunchKernelGGL((prefill_copy_kernel<E, D>), dim3(n_pairs * a.n_copy), dim3(kPT), 0, s, a);
 }
