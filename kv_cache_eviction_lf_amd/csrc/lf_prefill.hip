@@ -78,6 +78,13 @@ __device__ __forceinline__ float row_total(float x) {
   return x;
 }
 
+// 16-byte non-temporal load (data read once).
+__device__ __forceinline__ uint4 load_once(const uint4* p) {
+  typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+  const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(x[0], x[1], x[2], x[3]);
+}
+
 // (max, sum of exp2(x - max)) pairs combined.
 __device__ __forceinline__ void ml_merge(float& m, float& l, float m2, float l2) {
   const float mn = fmaxf(m, m2);
@@ -338,17 +345,38 @@ __global__ __launch_bounds__(kPT) void prefill_copy_kernel(PrefillArgs a) {
   const int32_t* kept = a.kept + (size_t)pair * a.max_budget;
   constexpr int kPieces = D * sizeof(elem) / 16;
   constexpr int kRowsPerWave = 64 / kPieces;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int sub = lane / kPieces, piece = lane % kPieces;
   const uint4* ksrc = reinterpret_cast<const uint4*>(static_cast<const elem*>(a.k_pre) + (size_t)pair * a.max_prefill * D);
   const uint4* vsrc = reinterpret_cast<const uint4*>(static_cast<const elem*>(a.v_pre) + (size_t)pair * a.max_prefill * D);
   uint4* kdst = reinterpret_cast<uint4*>(static_cast<elem*>(a.k_cache) + (size_t)pair * a.max_budget * D);
   uint4* vdst = reinterpret_cast<uint4*>(static_cast<elem*>(a.v_cache) + (size_t)pair * a.max_budget * D);
-  for (int r = r0 + wave * kRowsPerWave + sub; r < r1; r += kPW * kRowsPerWave) {
-    const int pos = kept[r];
-    if (pos < 0 || pos >= P) continue;  // not reached: kept[0, nkeep) holds positions below P
-    kdst[(size_t)r * kPieces + piece] = ksrc[(size_t)pos * kPieces + piece];
-    vdst[(size_t)r * kPieces + piece] = vsrc[(size_t)pos * kPieces + piece];
+  // The workgroup's kept positions first (one load each), then kU rows per
+  // lane group with all their loads issued before any store; source rows
+  // are read once, so the loads are non-temporal.
+  __shared__ int s_pos[kCopyRows];
+  const int n = r1 - r0;
+  if (n <= 0) return;
+  for (int i = tid; i < kCopyRows; i += kPT) s_pos[i] = i < n ? kept[r0 + i] : 0;
+  __syncthreads();
+  constexpr int kU = 4;
+  for (int rb = wave * kRowsPerWave * kU; rb < n; rb += kPW * kRowsPerWave * kU) {
+    uint4 kx[kU], vx[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i = min(rb + u * kRowsPerWave + sub, n - 1);
+      const int pos = min(max(s_pos[i], 0), P - 1);  // kept[0, nkeep) holds positions below P
+      kx[u] = load_once(ksrc + (size_t)pos * kPieces + piece);
+      vx[u] = load_once(vsrc + (size_t)pos * kPieces + piece);
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i = rb + u * kRowsPerWave + sub;
+      if (i < n) {
+        kdst[(size_t)(r0 + i) * kPieces + piece] = kx[u];
+        vdst[(size_t)(r0 + i) * kPieces + piece] = vx[u];
+      }
+    }
   }
 }
 
