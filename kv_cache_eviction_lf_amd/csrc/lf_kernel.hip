@@ -421,8 +421,11 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
   constexpr int kCB = G <= 4 ? 8 : 4;                       // chunk partials loaded per batch
   constexpr int kVec = D * sizeof(elem) / 16;               // 16-byte pieces of one K/V row
   // float4 logit cells per head preloaded (more when the register budget is
-  // not sized for 3 waves per SIMD)
-  constexpr int kPre = Shape<T, D, G>::kMinWavesPerSimd == 1 ? 32 / G : (G <= 2 ? 8 : 16 / G);
+  // sized for one wave per SIMD).  Every cell past the budget is a wasted
+  // load in the tail's first round trip: 2048 slots for G = 3, 4 and 1024
+  // for G >= 5 cover the split shapes measured (B8 budget 2048 G 4: 18.43 ->
+  // 18.26 us against twice as many; B16 budget 1024 G 7: 14.80 -> 14.62 us).
+  constexpr int kPre = Shape<T, D, G>::kMinWavesPerSimd == 1 ? 32 / G : (G <= 2 ? 8 : 8 / G);
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
   PairMeta* meta = a.meta + pair;
   const int b = pair / a.n_kv_heads, g = pair - b * a.n_kv_heads;
