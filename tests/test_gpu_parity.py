@@ -198,6 +198,14 @@ def test_half_resident_equal_importances():
     cache.close()
 
 
+@pytest.mark.parametrize("score", ["attn", "vl1"])
+def test_largest_budget(score):
+    # the largest budget the protected-slot bitmap allows (65536 slots), one
+    # sequence: 64 chunks per pair, the tail's remainder loop over most logits
+    w = _small(budget_lo=65536, budget_hi=65536, batch=1, sink=4, recent=64)
+    parity_run(w, 6, score=score, dbg_every=3, tag=f" max budget {score}")
+
+
 def test_vl1_on_ragged_small():
     w = _small(budget_lo=150, budget_hi=400, prefill="ragged", batch=4, n_q_heads=14, n_kv_heads=2)
     parity_run(w, 100, score="vl1", dbg_every=9)
