@@ -205,6 +205,95 @@ __global__ __launch_bounds__(kPT) void prefill_stats_kernel(PrefillArgs a) {
   }
 }
 
+// Pass 1 for bf16 on the matrix cores: each wave takes 128 consecutive rows of
+// the chunk in groups of 16; one v_mfma_f32_16x16x32_bf16 per 32 dimensions
+// multiplies the group's 16 key rows by the group's query heads (columns,
+// heads past G unused), so lane 16 j + n holds the logits of rows 4 j .. 4 j +
+// 3 of the group for head n.  Each lane keeps the running (max, sum) of its
+// head over its rows; lanes of one head are combined at the end.  Same
+// results as the vector-ALU pass up to the order of the dot products' sums.
+template <int D, int G>
+__global__ __launch_bounds__(kPT) void prefill_stats_mfma_kernel(PrefillArgs a) {
+  typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
+  constexpr int KB = D / 32;
+  constexpr int kWaveRows = kChunkRows / kPW;  // 128
+  const int pair = blockIdx.x / a.n_chunks, chunk = blockIdx.x - pair * a.n_chunks;
+  const int b = pair / a.n_kv_heads, g = pair - b * a.n_kv_heads;
+  const int P = a.prefill[b];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, n = lane & 15, j = lane >> 4;
+  const int r0 = chunk * kChunkRows + wave * kWaveRows;
+  const int r1 = min(P, r0 + kWaveRows);  // this wave's rows [r0, r1)
+  uint4 qb[KB];
+  {
+    const int hq = n < G ? n : 0;  // columns past G load head 0 and are not used
+    const uint16_t* qh = static_cast<const uint16_t*>(a.q_last) + ((size_t)b * a.n_q_heads + (size_t)g * G + hq) * D + 8 * j;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) qb[kb] = *reinterpret_cast<const uint4*>(qh + 32 * kb);
+  }
+  const uint16_t* kp = static_cast<const uint16_t*>(a.k_pre) + (size_t)pair * a.max_prefill * D + 8 * j;
+  // Logit stores go through a buffer resource over the pair's P * G logits;
+  // lanes without a logit to store (heads past G, rows past the wave's range)
+  // aim past it and the hardware drops the store, so no store (and no load
+  // below) sits under a branch and the loop's waits stay exact.
+  const auto lrs = __builtin_amdgcn_make_buffer_rsrc(a.logits + (size_t)pair * a.max_prefill * G, (short)0, P * G * 4,
+                                                     0x00020000);
+  float m = -INFINITY, l = 0.f;
+  const int last = max(r1 - 1, 0);
+  auto load = [&](int R, uint4(&kk)[KB]) {  // rows clamped to the wave's last valid row
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+      kk[kb] = load_once(reinterpret_cast<const uint4*>(kp + (size_t)min(R + n, last) * D + 32 * kb));
+  };
+  uint4 cur[KB], nxt[KB];
+  load(r0, cur);
+  for (int R = r0; R < r1; R += 16) {
+    load(R + 16, nxt);
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, cur[kb]),
+                                                    __builtin_bit_cast(bf16x8_t, qb[kb]), acc, 0, 0, 0);
+    float sv[4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = R + 4 * j + i;
+      sv[i] = row < r1 ? acc[i] * a.scale_log2 : -INFINITY;
+      mx = fmaxf(mx, sv[i]);
+      const int off = n < G && row < r1 ? (row * G + n) * 4 : 0x7FFFFFF0;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sv[i]), lrs, off, 0, 0);
+    }
+    if (mx > m) {
+      l *= __builtin_amdgcn_exp2f(m - mx);
+      m = mx;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) l += sv[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[i] - m);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) cur[kb] = nxt[kb];
+  }
+  // Combine the 4 lane groups of each head (lanes n, n + 16, n + 32, n + 48),
+  // then the waves.
+  ml_merge(m, l, __shfl_xor(m, 16), __shfl_xor(l, 16));
+  ml_merge(m, l, __shfl_xor(m, 32), __shfl_xor(l, 32));
+  __shared__ float s_m[kPW][16], s_l[kPW][16];
+  if (lane < 16) {
+    s_m[wave][lane] = m;
+    s_l[wave][lane] = l;
+  }
+  __syncthreads();
+  if (threadIdx.x < G) {
+    const int h = threadIdx.x;
+    float mm = s_m[0][h], ll = s_l[0][h];
+#pragma unroll
+    for (int w = 1; w < kPW; ++w) ml_merge(mm, ll, s_m[w][h], s_l[w][h]);
+    float* st = a.stats + ((size_t)pair * a.n_chunks + chunk) * kMaxG * 2;
+    st[2 * h] = mm;
+    st[2 * h + 1] = ll;
+  }
+}
+
 // Pass 2: the pair's chunk statistics combined in chunk order (the same bits
 // in every chunk), then the importance of the chunk's rows from their stored
 // logits, one row per thread.
@@ -351,27 +440,34 @@ __global__ __launch_bounds__(kPT) void prefill_copy_kernel(PrefillArgs a) {
   const uint4* vsrc = reinterpret_cast<const uint4*>(static_cast<const elem*>(a.v_pre) + (size_t)pair * a.max_prefill * D);
   uint4* kdst = reinterpret_cast<uint4*>(static_cast<elem*>(a.k_cache) + (size_t)pair * a.max_budget * D);
   uint4* vdst = reinterpret_cast<uint4*>(static_cast<elem*>(a.v_cache) + (size_t)pair * a.max_budget * D);
-  // The workgroup's kept positions first (one load each), then kU rows per
-  // lane group with all their loads issued before any store; source rows
-  // are read once, so the loads are non-temporal.
-  __shared__ int s_pos[kCopyRows];
+  // Each lane's kept positions first (independent loads, one round trip),
+  // then kU rows per lane group per pass with all their loads issued before
+  // any store; source rows are read once, so the loads are non-temporal.
   const int n = r1 - r0;
   if (n <= 0) return;
-  for (int i = tid; i < kCopyRows; i += kPT) s_pos[i] = i < n ? kept[r0 + i] : 0;
-  __syncthreads();
   constexpr int kU = 4;
-  for (int rb = wave * kRowsPerWave * kU; rb < n; rb += kPW * kRowsPerWave * kU) {
+  constexpr int kStep = kPW * kRowsPerWave * kU;  // rows per pass of the workgroup
+  constexpr int kPasses = (kCopyRows + kStep - 1) / kStep;
+  int pos[kPasses][kU];
+#pragma unroll
+  for (int ps = 0; ps < kPasses; ++ps)
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i = min(ps * kStep + wave * kRowsPerWave * kU + u * kRowsPerWave + sub, n - 1);
+      pos[ps][u] = min(max(kept[r0 + i], 0), P - 1);  // kept[0, nkeep) holds positions below P
+    }
+#pragma unroll
+  for (int ps = 0; ps < kPasses; ++ps) {
+    if (ps * kStep >= n) break;
     uint4 kx[kU], vx[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const int i = min(rb + u * kRowsPerWave + sub, n - 1);
-      const int pos = min(max(s_pos[i], 0), P - 1);  // kept[0, nkeep) holds positions below P
-      kx[u] = load_once(ksrc + (size_t)pos * kPieces + piece);
-      vx[u] = load_once(vsrc + (size_t)pos * kPieces + piece);
+      kx[u] = load_once(ksrc + (size_t)pos[ps][u] * kPieces + piece);
+      vx[u] = load_once(vsrc + (size_t)pos[ps][u] * kPieces + piece);
     }
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const int i = rb + u * kRowsPerWave + sub;
+      const int i = ps * kStep + wave * kRowsPerWave * kU + u * kRowsPerWave + sub;
       if (i < n) {
         kdst[(size_t)(r0 + i) * kPieces + piece] = kx[u];
         vdst[(size_t)(r0 + i) * kPieces + piece] = vx[u];
@@ -382,7 +478,10 @@ __global__ __launch_bounds__(kPT) void prefill_copy_kernel(PrefillArgs a) {
 
 template <class E, int D, int G>
 void launch_scores(const PrefillArgs& a, int n_pairs, hipStream_t s) {
-  hipLaunchKernelGGL((prefill_stats_kernel<E, D, G>), dim3(n_pairs * a.n_chunks), dim3(kPT), 0, s, a);
+  if constexpr (E::kEpl == 8)
+    hipLaunchKernelGGL((prefill_stats_mfma_kernel<D, G>), dim3(n_pairs * a.n_chunks), dim3(kPT), 0, s, a);
+  else
+    hipLaunchKernelGGL((prefill_stats_kernel<E, D, G>), dim3(n_pairs * a.n_chunks), dim3(kPT), 0, s, a);
   hipLaunchKernelGGL((prefill_importance_kernel<E, D, G>), dim3(n_pairs * a.n_chunks), dim3(kPT), 0, s, a);
 }
 
