@@ -226,7 +226,7 @@ __device__ __forceinline__ uint2 load_nt(const uint2* p) {
   return make_uint2(x[0], x[1]);
 }
 
-// Data one workgroup hands to another in the same launch (logits, |v| norms,
+// Data one workgroup hands to another in the same launch (logits and the
 // chunk partials of a split pair) moves only through device-scope stores and
 // loads: relaxed agent-scope atomics, or buffer stores and loads with the same
 // "sc1" cache policy (on gfx950: written through the non-coherent per-XCD L2
