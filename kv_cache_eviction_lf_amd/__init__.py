@@ -18,10 +18,12 @@ from ._lib import (
     lf_init_cache,
     lf_last_error,
     lf_probe_copy,
+    lf_probe_empty,
     lf_prefill_compress,
     lf_prefill_work_bytes,
     lf_probe_read,
     lf_reset_sequences,
+    lf_reset_sequences_budget,
     lf_state_bytes,
     load_library,
     make_config,
@@ -53,10 +55,12 @@ __all__ = [
     "lf_init_cache",
     "lf_last_error",
     "lf_probe_copy",
+    "lf_probe_empty",
     "lf_prefill_compress",
     "lf_prefill_work_bytes",
     "lf_probe_read",
     "lf_reset_sequences",
+    "lf_reset_sequences_budget",
     "lf_state_bytes",
     "load_library",
     "make_config",
