@@ -51,7 +51,7 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="launch step by step instead of replaying HIP graphs")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--probe", action="store_true", help="also time the HBM read/copy probes")
+    ap.add_argument("--no-probe", action="store_true", help="skip the HBM read/copy probes and the launch floor")
     return ap.parse_args()
 
 
@@ -79,15 +79,25 @@ def profiled_traffic(workload: str):
     return rec.get("traffic_bytes_per_launch") if rec.get("kernel_source_sha256") == sha else None
 
 
-def cpu_baseline(w, seconds: float, score: str = "attn") -> dict:
-    """Time the float64 oracle as it stands, single-threaded, on the same
-    workload (full batch of the first layer) for about `seconds`."""
+def host_cores() -> int:
+    """CPU cores this process may run on (the box's share, not the machine's)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(w, seconds: float, score: str = "attn", threads: int = 0) -> dict:
+    """Time the float64 oracle as it stands on the same workload (full batch of
+    the first layer) for about `seconds`, with BLAS allowed `threads` threads
+    (0 = every host core of this process)."""
     from threadpoolctl import threadpool_limits
 
     from oracle import SCORE_ATTN, SCORE_NONE, SCORE_VL1, OracleCache
     from workloads import budgets, initial_cache, step_inputs
 
-    with threadpool_limits(1):
+    threads = threads or host_cores()
+    with threadpool_limits(threads):
         ks, vs, ps, ts = initial_cache(w)
         oc = OracleCache(ks, vs, ps, ts, budgets(w), w.n_q_heads, w.sink, w.recent,
                          score={"vl1": SCORE_VL1, "none": SCORE_NONE}.get(score, SCORE_ATTN))
@@ -100,9 +110,10 @@ def cpu_baseline(w, seconds: float, score: str = "attn") -> dict:
             el = time.perf_counter() - t0
             if el >= seconds and n >= 2:
                 break
-    return {"value": n / el, "unit": "steps/s", "cores": 1, "kind": "oracle",
+    return {"value": n / el, "unit": "steps/s", "cores": threads, "kind": "oracle",
             "sample": f"{w.name} full batch ({w.batch} sequences), {n} float64 oracle steps after 1 warm-up, "
-                      f"{el:.1f} s, numpy with BLAS limited to 1 thread"}
+                      f"{el:.1f} s, numpy with BLAS allowed {threads} thread{'s' if threads > 1 else ''} "
+                      f"of the {host_cores()} host cores"}
 
 
 def bench_compress(args, w, torch, dev):
@@ -159,7 +170,8 @@ def bench_compress(args, w, torch, dev):
                    "budget": [int(bud.min()), int(bud.max())], "sink": w.sink, "recent": w.recent},
         "kv_GBps": round(gbps, 1), "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "bytes_per_call": nbytes,
-        "note": "the score pass reads the prefill K rows twice (maxima, then importance); bytes count them once",
+        "note": "bytes: every prefill K row read once (the statistics pass stores the logits the importance "
+                "pass reads) plus the kept K and V rows read and written",
     }), flush=True)
 
 
@@ -272,7 +284,7 @@ def main():
         c.close()
 
     probe = None
-    if args.probe:
+    if not args.no_probe:
         n = 1 << 30
         src = torch.empty(n, dtype=torch.uint8, device=dev)
         dst = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -315,7 +327,10 @@ def main():
         res["launch_floor_us"] = round(a.elapsed_time(b) * 1e3 / (4 * nodes), 2)
         probe = res
 
-    base = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_seconds, args.score)
+    base = base1 = None
+    if not args.no_cpu_baseline:
+        base = cpu_baseline(w, args.cpu_seconds, args.score)
+        base1 = cpu_baseline(w, args.cpu_seconds / 2, args.score, threads=1) if host_cores() > 1 else base
     # counters were taken on the default step of the named workload only
     profiled = profiled_traffic(w.name) if args.score == "attn" and not args.budget else None
     line = {
@@ -360,6 +375,7 @@ def main():
             "kernel": "lf_step_kernel",
         },
         "cpu_baseline": base,
+        "cpu_baseline_1thread": base1,
         "wall_s_timed": round(wall, 4),
     }
     if probe:

@@ -1410,6 +1410,10 @@ void lf_step_kernel(StepArgs a) {
   }
 
   if (nchunk == 1) {
+    // Logits this pair wrote to the workspace are read back by other waves of
+    // this workgroup with device-scope loads: every wave drains its stores
+    // before the barrier, as a split pair's chunks do before the ticket.
+    if (lmode == kLogitsOut) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // merged partial complete, bitmap cleared
     set_protect_bits<T, D, G>(a, pair, pm.budget, s_bits, s_pre);
     __syncthreads();

@@ -6,11 +6,12 @@ from .longflow_oracle import (
     SCORE_ATTN,
     SCORE_NONE,
     SCORE_VL1,
+    TIE_TOLERANCE,
     OracleCache,
     StepDecision,
     attention_step,
     prefill_keep,
 )
 
-__all__ = ["SCORE_ATTN", "SCORE_NONE", "SCORE_VL1", "OracleCache", "StepDecision", "attention_step",
+__all__ = ["SCORE_ATTN", "SCORE_NONE", "SCORE_VL1", "TIE_TOLERANCE", "OracleCache", "StepDecision", "attention_step",
            "prefill_keep"]

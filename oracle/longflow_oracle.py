@@ -63,6 +63,8 @@ SCORE_VL1 = 1
 # incoming token is appended while there is room; once the cache is full it is
 # attended but not stored (a reading: the pages' full cache never fills).
 SCORE_NONE = 2
+# Importances closer than this are a tie: either slot is a correct eviction.
+TIE_TOLERANCE = 1e-6
 
 
 def attention_step(keys: np.ndarray, values: np.ndarray, q_heads: np.ndarray, scale: float):
@@ -89,6 +91,24 @@ class StepDecision:
     gap: np.ndarray  # float64 [B][Hkv]: 2nd lowest - lowest eligible score (inf if < 2)
     alpha_new: np.ndarray  # float64 [B][Hq]: weight of the incoming token
     lse: np.ndarray  # float64 [B][Hq]
+
+    def accepts(self, b: int, g: int, slot: int, tol: float = TIE_TOLERANCE) -> bool:
+        """Whether ``slot`` is a correct choice for (sequence b, KV head g).
+
+        The oracle's own slot always is.  Where several slots are correct
+        answers, namely when the two lowest eligible importances are closer
+        than ``tol``, another slot is also accepted if it is eligible and its
+        importance is within ``tol`` of the lowest one.  Anything else (an
+        appended token in the wrong place, a protected slot, a clearly larger
+        importance) is rejected."""
+        want = int(self.evict[b, g])
+        slot = int(slot)
+        if slot == want:
+            return True
+        if want < 0 or slot < 0 or not self.gap[b, g] < tol:
+            return False
+        el, sc = self.eligible[b][g], self.scores[b][g]
+        return slot < el.shape[0] and bool(el[slot]) and sc[slot] - sc[want] < tol
 
 
 class OracleCache:

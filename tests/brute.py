@@ -71,5 +71,39 @@ class BruteCache:
             self.t[b] = t + 1
         return outs, slots, evs
 
+    def gaps(self, q, k_new, v_new):
+        """Per (b, g): second-lowest minus lowest importance over the eligible
+        cached entries (inf with fewer than two), found by scanning; no state change."""
+        out = []
+        for b in range(self.B):
+            t = self.t[b]
+            row = []
+            for g in range(self.Hkv):
+                ent = self.entries[b][g]
+                keys = [e[1] for e in ent] + [list(map(float, k_new[b][g]))]
+                imp = [0.0] * len(ent)
+                for j in range(self.G):
+                    qh = list(map(float, q[b][g * self.G + j]))
+                    logits = [self.scale * sum(a * c for a, c in zip(qh, kk)) for kk in keys]
+                    top = max(logits)
+                    w = [math.exp(x - top) for x in logits]
+                    z = sum(w)
+                    for i in range(len(ent)):
+                        imp[i] += w[i] / z
+                if self.vl1:
+                    imp = [imp[i] * sum(abs(x) for x in ent[i][2]) for i in range(len(ent))]
+                lowest = second = math.inf
+                for i in range(len(ent)):
+                    p = ent[i][0]
+                    if p < self.sink or p >= t - self.recent:
+                        continue
+                    if imp[i] < lowest:
+                        lowest, second = imp[i], lowest
+                    elif imp[i] < second:
+                        second = imp[i]
+                row.append(second - lowest if second < math.inf else math.inf)
+            out.append(row)
+        return out
+
     def positions(self, b, g):
         return [e[0] for e in self.entries[b][g]]

@@ -16,11 +16,11 @@ import numpy as np
 import torch
 
 from kv_cache_eviction_lf_amd import LongFlowCache
-from oracle import SCORE_ATTN, SCORE_NONE, SCORE_VL1, OracleCache
+from oracle import SCORE_ATTN, SCORE_NONE, SCORE_VL1, TIE_TOLERANCE, OracleCache
 from workloads import Workload, initial_sequence
 from workloads.device import device_cache, device_step
 
-TIE_EXEMPTION = 1e-6
+TIE_EXEMPTION = TIE_TOLERANCE
 
 
 def out_tolerance(w: Workload) -> float:
@@ -94,11 +94,8 @@ def parity_run(w: Workload, steps: int, check=None, score: str = "attn", chunk_s
                 rep.compared_slots += 1
                 if ge == oe:
                     continue
-                gap = dec.gap[j, g]
-                ok = (oe >= 0 and ge >= 0 and gap < TIE_EXEMPTION and dec.eligible[j][g, ge]
-                      and dec.scores[j][g, ge] - dec.scores[j][g, oe] < TIE_EXEMPTION)
-                assert ok, (f"step {s} seq {check[j]} kv {g}: GPU evicted {ge}, oracle {oe} "
-                            f"(gap {gap:.3e})")
+                assert dec.accepts(j, g, ge), (f"step {s} seq {check[j]} kv {g}: GPU evicted {ge}, "
+                                               f"oracle {oe} (gap {dec.gap[j, g]:.3e})")
                 rep.exempt_ties += 1
                 if free_running:
                     rep.diverged_at = s

@@ -9,7 +9,6 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_harness import TIE_EXEMPTION
 from oracle import OracleCache
 from workloads import Workload, initial_sequence
 from workloads.device import device_cache, device_step
@@ -25,9 +24,7 @@ def _check_step(s, out, ev, dec, tol):
     for b in range(ev_h.shape[0]):
         for g in range(ev_h.shape[1]):
             if ev_h[b, g] != dec.evict[b, g]:
-                ok = (dec.evict[b, g] >= 0 and ev_h[b, g] >= 0 and dec.gap[b, g] < TIE_EXEMPTION
-                      and dec.eligible[b][g, ev_h[b, g]])
-                assert ok, f"step {s} seq {b} kv {g}: GPU {ev_h[b, g]}, oracle {dec.evict[b, g]}"
+                assert dec.accepts(b, g, ev_h[b, g]), f"step {s} seq {b} kv {g}: GPU {ev_h[b, g]}, oracle {dec.evict[b, g]}"
                 slots[b, g] = ev_h[b, g]
     return slots
 

@@ -40,8 +40,10 @@ def test_tiny_f32_all_steps_lockstep():
 
 
 def test_tiny_f32_free_running():
+    # the oracle on its own state; the comparison may only stop at an exempt
+    # near-tie (a mismatch anywhere else fails inside the harness)
     rep = parity_run(get_workload("tiny_f32"), 512, free_running=True)
-    assert rep.steps >= 256, rep
+    assert rep.steps == 512 or (rep.diverged_at == rep.steps - 1 and rep.exempt_ties == 1), rep
 
 
 def test_tiny_f32_vl1_mode():
@@ -168,6 +170,17 @@ def test_half_resident_pairs(kw, score, chunk):
     # them and scores the possible minima exactly from their key rows
     w = _small(**kw)
     parity_run(w, 30, score=score, chunk_slots=chunk, dbg_every=6, tag=f" half {score}")
+
+
+@pytest.mark.parametrize("kw,chunk", [
+    (dict(budget_lo=5000, budget_hi=5000, batch=2), 8192),                     # bf16 G = 4, wave ranges > 2 buffers
+    (dict(budget_lo=300, budget_hi=300, batch=2, dtype="f32", n_q_heads=10, n_kv_heads=2), 320),  # fp32 G = 5
+])
+def test_unsplit_pairs_logits_through_memory(kw, chunk):
+    # one chunk per pair whose logits do not stay on chip: the streaming waves
+    # write them to the workspace and the same workgroup's tail reads them back
+    w = _small(**kw)
+    parity_run(w, 40, chunk_slots=chunk, dbg_every=5, tag=f" unsplit-out {kw.get('dtype', 'bf16')}")
 
 
 def test_half_resident_equal_importances():

@@ -95,7 +95,7 @@ def test_prefill_compress_matches_oracle(case):
         for b in range(w.batch):
             for g in range(w.n_kv_heads):
                 if ev_h[b, g] != dec.evict[b, g]:
-                    assert dec.gap[b, g] < TIE and dec.eligible[b][g, ev_h[b, g]], (s, b, g)
+                    assert dec.accepts(b, g, ev_h[b, g]), (s, b, g, int(ev_h[b, g]), int(dec.evict[b, g]))
                     slots[b, g] = ev_h[b, g]
         oc.commit(slots, ks, vs)
     cache.close()

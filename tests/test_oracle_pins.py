@@ -57,6 +57,8 @@ def test_hand_worked_example(score):
         np.testing.assert_allclose(dec.scores[0][0], [_frac(x) for x in st_[key + "_scores"]], rtol=0, atol=1e-14)
         assert dec.eligible[0][0].tolist() == st_["eligible"]
         assert int(dec.evict[0, 0]) == st_[key + "_evict"]
+        # the tie exemption's measure: second-lowest minus lowest eligible score
+        assert abs(float(dec.gap[0, 0]) - _frac(st_[key + "_gap"])) < 1e-14
         oc.commit(dec.slot, kn, vn)
         if "positions_after" in st_:
             assert oc.pos[0][0].tolist() == st_["positions_after"]
@@ -142,6 +144,9 @@ def test_uniform_keys_closed_form(score):
         mult = d if score == SCORE_VL1 else 1
         np.testing.assert_allclose(dec.scores[0][g], np.full(n, G * mult / (n + 1)), rtol=1e-14)
         assert dec.evict[0, g] == sink  # all eligible scores tie: lowest eligible slot
+        assert dec.gap[0, g] == 0.0  # several slots are correct answers
+        assert all(dec.accepts(0, g, e) for e in range(sink, n - recent))
+        assert not dec.accepts(0, g, sink - 1) and not dec.accepts(0, g, n - recent)  # protected slots
     np.testing.assert_allclose(dec.alpha_new[0], 1.0 / (n + 1), rtol=1e-14)
 
 
@@ -175,6 +180,50 @@ def test_g1_integer_logits_argmin_is_logit_argmin():
         cand = np.arange(sink, n - recent)
         want = cand[np.argmin(logits[cand])]
         assert dec.evict[0, 0] == want, trial
+
+
+def test_gap_counts_eligible_slots_only():
+    """G = 1, integer logits, scale 1: slot importances are exp(logit) / Z, so
+    their order and gaps are fixed by hand.  A protected slot holding the second
+    lowest importance does not enter the gap; one eligible slot gives an
+    infinite gap; and the acceptance rule takes only the oracle's slot."""
+    d, sink, recent = 1, 1, 1
+    # slots 0..4 hold positions 0..4; t = 5: slot 0 is the sink, slot 4 the recent window
+    logits = np.array([0.0, 1.0, 3.0, 5.0, 2.0])  # eligible slots 1, 2, 3; slot 4 (protected) is 2nd lowest
+    k0 = logits.reshape(1, 5, 1).astype(np.float32)
+    q = np.ones((1, 1, d), np.float32)
+    kn = np.array([[[4.0]]], np.float32)
+    oc = OracleCache([k0], [np.zeros_like(k0)], [np.arange(5)], [5], 5, 1, sink, recent, scale=1.0)
+    dec = oc.decide(q, kn, np.zeros((1, 1, d), np.float32))
+    z = math.exp(0) + math.exp(1) + math.exp(3) + math.exp(5) + math.exp(2) + math.exp(4)
+    assert dec.evict[0, 0] == 1
+    assert abs(dec.gap[0, 0] - (math.exp(3) - math.exp(1)) / z) < 1e-15  # not exp(2) - exp(1): slot 4 is protected
+    assert dec.accepts(0, 0, 1) and not dec.accepts(0, 0, 2) and not dec.accepts(0, 0, 4)
+    # a single eligible slot: no second score, infinite gap
+    oc1 = OracleCache([k0[:, :3]], [np.zeros_like(k0[:, :3])], [np.arange(3)], [3], 3, 1, sink, recent, scale=1.0)
+    dec1 = oc1.decide(q, kn, np.zeros((1, 1, d), np.float32))
+    assert dec1.evict[0, 0] == 1 and np.isinf(dec1.gap[0, 0])
+    assert not dec1.accepts(0, 0, 0) and not dec1.accepts(0, 0, 2)
+
+
+def test_accepts_near_ties_only_within_tolerance():
+    """Two eligible slots whose importances differ by less than the tolerance:
+    both are accepted, a third further away is not, and nothing is accepted in
+    place of an append."""
+    d = 1
+    eps = 1e-9  # logits 1 and 1 + eps give importances about 1e-10 apart
+    logits = np.array([0.0, 1.0 + eps, 1.0, 4.0, 0.0])
+    k0 = logits.reshape(1, 5, 1)
+    q = np.ones((1, 1, d))
+    oc = OracleCache([k0], [np.zeros_like(k0)], [np.arange(5)], [5], 5, 1, 1, 1, scale=1.0)
+    dec = oc.decide(q, np.array([[[0.0]]]), np.zeros((1, 1, d)))
+    assert dec.evict[0, 0] == 2 and dec.gap[0, 0] < 1e-6
+    assert dec.accepts(0, 0, 1) and dec.accepts(0, 0, 2) and not dec.accepts(0, 0, 3)
+    assert not dec.accepts(0, 0, -1)
+    # a cache that is not full appends: only the next free slot is right
+    oc2 = OracleCache([k0], [np.zeros_like(k0)], [np.arange(5)], [5], 8, 1, 1, 1, scale=1.0)
+    dec2 = oc2.decide(q, np.array([[[0.0]]]), np.zeros((1, 1, d)))
+    assert dec2.evict[0, 0] == -1 and dec2.accepts(0, 0, -1) and not dec2.accepts(0, 0, 2)
 
 
 def test_streaming_closed_form_when_logits_rise_with_position():
@@ -271,8 +320,13 @@ def test_oracle_matches_brute_force(hkv, G, d, budget, sink, recent, prefill, vl
         kn = rng.standard_normal((B, hkv, d)).astype(np.float32)
         vn = rng.standard_normal((B, hkv, d)).astype(np.float32)
         dec = oc.decide(q, kn, vn)
+        gap_b = br.gaps(q, kn, vn)  # before the step changes the cache
         out_b, slot_b, ev_b = br.step(q, kn, vn)
         np.testing.assert_allclose(dec.out, np.array(out_b), rtol=0, atol=1e-12)
+        gb = np.array(gap_b)
+        assert (np.isinf(gb) == np.isinf(dec.gap)).all()
+        fin = np.isfinite(gb)
+        np.testing.assert_allclose(dec.gap[fin], gb[fin], rtol=0, atol=1e-12)
         exact = dec.gap > 1e-12
         assert (np.array(ev_b)[exact] == dec.evict[exact]).all()
         oc.commit(np.array(slot_b), kn, vn)  # follow the brute force inside near-ties
