@@ -234,6 +234,25 @@ lf_status lf_prefill_compress(const lf_config* cfg, const int32_t* budgets, cons
                               void* k_cache, void* v_cache, int32_t* kept, void* work, size_t work_bytes,
                               void* stream);
 
+/*
+ * lf_prefill_compress_noalloc - lf_prefill_compress without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).  The
+ * scratch is a static device array inside the library, LF_PREFILL_SCRATCH_BYTES
+ * (64 MiB) per GPU, held by every GPU the library runs on until the process
+ * ends; its address is looked up once per device.  The call allocates nothing.
+ * Arguments, results and errors as lf_prefill_compress; batches whose
+ * lf_prefill_work_bytes() exceeds LF_PREFILL_SCRATCH_BYTES are rejected with
+ * LF_ERR_ARG (use lf_prefill_compress with a workspace instead).  All calls on
+ * one GPU share its scratch: calls that overlap on one GPU (different streams,
+ * different threads) race and must be serialised by the caller.
+ */
+#define LF_PREFILL_SCRATCH_BYTES ((size_t)64 << 20)
+lf_status lf_prefill_compress_noalloc(const lf_config* cfg, const int32_t* budgets, const int32_t* prefill,
+                                      int32_t max_prefill, const void* q_last, const void* k_pre,
+                                      const void* v_pre, void* k_cache, void* v_cache, int32_t* kept,
+                                      void* stream);
+
 /* lf_free - release the host handle (NULL-safe).  Device buffers stay the caller's. */
 void lf_free(lf_cache* cache);
 

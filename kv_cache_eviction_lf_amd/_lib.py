@@ -69,6 +69,11 @@ PROTOTYPES = {
         [POINTER(lf_config), POINTER(c_int32), POINTER(c_int32), c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
          c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
     ),
+    "lf_prefill_compress_noalloc": (
+        c_int32,
+        [POINTER(lf_config), POINTER(c_int32), POINTER(c_int32), c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
+         c_void_p, c_void_p, c_void_p],
+    ),
 }
 
 _lib = None
@@ -177,6 +182,14 @@ def lf_prefill_compress(cfg: lf_config, budgets, prefill, max_prefill: int, q_la
         ctypes.byref(cfg), _i32_array(budgets), _i32_array(prefill), c_int32(max_prefill), c_void_p(q_last),
         c_void_p(k_pre), c_void_p(v_pre), c_void_p(k_cache), c_void_p(v_cache), c_void_p(kept), c_void_p(work),
         c_size_t(work_bytes), c_void_p(stream)), "lf_prefill_compress")
+
+
+def lf_prefill_compress_noalloc(cfg: lf_config, budgets, prefill, max_prefill: int, q_last: int, k_pre: int,
+                                v_pre: int, k_cache: int, v_cache: int, kept: int, stream: int = 0) -> None:
+    _check(load_library().lf_prefill_compress_noalloc(
+        ctypes.byref(cfg), _i32_array(budgets), _i32_array(prefill), c_int32(max_prefill), c_void_p(q_last),
+        c_void_p(k_pre), c_void_p(v_pre), c_void_p(k_cache), c_void_p(v_cache), c_void_p(kept), c_void_p(stream)),
+        "lf_prefill_compress_noalloc")
 
 
 def lf_decode_step(q: int, k_new: int, v_new: int, cache: int, out: int, evict_idx: int, stream: int = 0) -> None:

@@ -275,6 +275,69 @@ lf_status step_impl(const void* q, const void* k_new, const void* v_new, lf_cach
   return LF_OK;
 }
 
+// Prefill compression with the scratch `work` (work_bytes >= need, the size
+// lf_prefill_work_bytes gives): shared by lf_prefill_compress (caller's
+// workspace) and lf_prefill_compress_noalloc (the library's static scratch).
+lf_status prefill_impl(const lf_config* cfg, const int32_t* budgets, const int32_t* prefill, int32_t max_prefill,
+                       const void* q_last, const void* k_pre, const void* v_pre, void* k_cache, void* v_cache,
+                       int32_t* kept, void* work, size_t work_bytes, size_t need, void* stream) {
+  std::vector<int32_t> bud;
+  lf_status st = validate_budgets(cfg, budgets, bud);
+  if (st != LF_OK) return st;
+  if (!prefill) return fail(LF_ERR_ARG, "prefill is NULL");
+  for (int b = 0; b < cfg->batch; ++b)
+    if (prefill[b] < 1 || prefill[b] > max_prefill)
+      return fail(LF_ERR_ARG, "prefill[%d] = %d outside [1, max_prefill = %d]", b, prefill[b], max_prefill);
+  const void* dev[] = {q_last, k_pre, v_pre, k_cache, v_cache, kept, work};
+  const char* names[] = {"q_last", "k_pre", "v_pre", "k_cache", "v_cache", "kept", "work"};
+  for (int i = 0; i < 7; ++i) {
+    if (!dev[i]) return fail(LF_ERR_ARG, "%s is NULL", names[i]);
+    if (reinterpret_cast<uintptr_t>(dev[i]) % 16) return fail(LF_ERR_ARG, "%s is not 16-byte aligned", names[i]);
+  }
+  if (work_bytes < need) return fail(LF_ERR_ARG, "work_bytes %zu < %zu (lf_prefill_work_bytes)", work_bytes, need);
+  const size_t pairs = (size_t)cfg->batch * cfg->n_kv_heads;
+  const int nck = (max_prefill + lf::kPrefillChunk - 1) / lf::kPrefillChunk;
+  char* w = static_cast<char*>(work);
+  float* stats = reinterpret_cast<float*>(w + align_up(sizeof(float) * pairs * (size_t)max_prefill));
+  int32_t* dlen = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(stats) + align_up(sizeof(float) * pairs * nck * 16));
+  float* logits = reinterpret_cast<float*>(reinterpret_cast<char*>(dlen) + align_up(sizeof(int32_t) * 2 * cfg->batch));
+  std::vector<int32_t> host(2 * cfg->batch);
+  for (int b = 0; b < cfg->batch; ++b) {
+    host[b] = prefill[b];
+    host[cfg->batch + b] = bud[b];
+  }
+  char err[256];
+  if (lf::upload_and_wait(dlen, host.data(), sizeof(int32_t) * host.size(), stream, err, sizeof(err)))
+    return fail(LF_ERR_HIP, "%s", err);
+  lf::PrefillArgs a{};
+  a.q_last = q_last;
+  a.k_pre = k_pre;
+  a.v_pre = v_pre;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.kept = kept;
+  a.work = reinterpret_cast<float*>(w);
+  a.stats = stats;
+  a.logits = logits;
+  a.n_chunks = nck;
+  a.n_copy = (cfg->max_budget + lf::kPrefillCopyRows - 1) / lf::kPrefillCopyRows;
+  a.prefill = dlen;
+  a.budget = dlen + cfg->batch;
+  a.n_kv_heads = cfg->n_kv_heads;
+  a.n_q_heads = cfg->n_q_heads;
+  a.group = cfg->n_q_heads / cfg->n_kv_heads;
+  a.max_prefill = max_prefill;
+  a.max_budget = cfg->max_budget;
+  a.sink = cfg->sink;
+  a.recent = cfg->recent;
+  const double scale = cfg->softmax_scale > 0 ? cfg->softmax_scale : 1.0 / std::sqrt((double)cfg->head_dim);
+  a.scale_log2 = (float)(scale * 1.4426950408889634);
+  if (lf::launch_prefill(cfg->dtype, cfg->head_dim, a, (int)pairs, stream, err, sizeof(err)))
+    return fail(LF_ERR_HIP, "%s", err);
+  g_err[0] = 0;
+  return LF_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -465,61 +528,28 @@ lf_status lf_prefill_compress(const lf_config* cfg, const int32_t* budgets, cons
   size_t need = 0;
   lf_status st = lf_prefill_work_bytes(cfg, max_prefill, &need);
   if (st != LF_OK) return st;
-  std::vector<int32_t> bud;
-  st = validate_budgets(cfg, budgets, bud);
+  if (!work) return fail(LF_ERR_ARG, "work is NULL");
+  return prefill_impl(cfg, budgets, prefill, max_prefill, q_last, k_pre, v_pre, k_cache, v_cache, kept, work,
+                      work_bytes, need, stream);
+}
+
+lf_status lf_prefill_compress_noalloc(const lf_config* cfg, const int32_t* budgets, const int32_t* prefill,
+                                      int32_t max_prefill, const void* q_last, const void* k_pre,
+                                      const void* v_pre, void* k_cache, void* v_cache, int32_t* kept,
+                                      void* stream) {
+  size_t need = 0;
+  lf_status st = lf_prefill_work_bytes(cfg, max_prefill, &need);
   if (st != LF_OK) return st;
-  if (!prefill) return fail(LF_ERR_ARG, "prefill is NULL");
-  for (int b = 0; b < cfg->batch; ++b)
-    if (prefill[b] < 1 || prefill[b] > max_prefill)
-      return fail(LF_ERR_ARG, "prefill[%d] = %d outside [1, max_prefill = %d]", b, prefill[b], max_prefill);
-  const void* dev[] = {q_last, k_pre, v_pre, k_cache, v_cache, kept, work};
-  const char* names[] = {"q_last", "k_pre", "v_pre", "k_cache", "v_cache", "kept", "work"};
-  for (int i = 0; i < 7; ++i) {
-    if (!dev[i]) return fail(LF_ERR_ARG, "%s is NULL", names[i]);
-    if (reinterpret_cast<uintptr_t>(dev[i]) % 16) return fail(LF_ERR_ARG, "%s is not 16-byte aligned", names[i]);
-  }
-  if (work_bytes < need) return fail(LF_ERR_ARG, "work_bytes %zu < %zu (lf_prefill_work_bytes)", work_bytes, need);
-  const size_t pairs = (size_t)cfg->batch * cfg->n_kv_heads;
-  const int nck = (max_prefill + lf::kPrefillChunk - 1) / lf::kPrefillChunk;
-  char* w = static_cast<char*>(work);
-  float* stats = reinterpret_cast<float*>(w + align_up(sizeof(float) * pairs * (size_t)max_prefill));
-  int32_t* dlen = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(stats) + align_up(sizeof(float) * pairs * nck * 16));
-  float* logits = reinterpret_cast<float*>(reinterpret_cast<char*>(dlen) + align_up(sizeof(int32_t) * 2 * cfg->batch));
-  std::vector<int32_t> host(2 * cfg->batch);
-  for (int b = 0; b < cfg->batch; ++b) {
-    host[b] = prefill[b];
-    host[cfg->batch + b] = bud[b];
-  }
+  if (need > lf::kPrefillScratchBytes)
+    return fail(LF_ERR_ARG,
+                "this batch needs %zu bytes of prefill scratch, the static scratch holds %zu: use "
+                "lf_prefill_compress with a workspace",
+                need, lf::kPrefillScratchBytes);
+  void* work = nullptr;
   char err[256];
-  if (lf::upload_and_wait(dlen, host.data(), sizeof(int32_t) * host.size(), stream, err, sizeof(err)))
-    return fail(LF_ERR_HIP, "%s", err);
-  lf::PrefillArgs a{};
-  a.q_last = q_last;
-  a.k_pre = k_pre;
-  a.v_pre = v_pre;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  a.kept = kept;
-  a.work = reinterpret_cast<float*>(w);
-  a.stats = stats;
-  a.logits = logits;
-  a.n_chunks = nck;
-  a.n_copy = (cfg->max_budget + lf::kPrefillCopyRows - 1) / lf::kPrefillCopyRows;
-  a.prefill = dlen;
-  a.budget = dlen + cfg->batch;
-  a.n_kv_heads = cfg->n_kv_heads;
-  a.n_q_heads = cfg->n_q_heads;
-  a.group = cfg->n_q_heads / cfg->n_kv_heads;
-  a.max_prefill = max_prefill;
-  a.max_budget = cfg->max_budget;
-  a.sink = cfg->sink;
-  a.recent = cfg->recent;
-  const double scale = cfg->softmax_scale > 0 ? cfg->softmax_scale : 1.0 / std::sqrt((double)cfg->head_dim);
-  a.scale_log2 = (float)(scale * 1.4426950408889634);
-  if (lf::launch_prefill(cfg->dtype, cfg->head_dim, a, (int)pairs, stream, err, sizeof(err)))
-    return fail(LF_ERR_HIP, "%s", err);
-  g_err[0] = 0;
-  return LF_OK;
+  if (lf::prefill_scratch(&work, err, sizeof(err))) return fail(LF_ERR_HIP, "%s", err);
+  return prefill_impl(cfg, budgets, prefill, max_prefill, q_last, k_pre, v_pre, k_cache, v_cache, kept, work,
+                      lf::kPrefillScratchBytes, need, stream);
 }
 
 }  // extern "C"

@@ -19,6 +19,9 @@ constexpr int kTargetItems = 256;   // split pairs into chunks until about this 
 constexpr int kMaxPrefill = 65536;  // prefill compression: positions fit 16 bits of the selection key
 constexpr int kPrefillChunk = 512;  // rows per workgroup of the prefill score passes
 constexpr int kPrefillCopyRows = 256;  // kept rows per workgroup of the prefill copy
+// Static device scratch of lf_prefill_compress_noalloc (one copy per GPU).
+constexpr size_t kPrefillScratchBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;
 
 // Per (sequence, KV head) pair.  Written by lf_init_cache, updated in place by
 // the last-arriving workgroup of the pair at the end of every step.
@@ -128,6 +131,9 @@ struct PrefillArgs {
 int launch_step(int dtype, int head_dim, int group, const StepArgs& a, void* stream, char* err, size_t errlen);
 int launch_prefill(int dtype, int head_dim, const PrefillArgs& a, int n_pairs, void* stream, char* err,
                    size_t errlen);
+// Device address of the static prefill scratch on the current device (looked
+// up once per device); 0 on success.
+int prefill_scratch(void** ptr, char* err, size_t errlen);
 int upload_and_wait(void* dst, const void* src, size_t bytes, void* stream, char* err, size_t errlen);
 int download_and_wait(void* dst, const void* src, size_t bytes, void* stream, char* err, size_t errlen);
 

@@ -24,6 +24,8 @@
 //   prefill_copy_kernel        a workgroup per (pair, 256 kept rows): the
 //                              kept K/V rows copied in order.
 #include <hip/hip_runtime.h>
+
+#include <mutex>
 #include <stdint.h>
 
 #include "lf_internal.h"
@@ -50,7 +52,7 @@ __device__ __forceinline__ void unpack16(const uint4& r, float (&x)[4], F32E) {
   x[2] = __uint_as_float(r.z);
   x[3] = __uint_as_float(r.w);
 }
-__device__ __forceinline__ void unpack16(const uint4& r, float (&x)[8], BF16E) {
+[[maybe_unused]] __device__ __forceinline__ void unpack16(const uint4& r, float (&x)[8], BF16E) {
   const uint32_t w[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -497,6 +499,42 @@ void launch_prefill(const PrefillArgs& a, int n_pairs, hipStream_t s) {
 }
 
 }  // namespace
+
+// Device scratch of the allocation-free prefill compression
+// (lf_prefill_compress_noalloc): every GPU the library runs on holds one copy
+// until the process ends.  Host code must not pass `scratch` itself to a
+// kernel (in host code the name is a host-side stand-in, not a device
+// address): prefill_scratch() looks up each device's address once and the
+// kernels receive that pointer.  The prefill kernels write every byte they
+// read in a call, so nothing needs clearing between calls.
+static __device__ __align__(256) unsigned char scratch[kPrefillScratchBytes];
+
+int prefill_scratch(void** ptr, char* err, size_t errlen) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    snprintf(err, errlen, "hipGetDevice failed: %s", hipGetErrorString(e));
+    return 1;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    snprintf(err, errlen, "device %d beyond the %d devices the static scratch supports", dev, kMaxDevices);
+    return 1;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      snprintf(err, errlen, "hipGetSymbolAddress(scratch) on device %d failed: %s", dev, hipGetErrorString(e));
+      return 1;
+    }
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return 0;
+}
 
 int launch_prefill(int dtype, int head_dim, const PrefillArgs& a, int n_pairs, void* stream, char* err,
                    size_t errlen) {

@@ -167,3 +167,15 @@ def test_reset_sequences_rejects_bad_handles_and_arguments():
     assert ei.value.status == LF_ERR_STATE
     with pytest.raises(ValueError):
         _lib.lf_reset_sequences_budget(0, [0, 1], [5, 5], [100])
+
+
+def test_prefill_noalloc_rejects_batches_beyond_its_scratch():
+    # 128 sequences x 8 KV heads x 16384 prefill positions at G = 5 need far
+    # more than the static scratch holds: rejected before any device work
+    cfg = _cfg(batch=128, n_q_heads=40, n_kv_heads=8, max_budget=8192, recent=64)
+    need = _lib.lf_prefill_work_bytes(cfg, 16384)
+    assert need > (64 << 20)
+    with pytest.raises(LFError) as ei:
+        _lib.lf_prefill_compress_noalloc(cfg, [8192] * 128, [16384] * 128, 16384, 16, 16, 16, 16, 16, 16)
+    assert ei.value.status == LF_ERR_ARG
+    assert "static scratch" in _lib.lf_last_error()
