@@ -152,6 +152,44 @@ lf_status lf_decode_step_dbg(const void* q, const void* k_new, const void* v_new
                              void* out, int32_t* evict_idx, float* scores, float* lse, void* stream);
 
 /*
+ * lf_set_split_wait - how long a chunk of a split (sequence, KV head) pair
+ * waits, after streaming its rows, for the pair's other chunks to publish
+ * their softmax statistics; with them it scores its own slots from on-chip
+ * logits.  A chunk that stops waiting (or never waits) hands its logits over
+ * through the state buffer and the pair's last chunk scores them: results are
+ * bit-identical either way, only slower (lf_check_state counts such chunks,
+ * together with the chunks whose logits never stay on chip: fp32 caches and
+ * chunks longer than the on-chip buffers).  Waiting pays when the pair's
+ * chunks run at the same time, which a step whose work items fit the GPU at
+ * once gives.
+ *   cache        live handle.
+ *   max_wait_us  0 .. 1000000 microseconds; 0: never wait.  Default 100.
+ * Takes effect for the steps launched after the call.  Errors: LF_ERR_ARG,
+ * LF_ERR_STATE.
+ */
+lf_status lf_set_split_wait(lf_cache* cache, int32_t max_wait_us);
+
+/* Result of lf_check_state. */
+typedef struct {
+  uint32_t deferred; /* split chunks that handed their logits over through memory, since init */
+  int32_t n_pairs;   /* batch * n_kv_heads */
+  int32_t bad_pair;  /* first pair that failed a check, or -1 */
+  int32_t reserved;
+} lf_state_report;
+
+/*
+ * lf_check_state - read the state back (after the steps queued on `stream`)
+ * and check its invariants: the header matches the handle; per pair the
+ * layout fields are the handle's, the fill level is min(position, budget),
+ * the epoch is non-zero, no chunk counter is left over from a step, and the
+ * slots of the `recent` newest positions are distinct filled slots.
+ *   report  host: filled on LF_OK and on LF_ERR_STATE (bad_pair names the pair).
+ * Synchronous (a device-to-host copy); errors: LF_ERR_ARG, LF_ERR_STATE
+ * (a broken invariant, described by lf_last_error), LF_ERR_HIP.
+ */
+lf_status lf_check_state(const lf_cache* cache, void* stream, lf_state_report* report);
+
+/*
  * lf_reset_sequences - restart some sequences of the batch in place (a finished
  * request's place taken by a new one under continuous batching) while the
  * others keep their state.  The decode step runs over a static, pre-allocated

@@ -25,6 +25,10 @@ class LFError(RuntimeError):
         self.status = status
 
 
+class lf_state_report(ctypes.Structure):
+    _fields_ = [("deferred", c_uint32), ("n_pairs", c_int32), ("bad_pair", c_int32), ("reserved", c_int32)]
+
+
 class lf_config(ctypes.Structure):
     _fields_ = [
         ("batch", c_int32),
@@ -61,6 +65,8 @@ PROTOTYPES = {
     "lf_probe_read_sink_words": (c_int32, []),
     "lf_probe_empty": (c_int32, [c_int32, c_void_p]),
     "lf_prefill_work_bytes": (c_int32, [POINTER(lf_config), c_int32, POINTER(c_size_t)]),
+    "lf_set_split_wait": (c_int32, [c_void_p, c_int32]),
+    "lf_check_state": (c_int32, [c_void_p, c_void_p, POINTER(lf_state_report)]),
     "lf_reset_sequences": (c_int32, [c_void_p, c_int32, POINTER(c_int32), POINTER(c_int64), c_void_p]),
     "lf_reset_sequences_budget": (
         c_int32, [c_void_p, c_int32, POINTER(c_int32), POINTER(c_int64), POINTER(c_int32), c_void_p]),
@@ -190,6 +196,16 @@ def lf_prefill_compress_noalloc(cfg: lf_config, budgets, prefill, max_prefill: i
         ctypes.byref(cfg), _i32_array(budgets), _i32_array(prefill), c_int32(max_prefill), c_void_p(q_last),
         c_void_p(k_pre), c_void_p(v_pre), c_void_p(k_cache), c_void_p(v_cache), c_void_p(kept), c_void_p(stream)),
         "lf_prefill_compress_noalloc")
+
+
+def lf_set_split_wait(cache: int, max_wait_us: int) -> None:
+    _check(load_library().lf_set_split_wait(c_void_p(cache), c_int32(max_wait_us)), "lf_set_split_wait")
+
+
+def lf_check_state(cache: int, stream: int = 0) -> lf_state_report:
+    rep = lf_state_report()
+    _check(load_library().lf_check_state(c_void_p(cache), c_void_p(stream), ctypes.byref(rep)), "lf_check_state")
+    return rep
 
 
 def lf_decode_step(q: int, k_new: int, v_new: int, cache: int, out: int, evict_idx: int, stream: int = 0) -> None:

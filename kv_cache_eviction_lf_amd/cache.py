@@ -114,6 +114,20 @@ class LongFlowCache:
             full[int(b)] = int(nb)
         self.budgets = full
 
+    def set_split_wait(self, max_wait_us: int) -> None:
+        """How long a chunk of a split pair waits for the pair's statistics
+        before handing its logits over through memory (lf_set_split_wait)."""
+        if not self.handle:
+            raise RuntimeError("cache is closed")
+        _lib.lf_set_split_wait(self.handle, int(max_wait_us))
+
+    def check_state(self):
+        """Read the state back and check its invariants (lf_check_state);
+        returns the report (deferred chunks since init, pairs)."""
+        if not self.handle:
+            raise RuntimeError("cache is closed")
+        return _lib.lf_check_state(self.handle, _stream_handle(self.device))
+
     def close(self) -> None:
         if self.handle:
             _lib.lf_free(self.handle)

@@ -7,6 +7,7 @@
 // summary, section 2.C).  This file only plans work and launches it; every
 // arithmetic step of the decode runs in lf_kernel.hip.
 #include <cmath>
+#include <cstddef>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -27,6 +28,7 @@ struct lf_cache {
   char* state;
   size_t state_bytes;  // capacity of the caller's state buffer
   float scale_log2;
+  uint32_t wait_ticks;  // split chunks' wait for their pair's statistics (s_memrealtime ticks)
   int32_t u_budget;  // the common budget when every sequence has the same one, else 0
   std::vector<int32_t> budgets;  // per sequence, as validated at init
 };
@@ -44,6 +46,9 @@ lf_status fail(lf_status st, const char* fmt, ...) {
 }
 
 size_t align_up(size_t x) { return (x + lf::kAlign - 1) / lf::kAlign * lf::kAlign; }
+
+// Default wait of a split chunk for its pair's statistics: 100 us (100 MHz ticks).
+constexpr uint32_t kDefaultWaitTicks = 10000;
 
 lf_status validate_config(const lf_config* cfg) {
   if (!cfg) return fail(LF_ERR_ARG, "cfg is NULL");
@@ -89,7 +94,6 @@ void start_sequence(const lf_config& cfg, int b, int64_t t, int32_t budget, lf::
     const int p = b * cfg.n_kv_heads + g;
     meta[p].t = (int32_t)t;
     meta[p].len = (int32_t)len;
-    meta[p].ticket = 0;
     for (int j = 0; j < R; ++j) ring[(size_t)p * R + j] = -1;
     // The R newest cached positions [t - R, t): slot = position while the
     // prefill fits, else they are the last R slots (layout contract).
@@ -157,12 +161,14 @@ lf_status make_layout(const lf_config* cfg, const std::vector<int32_t>& bud, lf:
   off = align_up(off + sizeof(lf::PairMeta) * P);
   L.ring = off;
   off = align_up(off + sizeof(int32_t) * P * (size_t)cfg->recent);
+  L.count = off;
+  off = align_up(off + sizeof(uint32_t) * P);
   L.items = off;
   off = align_up(off + sizeof(lf::WorkItem) * W);
-  L.part_ml = off;
-  off = align_up(off + sizeof(float) * 2 * group * W);
-  L.part_acc = off;
-  off = align_up(off + sizeof(float) * (size_t)group * cfg->head_dim * W);
+  L.xcell = off;
+  off = align_up(off + sizeof(uint64_t) * (size_t)group * (cfg->head_dim + 2) * W);
+  L.xcand = off;
+  off = align_up(off + sizeof(uint64_t) * 2 * W);
   L.logits = off;  // none without importance (LF_SCORE_NONE)
   if (cfg->score != LF_SCORE_NONE) off = align_up(off + sizeof(float) * (size_t)group * S);
   L.total = off;
@@ -182,6 +188,7 @@ lf_status make_layout(const lf_config* cfg, const std::vector<int32_t>& bud, lf:
           m.nchunk = (bud[b] + chunk - 1) / chunk;
           m.slot0 = slot;
           m.lstride = lstride;
+          m.epoch = 1;
         }
         slot += lstride;
       }
@@ -254,9 +261,13 @@ lf_status step_impl(const void* q, const void* k_new, const void* v_new, lf_cach
   a.meta = reinterpret_cast<lf::PairMeta*>(s + L.meta);
   a.ring = reinterpret_cast<int32_t*>(s + L.ring);
   a.items = reinterpret_cast<const lf::WorkItem*>(s + L.items);
-  a.part_ml = reinterpret_cast<float*>(s + L.part_ml);
-  a.part_acc = reinterpret_cast<float*>(s + L.part_acc);
+  a.xcell = reinterpret_cast<uint64_t*>(s + L.xcell);
+  a.xcand = reinterpret_cast<uint64_t*>(s + L.xcand);
+  a.count = reinterpret_cast<uint32_t*>(s + L.count);
+  a.deferred = reinterpret_cast<uint32_t*>(s + L.header + offsetof(lf::StateHeader, deferred));
+  a.fault = reinterpret_cast<uint32_t*>(s + L.header + offsetof(lf::StateHeader, fault));
   a.logits = reinterpret_cast<float*>(s + L.logits);
+  a.wait_ticks = cache->wait_ticks;
   a.n_items = L.n_items;
   a.n_pairs = cfg.batch * cfg.n_kv_heads;
   a.n_q_heads = cfg.n_q_heads;
@@ -385,9 +396,10 @@ lf_status lf_init_cache(const lf_config* cfg, const int32_t* budgets, const int6
     return fail(LF_ERR_ARG, "state_bytes %zu < required %zu (see lf_state_bytes)", state_bytes, L.total);
 
   if (!(flags & LF_INIT_ATTACH)) {
-    // Host image of header + meta + ring + work list, uploaded in one copy.
-    std::vector<char> img(L.part_ml, 0);
-    lf::StateHeader h{lf::kStateMagic, L.n_pairs, L.n_items, L.total_slots};
+    // Host image of header, meta, ring, work list and the zeroed exchange
+    // cells (no stale epoch tag may survive), uploaded in one copy.
+    std::vector<char> img(L.logits, 0);
+    lf::StateHeader h{lf::kStateMagic, L.n_pairs, L.n_items, L.total_slots, 0, 0, {0, 0}};
     std::memcpy(img.data() + L.header, &h, sizeof(h));
     int32_t* ring = reinterpret_cast<int32_t*>(img.data() + L.ring);
     for (int b = 0; b < cfg->batch; ++b) start_sequence(*cfg, b, seq_len[b], bud[b], meta.data(), ring);
@@ -410,6 +422,7 @@ lf_status lf_init_cache(const lf_config* cfg, const int32_t* budgets, const int6
   c->v_cache = v_cache;
   c->state = static_cast<char*>(state);
   c->state_bytes = state_bytes;
+  c->wait_ticks = kDefaultWaitTicks;
   const double scale = cfg->softmax_scale > 0 ? cfg->softmax_scale : 1.0 / std::sqrt((double)cfg->head_dim);
   c->scale_log2 = (float)(scale * 1.4426950408889634);
   *out = c;
@@ -433,6 +446,76 @@ void lf_free(lf_cache* cache) {
   delete cache;
 }
 
+lf_status lf_set_split_wait(lf_cache* cache, int32_t max_wait_us) {
+  lf_status st = check_handle(cache);
+  if (st != LF_OK) return st;
+  if (max_wait_us < 0 || max_wait_us > 1000000)
+    return fail(LF_ERR_ARG, "max_wait_us %d outside [0, 1000000]", max_wait_us);
+  cache->wait_ticks = (uint32_t)max_wait_us * 100u;  // s_memrealtime runs at 100 MHz
+  g_err[0] = 0;
+  return LF_OK;
+}
+
+lf_status lf_check_state(const lf_cache* cache, void* stream, lf_state_report* report) {
+  lf_status st = check_handle(cache);
+  if (st != LF_OK) return st;
+  if (!report) return fail(LF_ERR_ARG, "report is NULL");
+  const lf_config& cfg = cache->cfg;
+  const lf::StateLayout& L = cache->lay;
+  std::vector<char> img(L.items);
+  if (lf::download_and_wait(img.data(), cache->state, L.items, stream, g_err, sizeof(g_err))) return LF_ERR_HIP;
+  const lf::StateHeader* h = reinterpret_cast<const lf::StateHeader*>(img.data() + L.header);
+  report->deferred = h->deferred;
+  report->n_pairs = L.n_pairs;
+  report->bad_pair = -1;
+  report->reserved = 0;
+  if (h->magic != lf::kStateMagic || h->n_pairs != L.n_pairs || h->n_items != L.n_items)
+    return fail(LF_ERR_STATE, "state header does not match the handle (magic 0x%08x, %d pairs, %d items)", h->magic,
+                h->n_pairs, h->n_items);
+  if (h->fault)
+    return fail(LF_ERR_STATE, "a step's wait for another workgroup's published words hit its safety bound "
+                "(fault bits 0x%x: 1 statistics, 2 value sums, 4 candidates); results since are not valid", h->fault);
+  lf::StateLayout L2{};
+  std::vector<lf::PairMeta> want;
+  if ((st = make_layout(&cfg, cache->budgets, L2, nullptr, &want)) != LF_OK) return st;
+  const lf::PairMeta* meta = reinterpret_cast<const lf::PairMeta*>(img.data() + L.meta);
+  const int32_t* ring = reinterpret_cast<const int32_t*>(img.data() + L.ring);
+  const uint32_t* count = reinterpret_cast<const uint32_t*>(img.data() + L.count);
+  const int R = cfg.recent;
+  std::vector<char> seen;
+  for (int p = 0; p < L.n_pairs; ++p) {
+    const lf::PairMeta& m = meta[p];
+    const lf::PairMeta& w = want[p];
+    const char* why = nullptr;
+    if (m.budget != w.budget || m.nchunk != w.nchunk || m.item0 != w.item0 || m.slot0 != w.slot0 ||
+        m.lstride != w.lstride)
+      why = "layout fields differ from the handle's";
+    else if (m.t < 0 || m.len != (m.t < m.budget ? m.t : m.budget))
+      why = "fill level is not min(position, budget)";
+    else if (m.epoch == 0)
+      why = "epoch is 0";
+    else if (count[p] != 0)
+      why = "chunk counter is not 0 between steps";
+    if (!why && R > 0) {
+      seen.assign(m.budget, 0);
+      for (int64_t pos = m.t - R < 0 ? 0 : m.t - R; pos < m.t && !why; ++pos) {
+        const int32_t sl = ring[(size_t)p * R + pos % R];
+        if (sl < 0 || sl >= m.len)
+          why = "a recent position's slot is outside the filled slots";
+        else if (seen[sl]++)
+          why = "two recent positions share a slot";
+      }
+    }
+    if (why) {
+      report->bad_pair = p;
+      return fail(LF_ERR_STATE, "pair %d (sequence %d, KV head %d): %s", p, p / cfg.n_kv_heads, p % cfg.n_kv_heads,
+                  why);
+    }
+  }
+  g_err[0] = 0;
+  return LF_OK;
+}
+
 lf_status lf_reset_sequences(lf_cache* cache, int32_t n, const int32_t* seqs, const int64_t* seq_len,
                              void* stream) {
   lf_status st = check_reset_args(cache, n, seqs, seq_len);
@@ -445,6 +528,11 @@ lf_status lf_reset_sequences(lf_cache* cache, int32_t n, const int32_t* seqs, co
   std::vector<int32_t> ring((size_t)L.n_pairs * (R > 0 ? R : 1));
   for (int i = 0; i < n; ++i) {
     const int b = seqs[i];
+    // The pairs' epochs tag their exchange cells: read the metadata back so
+    // they carry on (a restarted epoch could match a stale tag).
+    if (lf::download_and_wait(meta.data() + (size_t)b * H, cache->state + L.meta + sizeof(lf::PairMeta) * (size_t)b * H,
+                              sizeof(lf::PairMeta) * H, stream, g_err, sizeof(g_err)))
+      return LF_ERR_HIP;
     start_sequence(cfg, b, seq_len[i], cache->budgets[b], meta.data(), ring.data());
     // A sequence's pairs are contiguous in the metadata and in the ring.
     if (lf::upload_and_wait(cache->state + L.meta + sizeof(lf::PairMeta) * (size_t)b * H, meta.data() + (size_t)b * H,
@@ -482,17 +570,20 @@ lf_status lf_reset_sequences_budget(lf_cache* cache, int32_t n, const int32_t* s
   // every other sequence's position, fill level and ring, restart the listed
   // ones, and write header, metadata, rings and the new work list back.
   const lf::StateLayout& old = cache->lay;
-  std::vector<char> img(L.part_ml, 0);
+  // The new work list moves the exchange cells: they are zeroed (no stale
+  // epoch tag may survive); the pairs' epochs and the chunk counters carry on.
+  std::vector<char> img(L.logits, 0);
   if (lf::download_and_wait(img.data(), cache->state, old.items, stream, g_err, sizeof(g_err))) return LF_ERR_HIP;
   const lf::PairMeta* cur = reinterpret_cast<const lf::PairMeta*>(img.data() + L.meta);
   for (int p = 0; p < L.n_pairs; ++p) {
     meta[p].t = cur[p].t;
     meta[p].len = cur[p].len;
-    meta[p].ticket = 0;
+    meta[p].epoch = cur[p].epoch;
   }
   int32_t* ring = reinterpret_cast<int32_t*>(img.data() + L.ring);
   for (int i = 0; i < n; ++i) start_sequence(cfg, seqs[i], seq_len[i], nb[seqs[i]], meta.data(), ring);
-  lf::StateHeader h{lf::kStateMagic, L.n_pairs, L.n_items, L.total_slots};
+  const lf::StateHeader* oldh = reinterpret_cast<const lf::StateHeader*>(img.data() + L.header);
+  lf::StateHeader h{lf::kStateMagic, L.n_pairs, L.n_items, L.total_slots, oldh->deferred, oldh->fault, {0, 0}};
   std::memcpy(img.data() + L.header, &h, sizeof(h));
   std::memcpy(img.data() + L.meta, meta.data(), sizeof(lf::PairMeta) * meta.size());
   std::memcpy(img.data() + L.items, items.data(), sizeof(lf::WorkItem) * items.size());

@@ -24,15 +24,15 @@ constexpr size_t kPrefillScratchBytes = size_t(64) << 20;
 constexpr int kMaxDevices = 64;
 
 // Per (sequence, KV head) pair.  Written by lf_init_cache, updated in place by
-// the last-arriving workgroup of the pair at the end of every step.
+// the workgroup that finishes the pair at the end of every step.
 struct PairMeta {
   int32_t t;        // position of the next incoming token
   int32_t len;      // filled slots, == budget once the cache is full
   int32_t budget;   // slot budget of this sequence
   int32_t nchunk;   // split-KV chunks of this pair
   int32_t item0;    // index of the pair's first work item
-  int32_t slot0;    // first slot of the pair in the logit / |v| workspaces
-  uint32_t ticket;  // chunks finished in the current step (reset to 0 by the last one)
+  int32_t slot0;    // first slot of the pair in the logit workspace
+  uint32_t epoch;   // step counter of a split pair (1 at init, never 0): tags its exchange cells
   int32_t lstride;  // row stride of the pair's logit workspace: budget rounded up to 64
 };
 static_assert(sizeof(PairMeta) == 32, "PairMeta layout");
@@ -51,11 +51,20 @@ struct StateHeader {
   int32_t n_pairs;
   int32_t n_items;
   int32_t total_slots;
+  uint32_t deferred;  // split chunks that handed their logits over through memory (counted by the kernel)
+  uint32_t fault;     // kFault* bits: a wait for another workgroup's words hit its safety bound
+  uint32_t pad[2];
 };
+// Every wait of one workgroup for words another has already issued ends
+// within this many s_memrealtime ticks (100 MHz: 0.2 s) even if the protocol
+// were broken; the kernel then records a fault bit instead of hanging.
+constexpr uint64_t kSafetyTicks = 20000000;
+constexpr uint32_t kFaultStats = 1, kFaultValues = 2, kFaultCandidates = 4;
 
-// Byte offsets of the regions of the caller's state buffer.
+// Byte offsets of the regions of the caller's state buffer.  Everything before
+// `items` depends only on the numbers of pairs and ring entries.
 struct StateLayout {
-  size_t header, meta, ring, items, part_ml, part_acc, logits, total;
+  size_t header, meta, ring, count, items, xcell, xcand, logits, total;
   int32_t n_pairs, n_items, total_slots, chunk, max_nchunk;
 };
 
@@ -73,9 +82,15 @@ struct StepArgs {
   PairMeta* meta;
   int32_t* ring;
   const WorkItem* items;
-  float* part_ml;   // [n_items][G][2]: (max of log2-domain logits, sum of exp2)
-  float* part_acc;  // [n_items][G][d]
-  float* logits;    // per pair [G][budget], logits of this step (VL1: plus log2 |v|_1)
+  // Exchange between the chunks of a split pair, every value a 64-bit word
+  // whose high half is the pair's epoch of the step that wrote it:
+  uint64_t* xcell;   // [n_items][G][d + 2]: the chunk's weighted value sums, then (max, sum) per head
+  uint64_t* xcand;   // [n_items][2]: the chunk's (score) and (slot | deferred << 31) candidate
+  uint32_t* count;   // [n_pairs]: chunks of the pair done with the step (reset by the finisher)
+  uint32_t* deferred;  // header counter of deferred chunks
+  uint32_t* fault;     // header fault bits (kFault*)
+  float* logits;    // per pair [G][lstride], logits of a deferred chunk's rows (VL1: plus log2 |v|_1)
+  uint32_t wait_ticks;  // how long (s_memrealtime ticks, 100 MHz) a chunk waits for its pair's statistics; 0: never
   int32_t n_items;
   int32_t n_pairs;  // batch * n_kv_heads
   int32_t n_q_heads;

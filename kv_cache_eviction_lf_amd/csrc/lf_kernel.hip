@@ -25,22 +25,23 @@
 //  * Work is a static list of (pair, row range) chunks, pair = (sequence, KV
 //    head); pairs are split only when there are too few of them to fill the
 //    GPU.  A chunk keeps a running max / sum / weighted value sum per head
-//    (log2 domain) and writes its raw logits out for the importance pass, or
-//    keeps them in LDS when its own workgroup will run the pair's tail: in
-//    fp32 when they fit, else in half precision, from which the tail bounds
-//    every slot's importance and scores exactly, from the key rows, only the
-//    slots that can still be the minimum.
-//  * A pair's tail runs in the workgroup that finishes it: directly when the
-//    pair is one chunk, else in the chunk that takes the last ticket
-//    (device-scope stores and loads on both sides of a relaxed device-scope
-//    fetch-add; the protocol is described at store_wt).  The tail merges the
-//    partials in chunk order, adds the incoming token, writes the output,
-//    computes the importance of every slot from the stored logits with the
-//    global max / normaliser (exactly; or bounded, then exact for the possible
-//    minima), takes the lexicographic (score, slot) argmin
+//    (log2 domain) and keeps its rows' logits in LDS (fp32; an unsplit pair
+//    also in half precision, from which its tail bounds every slot's
+//    importance and scores exactly, from the key rows, only the slots that
+//    can still be the minimum), or writes them to the workspace when they do
+//    not fit.
+//  * An unsplit pair's tail runs in its own workgroup: it adds the incoming
+//    token, writes the output, computes the importance of every slot with the
+//    step's max / normaliser, takes the lexicographic (score, slot) argmin
 //    outside the sink slots and the ring of recent slots, and copies k_new /
-//    v_new into the victim slot.  No other workgroup reads the pair after its
-//    ticket, so the in-place write cannot race with a reader.
+//    v_new into the victim slot.
+//  * The chunks of a split pair exchange only their statistics and value
+//    sums (epoch-tagged 64-bit words), each scores its own slots from LDS and
+//    writes the output rows of its share of the heads, and the chunk taking
+//    the pair's last ticket picks the argmin of the chunks' candidates and
+//    inserts the token (the protocol is described at split_tail).  No other
+//    workgroup reads the pair after its ticket, so the in-place write cannot
+//    race with a reader.
 //  * Cross-lane reductions use DPP and lane swaps; every reduction has a fixed
 //    order, so results are bit-reproducible.
 #include <hip/hip_runtime.h>
@@ -226,24 +227,20 @@ __device__ __forceinline__ uint2 load_nt(const uint2* p) {
   return make_uint2(x[0], x[1]);
 }
 
-// Data one workgroup hands to another in the same launch (logits and the
-// chunk partials of a split pair) moves only through device-scope stores and
-// loads: relaxed agent-scope atomics, or buffer stores and loads with the same
-// "sc1" cache policy (on gfx950: written through the non-coherent per-XCD L2
-// to memory, and read past it).  Each chunk drains its
-// stores (s_waitcnt vmcnt(0): a device-scope store has then reached memory)
-// before its thread 0 increments the pair's ticket with a device-scope RMW, and
-// the chunk that takes the last ticket reads the others' data with
-// device-scope loads issued after that RMW returned.  This is the ordering a
+// Logits one workgroup hands to another in the same launch (a deferred chunk
+// of a split pair, see split_tail) move through device-scope stores and loads:
+// relaxed agent-scope atomics, or buffer stores and loads with the same "sc1"
+// cache policy (on gfx950: written through the non-coherent per-XCD L2 to
+// memory, and read past it).  The writer drains its stores (s_waitcnt
+// vmcnt(0): a device-scope store has then reached memory) before it publishes
+// the word that tells the reader to look, and the reader issues its
+// device-scope loads after it has seen that word.  This is the ordering a
 // release/acquire pair would give, without the L2 write-back and invalidate
-// that only plain (non-atomic) stores and loads need.
+// that only plain (non-atomic) stores and loads need.  An unsplit pair whose
+// logits go to the workspace reads them back the same way within its own
+// workgroup (a drain, then a barrier).
 __device__ __forceinline__ void store_wt(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void store_wt(float2* p, float2 v) {
-  const unsigned long long x =
-      (unsigned long long)__float_as_uint(v.x) | ((unsigned long long)__float_as_uint(v.y) << 32);
-  __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 // 16-byte device-scope store through a buffer resource over [base, base + bytes).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t wt_rsrc(float* base, int bytes) {
@@ -261,13 +258,6 @@ __device__ __forceinline__ void store_wt4(__amdgpu_buffer_rsrc_t r, int byte_off
 // every load in flight) and gives an empty range where the data is not needed.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t coh_rsrc(const float* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, bytes, 0x00020000);
-}
-__device__ __forceinline__ float load_c1(__amdgpu_buffer_rsrc_t r, int byte_off) {
-  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 16 /* sc1 */));
-}
-__device__ __forceinline__ float2 load_c2(__amdgpu_buffer_rsrc_t r, int byte_off) {
-  const auto x = __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 16 /* sc1 */);
-  return make_float2(__uint_as_float(x[0]), __uint_as_float(x[1]));
 }
 __device__ __forceinline__ float4 load_c4(__amdgpu_buffer_rsrc_t r, int byte_off) {
   const auto x = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 16 /* sc1 */);
@@ -336,7 +326,7 @@ __device__ __forceinline__ void argmin_merge(float& s, int& i, float so, int io)
 // rows, in 16-byte cells; then ring entries (4-byte cells).  Lanes past the
 // end load a clamped valid cell into padding that nobody reads.
 template <int D, int G>
-__device__ void prefetch_tail(const StepArgs& a, int pair, float* s_pre) {
+__device__ __forceinline__ void prefetch_tail(const StepArgs& a, int pair, float* s_pre) {
   using S = Shape<BF16T, D, G>;
   typedef __attribute__((address_space(3))) void* lds_ptr;
   constexpr int QC = G * D / 8, KC = D / 8, NC = S::kPreCells;
@@ -364,23 +354,27 @@ __device__ void prefetch_tail(const StepArgs& a, int pair, float* s_pre) {
 }
 
 // LDS bitmap of the pair's protected recent slots (the ring's entries) over
-// its budget, built before the tail: cleared while the chunk partials merge,
-// then set during the ticket's round trip (a barrier between the two).
-__device__ __forceinline__ void clear_protect_bits(uint32_t* bits, int budget) {
-  for (int i = threadIdx.x; i < (budget + 31) >> 5; i += kThreads) bits[i] = 0u;
+// its budget, built before the tail: cleared while the waves' partials merge,
+// then set (a barrier between the two).
+__device__ __forceinline__ void clear_protect_bits(uint32_t* bits, int budget, int t0 = 0, int nt = kThreads) {
+  for (int i = (int)threadIdx.x - t0; i >= 0 && i < (budget + 31) >> 5; i += nt) bits[i] = 0u;
 }
+// Threads t0 .. t0 + nt - 1 set the bits (the first entries from the LDS
+// copy, the others from memory).
 template <class T, int D, int G>
-__device__ void set_protect_bits(const StepArgs& a, int pair, int budget, uint32_t* bits, const float* s_pre) {
-  const int R = a.recent, tid = threadIdx.x;
+__device__ __forceinline__ void set_protect_bits(const StepArgs& a, int pair, int budget, uint32_t* bits,
+                                                 const float* s_pre, int t0 = 0, int nt = kThreads) {
+  const int R = a.recent, tid = threadIdx.x - t0;
+  if (tid < 0) return;
   const int32_t* ring = a.ring + (size_t)pair * R;
   // bf16: the first entries were copied to LDS when the workgroup started.
   const int32_t* first =
       T::kEpl == 8 ? reinterpret_cast<const int32_t*>(s_pre + Shape<T, D, G>::kPreBlocks * 256) : ring;
-  if (tid < R) {
+  if (tid < R && tid < nt) {
     const int sl = first[tid];
     if (sl >= 0 && sl < budget) atomicOr(&bits[sl >> 5], 1u << (sl & 31));
   }
-  for (int j = tid + kThreads; j < R; j += kThreads) {
+  for (int j = tid + nt; j < R; j += nt) {
     const int sl = ring[j];
     if (sl >= 0 && sl < budget) atomicOr(&bits[sl >> 5], 1u << (sl & 31));
   }
@@ -405,35 +399,200 @@ __device__ __forceinline__ void wave_argmin(float& s, int& i) {
   i = i0;
 }
 
-// Tail of one pair: merge chunk partials, output, importance, argmin, insert.
-// Every workspace load (chunk statistics and partials, the first logits) is
-// issued at once at the start, so the tail costs about one memory round trip
-// plus arithmetic; the new token's rows and the ring are already in LDS
-// (s_pre) and the bitmap of protected slots was built before the tail.
-// s_part: this workgroup's merged partial ([G][D + 2], used when nchunk == 1);
-// s_tail: the region after the merge area holds the bitmap and the argmin
-// candidates (Shape::kBitsOffset).
+// Exchange words between the chunks of a split pair: the value's bits in the
+// low half, the pair's epoch of the step that wrote it in the high half.  They
+// are written and read as single 64-bit device-scope atomics (relaxed, agent
+// scope), so a reader sees either the previous step's word or this step's,
+// never a mix, and tells them apart by the epoch; no store needs to be drained
+// before another workgroup may look.
+__device__ __forceinline__ uint64_t xword(uint32_t bits, uint32_t epoch) {
+  return (static_cast<uint64_t>(epoch) << 32) | bits;
+}
+__device__ __forceinline__ uint64_t xword(float v, uint32_t epoch) { return xword(__float_as_uint(v), epoch); }
+__device__ __forceinline__ void xstore(uint64_t* p, uint64_t w) {
+  __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t xload(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool xfresh(uint64_t w, uint32_t epoch) { return static_cast<uint32_t>(w >> 32) == epoch; }
+__device__ __forceinline__ float xval(uint64_t w) { return __uint_as_float(static_cast<uint32_t>(w)); }
+
+// Reductions over the wave by DPP within rows of 16 lanes, a lane swizzle
+// across rows and a swap of the wave's halves: every step combines a lane's
+// value with its partner's by a commutative operation, so every lane ends
+// with the same bits, and the order is fixed by the layout alone.
+template <class Op>
+__device__ __forceinline__ float wave_reduce(float x, Op op) {
+  x = row_reduce16(x, op);
+  x = op(x, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F)));  // lane ^ 16
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return op(__uint_as_float(sw[0]), __uint_as_float(sw[1]));  // lane ^ 32
+}
+__device__ __forceinline__ float wave_max(float x) {
+  return wave_reduce(x, [](float u, float v) { return fmaxf(u, v); });
+}
+__device__ __forceinline__ float wave_sum(float x) {
+  return wave_reduce(x, [](float u, float v) { return u + v; });
+}
+
+// Importance of the 4 slots base .. base + 3 from their logits lv[h] (log2
+// domain after the factor ls), with the step's max M and 1 / normaliser per
+// head; masked (filled, past the sink window, not among the recent slots) into
+// the running first-index minimum.  Optionally exports every filled slot's
+// score.
+template <int G>
+__device__ __forceinline__ void score4(int base, const float4 (&lv)[G], const float (&M)[G], const float (&invL)[G],
+                                       float ls, const uint32_t* s_bits, int sink, int len, float* dbg, float& best,
+                                       int& besti) {
+  const uint32_t bits = s_bits[base >> 5] >> (base & 31);
+  float sc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    sc[0] = fmaf(fast_exp2(fmaf(lv[h].x, ls, -M[h])), invL[h], sc[0]);
+    sc[1] = fmaf(fast_exp2(fmaf(lv[h].y, ls, -M[h])), invL[h], sc[1]);
+    sc[2] = fmaf(fast_exp2(fmaf(lv[h].z, ls, -M[h])), invL[h], sc[2]);
+    sc[3] = fmaf(fast_exp2(fmaf(lv[h].w, ls, -M[h])), invL[h], sc[3]);
+  }
+  if (dbg) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (base + j < len) dbg[base + j] = sc[j];
+  }
+  // Branch-free masked minimum; slots increase per thread, so the strict
+  // comparison keeps the first index on ties.
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = base + j;
+    const bool ok = i < len && i >= sink && !((bits >> j) & 1u);
+    const float v = ok ? sc[j] : INFINITY;
+    const bool lt = v < best;
+    best = lt ? v : best;
+    besti = lt ? i : besti;
+  }
+}
+
+// Logit of the incoming token for every head of the group (every lane holds
+// all of them), from q and k_new (bf16: the copies made in LDS at workgroup
+// start; fp32: global memory).  bf16 logits are the raw q.k times scale log2 e,
+// fp32 q comes pre-multiplied.
 template <class T, int D, int G>
-__device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const float* s_part, float* s_tail,
+__device__ __forceinline__ void new_token_logits(const StepArgs& a, int pair, const float* s_pre, QReg<T, G>& q, uint4& kn,
+                                 float (&snew)[G]) {
+  using elem = typename T::elem;
+  using S = Shape<T, D, G>;
+  constexpr int EPL = S::kEpl, LPR = S::kLpr;
+  const int lane = threadIdx.x & 63;
+  const int b = pair / a.n_kv_heads, g = pair - b * a.n_kv_heads;
+  const elem* pre = reinterpret_cast<const elem*>(s_pre);
+  const elem* qsrc = T::kEpl == 8 ? pre : static_cast<const elem*>(a.q) + ((size_t)b * a.n_q_heads + (size_t)g * G) * D;
+  const elem* knsrc = T::kEpl == 8 ? pre + G * D : static_cast<const elem*>(a.k_new) + (size_t)pair * D;
+  const int c = lane % LPR;
+  load_q<T, G>(q, qsrc + c * EPL, D, a.scale_log2);
+  kn = *reinterpret_cast<const uint4*>(knsrc + c * EPL);
+  const float post_scale = T::kEpl == 8 ? a.scale_log2 : 1.0f;
+#pragma unroll
+  for (int h = 0; h < G; ++h) snew[h] = row_sum<LPR>(qk_part<T, G>(q, h, kn)) * post_scale;
+}
+
+// Stores the incoming token: appended while the cache fills, else written
+// over the victim slot (besti, or nothing when no slot was a candidate: a full
+// LF_SCORE_NONE cache); then the ring entry, position, fill level and the
+// evicted index.  Run by the threads of wave 0 (2 kVec <= 64 of them copy the
+// row).  `ins` is this thread's 16-byte piece of the k_new / v_new rows.
+template <class T, int D>
+__device__ __forceinline__ void insert_token(const StepArgs& a, int pair, const PairMeta& pm, int besti, const uint4& ins,
+                             bool split) {
+  using elem = typename T::elem;
+  constexpr int kVec = D * sizeof(elem) / 16;  // 16-byte pieces of one K/V row
+  const int tid = threadIdx.x, t = pm.t, len = pm.len, budget = pm.budget, R = a.recent;
+  int e, ev;
+  if (len < budget) {
+    e = len;
+    ev = -1;
+  } else if (besti < budget) {
+    e = besti;
+    ev = besti;
+  } else {
+    e = -1;  // not stored: score_none on a full cache (validation guarantees a candidate otherwise)
+    ev = -2;
+  }
+  if (e >= 0 && tid < 2 * kVec) {
+    const int which = tid / kVec, part = tid - which * kVec;
+    const size_t pair_off = (size_t)pair * a.max_budget * D;
+    reinterpret_cast<uint4*>(static_cast<elem*>(which ? a.v_cache : a.k_cache) + pair_off + (size_t)e * D)[part] =
+        ins;
+  }
+  if (tid == 0) {
+    PairMeta* meta = a.meta + pair;
+    if (e >= 0) {
+      if (R > 0) a.ring[(size_t)pair * R + t % R] = e;
+      meta->t = t + 1;
+      meta->len = len < budget ? len + 1 : budget;
+    }
+    a.evict_idx[pair] = ev;
+    if (split) {
+      // Next step's epoch (never 0, so zeroed exchange words never look
+      // fresh) and the pair's chunk counter back to 0.
+      meta->epoch = pm.epoch + 1u == 0u ? 1u : pm.epoch + 1u;
+      a.count[pair] = 0u;
+    }
+  }
+}
+
+// This thread's 16-byte piece of the k_new / v_new rows for insert_token
+// (bf16: from the LDS copy; fp32: global memory).
+template <class T, int D, int G>
+__device__ __forceinline__ uint4 insert_piece(const StepArgs& a, int pair, const float* s_pre) {
+  using elem = typename T::elem;
+  constexpr int kVec = D * sizeof(elem) / 16;
+  const int c = min((int)threadIdx.x, 2 * kVec - 1), which = c / kVec, part = c - which * kVec;
+  const elem* src = T::kEpl == 8 ? reinterpret_cast<const elem*>(s_pre) + (G + which) * D
+                                 : static_cast<const elem*>(which ? a.v_new : a.k_new) + (size_t)pair * D;
+  return reinterpret_cast<const uint4*>(src)[part];
+}
+
+// Workgroup-wide lexicographic (score, slot) minimum: waves reduce with DPP,
+// then through LDS (s_arg: [kWaves] scores, [kWaves] slots) with one barrier.
+// Every thread gets the result.
+__device__ __forceinline__ void block_argmin(float& best, int& besti, float* s_arg) {
+  const int lane = threadIdx.x & 63, wave = wave_index();
+  wave_argmin(best, besti);
+  if (lane == 0) {
+    s_arg[wave] = best;
+    reinterpret_cast<int*>(s_arg)[kWaves + wave] = besti;
+  }
+  __syncthreads();
+  float sw[kWaves];
+  int iw[kWaves];
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {  // all reads first, one wait
+    sw[w] = s_arg[w];
+    iw[w] = reinterpret_cast<int*>(s_arg)[kWaves + w];
+  }
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) argmin_merge(best, besti, sw[w], iw[w]);
+}
+
+// Tail of an unsplit pair (its one chunk is this workgroup): output,
+// importance, argmin, insert.  The merged partial is in s_part [G][D + 2];
+// the logits are in the streaming waves' LDS buffers (fp32 or half precision)
+// or, when they did not fit, in the workspace (issued at once at the start, so
+// the tail costs about one memory round trip plus arithmetic).  The new
+// token's rows and the ring are already in LDS (s_pre) and the bitmap of
+// protected slots was built before the tail.  s_tail: the region after the
+// merge area holds the bitmap and the argmin candidates (Shape::kBitsOffset).
+template <class T, int D, int G>
+__device__ __forceinline__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const float* s_part, float* s_tail,
                           const float* s_logit, int lmode, const float* s_pre) {
   using elem = typename T::elem;
   constexpr int kOut = (G * D + kThreads - 1) / kThreads;  // output elements per thread
-  constexpr int kCB = G <= 4 ? 8 : 4;                       // chunk partials loaded per batch
-  constexpr int kVec = D * sizeof(elem) / 16;               // 16-byte pieces of one K/V row
-  // float4 logit cells per head preloaded (more when the register budget is
-  // sized for one wave per SIMD).  Every cell past the budget is a wasted
-  // load in the tail's first round trip: 2048 slots for G = 3, 4 and 1024
-  // for G >= 5 cover the split shapes measured (B8 budget 2048 G 4: 18.43 ->
-  // 18.26 us against twice as many; B16 budget 1024 G 7: 14.80 -> 14.62 us).
+  // float4 logit cells per head preloaded from the workspace (more when the
+  // register budget is sized for one wave per SIMD).
   constexpr int kPre = Shape<T, D, G>::kMinWavesPerSimd == 1 ? 32 / G : (G <= 2 ? 8 : 8 / G);
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
-  PairMeta* meta = a.meta + pair;
   const int b = pair / a.n_kv_heads, g = pair - b * a.n_kv_heads;
-  const int t = pm.t, len = pm.len, budget = pm.budget;
-  const int nchunk = pm.nchunk, item0 = pm.item0, lstride = pm.lstride;
-  const int R = a.recent;
-  const int ring_pos = R > 0 ? t % R : 0;  // ring entry the incoming token takes
-  const bool split = nchunk > 1;
+  const int len = pm.len, budget = pm.budget, lstride = pm.lstride;
   const size_t pair_off = (size_t)pair * a.max_budget * D;
 
   const uint32_t* s_bits = reinterpret_cast<const uint32_t*>(s_tail + Shape<T, D, G>::kBitsOffset);  // protected slots
@@ -444,31 +603,10 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
   // back and one wait covers them; out-of-range lanes are masked where used.
   using S = Shape<T, D, G>;
   constexpr int EPL = S::kEpl, LPR = S::kLpr;
-  // bf16: q, k_new, v_new and the first ring entries were copied to s_pre when
-  // the workgroup started (prefetch_tail).
-  constexpr bool kPre16 = T::kEpl == 8;
-  const elem* pre = reinterpret_cast<const elem*>(s_pre);
-  const elem* qsrc = kPre16 ? pre : static_cast<const elem*>(a.q) + ((size_t)b * a.n_q_heads + (size_t)g * G) * D;
-  const elem* knsrc = kPre16 ? pre + G * D : static_cast<const elem*>(a.k_new) + (size_t)pair * D;
-  const elem* vnsrc = kPre16 ? pre + (G + 1) * D : static_cast<const elem*>(a.v_new) + (size_t)pair * D;
-  QReg<T, G> q;
-  uint4 kn;
-  {
-    const int c = lane % LPR;
-    load_q<T, G>(q, qsrc + c * EPL, D, a.scale_log2);
-    kn = *reinterpret_cast<const uint4*>(knsrc + c * EPL);
-  }
-  // Chunk partials exist only for a split pair; logits are read from memory
-  // unless the pair kept them in LDS.
-  const auto ml_rs = coh_rsrc(a.part_ml + (size_t)item0 * G * 2, split ? nchunk * G * 8 : 0);
-  const auto pa_rs = coh_rsrc(a.part_acc + (size_t)item0 * G * D, split ? nchunk * G * D * 4 : 0);
   const auto lg_rs = coh_rsrc(a.logits + (size_t)pm.slot0 * G, lmode != kLogitsOut || a.score_none ? 0 : G * lstride * 4);
-  uint4 ins;
-  {
-    const int c = min(tid, 2 * kVec - 1), which = c / kVec, part = c - which * kVec;
-    ins = reinterpret_cast<const uint4*>(which ? vnsrc : knsrc)[part];
-  }
-  const elem* vnp = vnsrc;
+  const uint4 ins = insert_piece<T, D, G>(a, pair, s_pre);
+  const elem* vnp = T::kEpl == 8 ? reinterpret_cast<const elem*>(s_pre) + (G + 1) * D
+                                 : static_cast<const elem*>(a.v_new) + (size_t)pair * D;
   float vnv[kOut];
 #pragma unroll
   for (int o = 0; o < kOut; ++o) vnv[o] = load_elem<T>(vnp, min(tid + o * kThreads, G * D - 1) % D);
@@ -477,142 +615,50 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
   // weight-times-norm product is one exp2.
   const float ls = T::kEpl == 8 && !a.vl1 ? a.scale_log2 : 1.0f;
   auto logit4 = [&](int h, int base) { return load_c4(lg_rs, (h * lstride + base) * 4); };
-  // Every workspace value the tail needs first is requested here at once: the
-  // chunk partials and the first kPre * 4 * kThreads slots' logits (all of
-  // them for budgets up to that).  A pair that kept its logits in LDS needs
-  // none of them: it skips the block, which leaves its waits below with
-  // nothing to wait for.
-  // Chunk statistics, packed: lane 16 r + c holds, for pass k, head 4 k + r of
-  // chunks c, c + 16, c + 32, c + 48 (j = 0..3).
-  constexpr int KP = (G + 3) / 4;
-  const int prow = lane >> 4, pcol = lane & 15;
-  float2 ml[KP][4];
-  float pa[kOut][kCB];
+  // The first kPre * 4 * kThreads slots' logits are requested here at once
+  // when the pair's logits went to the workspace (an empty range otherwise).
   float4 lvp[kPre][G];
   if (lmode == kLogitsOut) {
-#pragma unroll
-    for (int k = 0; k < KP; ++k)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) ml[k][j] = load_c2(ml_rs, ((pcol + 16 * j) * G + min(4 * k + prow, G - 1)) * 8);
-#pragma unroll
-    for (int o = 0; o < kOut; ++o) {
-      const int idx = min(tid + o * kThreads, G * D - 1);
-#pragma unroll
-      for (int k = 0; k < kCB; ++k) pa[o][k] = load_c1(pa_rs, (k * G * D + idx) * 4);
-    }
 #pragma unroll
     for (int p = 0; p < kPre; ++p) {
       const int base = min(4 * (tid + p * kThreads), lstride - 4);
 #pragma unroll
       for (int h = 0; h < G; ++h) lvp[p][h] = logit4(h, base);
     }
-  } else {
-#pragma unroll
-    for (int k = 0; k < KP; ++k)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) ml[k][j] = make_float2(0.f, 0.f);
-#pragma unroll
-    for (int o = 0; o < kOut; ++o)
-#pragma unroll
-      for (int k = 0; k < kCB; ++k) pa[o][k] = 0.f;
   }
-  // ---- global max and normaliser over the chunks and the incoming token.
-  // Every wave computes them itself, lane c holding chunk c (the own merged
-  // partial in lane 0 for an unsplit pair): no LDS exchange, no barrier.  The
-  // reductions give every lane, and every wave, the same bits.
-  // Logit of the incoming token (every lane of a row lineage holds it).
+  QReg<T, G> q;
+  uint4 kn;
   float snew[G];
-  {
-    const float post_scale = T::kEpl == 8 ? a.scale_log2 : 1.0f;
+  new_token_logits<T, D, G>(a, pair, s_pre, q, kn, snew);
+  // ---- global max and normaliser: the chunk's merged partial and the
+  // incoming token (every thread computes them itself).
+  float M[G], invL[G], en[G], w0[G];
 #pragma unroll
-    for (int h = 0; h < G; ++h) snew[h] = row_sum<LPR>(qk_part<T, G>(q, h, kn)) * post_scale;
-  }
-  // Row reductions (16 lanes) over the packed chunk statistics: one pass
-  // serves four heads.  Results are read back per head with readlane, so every
-  // wave holds the same values.
-  float M[G], invL[G], en[G];
-  float wp[KP][4];  // lane (r, c), slot j: weight exp2(m - M) of chunk c + 16 j for head 4 k + r
-#pragma unroll
-  for (int k = 0; k < KP; ++k) {
-    const int h = 4 * k + prow;
-    float sn = snew[0];
-#pragma unroll
-    for (int hh = 1; hh < G; ++hh) sn = h == hh ? snew[hh] : sn;
-    float mcj[4], lcj[4];
-    float mx = kNegBig;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c = pcol + 16 * j;
-      const bool own = h < G && (split ? c < nchunk : c == 0);
-      mcj[j] = own ? (split ? ml[k][j].x : s_part[min(h, G - 1) * (D + 2) + D]) : kNegBig;
-      lcj[j] = own ? (split ? ml[k][j].y : s_part[min(h, G - 1) * (D + 2) + D + 1]) : 0.f;
-      mx = fmaxf(mx, mcj[j]);
-    }
-    const float Mh = fmaxf(row_reduce16(mx, [](float u, float v) { return fmaxf(u, v); }), sn);
-    float ls4 = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      wp[k][j] = fast_exp2(mcj[j] - Mh);  // 0 without a chunk
-      ls4 = fmaf(lcj[j], wp[k][j], ls4);
-    }
-    const float enh = fast_exp2(sn - Mh);
-    const float Lh = row_reduce16(ls4, [](float u, float v) { return u + v; }) + enh;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if (4 * k + r < G) {
-        M[4 * k + r] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Mh), 16 * r));
-        en[4 * k + r] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(enh), 16 * r));
-        const float L = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Lh), 16 * r));
-        invL[4 * k + r] = 1.0f / L;
-        if (tid == 0 && a.dbg_lse)
-          a.dbg_lse[(size_t)b * a.n_q_heads + g * G + 4 * k + r] = (M[4 * k + r] + __log2f(L)) * 0.6931471805599453f;
-      }
-    }
+  for (int h = 0; h < G; ++h) {
+    const float mp = s_part[h * (D + 2) + D], lp = s_part[h * (D + 2) + D + 1];
+    M[h] = fmaxf(mp, snew[h]);
+    w0[h] = fast_exp2(mp - M[h]);
+    en[h] = fast_exp2(snew[h] - M[h]);
+    const float L = lp * w0[h] + en[h];
+    invL[h] = 1.0f / L;
+    if (tid == 0 && a.dbg_lse) a.dbg_lse[(size_t)b * a.n_q_heads + g * G + h] = (M[h] + __log2f(L)) * 0.6931471805599453f;
   }
 
-  // ---- output: chunk partials in chunk order + the new token, normalised
+  // ---- output: the partial + the new token, normalised
 #pragma unroll
   for (int o = 0; o < kOut; ++o) {
     const int idx = tid + o * kThreads;
     if (idx < G * D) {
       const int h = idx / D;
-      // h is the same on the whole wave (D is a multiple of 64), so lane c's
-      // weight for head h is chunk c's, read with readlane.
-      float enh = en[0], il = invL[0];
+      float enh = en[0], il = invL[0], wh = w0[0];
 #pragma unroll
       for (int hh = 1; hh < G; ++hh) {
         enh = h == hh ? en[hh] : enh;
         il = h == hh ? invL[hh] : il;
+        wh = h == hh ? w0[hh] : wh;
       }
-      // Chunk c's weight for head h: lane 16 (h % 4) + c % 16, slot c / 16, pass h / 4.
-      float wj[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        wj[j] = wp[0][j];
-#pragma unroll
-        for (int k = 1; k < KP; ++k) wj[j] = (h >> 2) == k ? wp[k][j] : wj[j];
-      }
-      const int wbase = 16 * (h & 3);
-      auto wchunk = [&](int c) {
-        const float w = (c >> 4) == 0 ? wj[0] : (c >> 4) == 1 ? wj[1] : (c >> 4) == 2 ? wj[2] : wj[3];
-        return __builtin_amdgcn_readlane(__float_as_int(w), wbase + (c & 15));
-      };
       float acc = enh * vnv[o];
-      if (!split) {
-        acc = fmaf(s_part[h * (D + 2) + idx - h * D], __int_as_float(wchunk(0)), acc);
-      } else {
-#pragma unroll
-        for (int k = 0; k < kCB; ++k)
-          if (k < nchunk) acc = fmaf(pa[o][k], __int_as_float(wchunk(k)), acc);
-        for (int ci = kCB; ci < nchunk; ci += kCB) {
-          float x[kCB];
-#pragma unroll
-          for (int k = 0; k < kCB; ++k) x[k] = load_c1(pa_rs, ((ci + k) * G * D + idx) * 4);
-#pragma unroll
-          for (int k = 0; k < kCB; ++k)
-            if (ci + k < nchunk) acc = fmaf(x[k], __int_as_float(wchunk(ci + k)), acc);
-        }
-      }
+      acc = fmaf(s_part[h * (D + 2) + idx - h * D], wh, acc);
       store_elem<T>(a.out, ((size_t)b * a.n_q_heads + g * G + h) * D + idx - h * D, acc * il);
     }
   }
@@ -624,33 +670,6 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
   // every slot, so a full cache stores nothing.
   if (!a.score_none) {
     float* dbg = a.dbg_scores ? a.dbg_scores + (size_t)pair * a.max_budget : nullptr;
-    auto score4 = [&](int base, const float4(&lv)[G]) {
-      const uint32_t bits = s_bits[base >> 5] >> (base & 31);
-      float sc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        sc[0] = fmaf(fast_exp2(fmaf(lv[h].x, ls, -M[h])), invL[h], sc[0]);
-        sc[1] = fmaf(fast_exp2(fmaf(lv[h].y, ls, -M[h])), invL[h], sc[1]);
-        sc[2] = fmaf(fast_exp2(fmaf(lv[h].z, ls, -M[h])), invL[h], sc[2]);
-        sc[3] = fmaf(fast_exp2(fmaf(lv[h].w, ls, -M[h])), invL[h], sc[3]);
-      }
-      if (dbg) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (base + j < len) dbg[base + j] = sc[j];
-      }
-      // Branch-free masked minimum; i increases per thread, so the strict
-      // comparison keeps the first index on ties.
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i = base + j;
-        const bool ok = i < len && i >= a.sink && !((bits >> j) & 1u);
-        const float v = ok ? sc[j] : INFINITY;
-        const bool lt = v < best;
-        best = lt ? v : best;
-        besti = lt ? i : besti;
-      }
-    };
     // Exact importance of slot i from its key row, on the LPR lanes of one row
     // lineage (every lane of the lineage gets the same value).
     // (key_row issues the loads, exact_score takes them, so that several
@@ -697,7 +716,7 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
         float4 lv[G];
 #pragma unroll
         for (int h = 0; h < G; ++h) lv[h] = *reinterpret_cast<const float4*>(src + h * LR);
-        score4(base, lv);
+        score4<G>(base, lv, M, invL, ls, s_bits, a.sink, len, dbg, best, besti);
       }
     } else if (lmode == kLogitsHalf) {
       if constexpr (T::kEpl == 8) {
@@ -820,60 +839,591 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
 #pragma unroll
       for (int p = 0; p < kPre; ++p)
         if (4 * (tid + p * kThreads) < len)
-          score4(4 * (tid + p * kThreads), lvp[p]);
+          score4<G>(4 * (tid + p * kThreads), lvp[p], M, invL, ls, s_bits, a.sink, len, dbg, best, besti);
 #pragma unroll 2
       for (int base = 4 * (tid + kPre * kThreads); base < len; base += 4 * kThreads) {
         float4 lv[G];
 #pragma unroll
         for (int h = 0; h < G; ++h) lv[h] = logit4(h, base);
-        score4(base, lv);
+        score4<G>(base, lv, M, invL, ls, s_bits, a.sink, len, dbg, best, besti);
       }
     }
-    wave_argmin(best, besti);
-    if (lane == 0) {
-      s_arg[wave] = best;
-      reinterpret_cast<int*>(s_arg)[kWaves + wave] = besti;
-    }
-    __syncthreads();
-    {
-      float sw[kWaves];
-      int iw[kWaves];
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {  // all reads first, one wait
-        sw[w] = s_arg[w];
-        iw[w] = reinterpret_cast<int*>(s_arg)[kWaves + w];
-      }
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) argmin_merge(best, besti, sw[w], iw[w]);
-    }
+    block_argmin(best, besti, s_arg);
   }
+  if (wave == 0) insert_token<T, D>(a, pair, pm, besti, ins, false);
+}
 
-  // ---- insert the incoming token: append while filling, else overwrite the victim
-  int e, ev;
-  if (len < budget) {
-    e = len;
-    ev = -1;
-  } else if (besti < budget) {
-    e = besti;
-    ev = besti;
-  } else {
-    e = -1;  // not stored: score_none on a full cache (no evictable slot is prevented by validation)
-    ev = -2;
+// ---------------------------------------------------------------------------
+// Split pairs.  The chunks of a pair are separate workgroups of the same
+// launch.  Each keeps its rows' logits on chip and publishes its merged
+// partial (weighted value sums, then max and sum per head) as exchange words.
+// Every chunk then waits, for a bounded time, until all chunks of its pair
+// have published their statistics, computes the step's global max and
+// normaliser per head itself (the same bits in every chunk), scores its own
+// slots from its on-chip logits, takes their masked argmin and publishes it as
+// its candidate; the output rows of head h are written by chunk h mod nchunk.
+// A chunk that stops waiting (its pair's chunks did not all run at the same
+// time), or whose logits did not stay on chip (fp32 streaming, long chunks),
+// is deferred: it writes its logits to the workspace, waits for those stores
+// to complete, and publishes a deferred candidate.  Every chunk then takes a
+// ticket on the pair's counter (a relaxed device-scope fetch-add); the chunk
+// taking the last one finishes the pair: it reads every chunk's candidate
+// (each was stored before its chunk's ticket, so waiting for it ends), scores
+// the deferred chunks' slots and writes their output rows, and inserts the
+// incoming token.  The finisher only waits for words whose stores were already
+// issued, and a chunk never waits without a bound for a chunk that may not
+// have started: the result never depends on how the chunks were scheduled.
+// Those waits for issued stores still stop after kSafetyTicks and record a
+// fault bit in the state header (reported by lf_check_state) rather than hang
+// the GPU, should the protocol ever be broken.
+// ---------------------------------------------------------------------------
+
+// A chunk's own (max, sum) of head h from its waves' partials ([wave][G][D + 2]
+// in s_part_w): the same bits wherever it is computed.
+template <int D, int G>
+__device__ __forceinline__ void chunk_stat(const float* s_part_w, int h, float& mm, float& sl) {
+  mm = kNegBig;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) mm = fmaxf(mm, s_part_w[(w * G + h) * (D + 2) + D]);
+  sl = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const float* src = s_part_w + (w * G + h) * (D + 2);
+    sl = fmaf(src[D + 1], fast_exp2(src[D] - mm), sl);
   }
-  if (e >= 0 && tid < 2 * kVec) {
-    const int which = tid / kVec, part = tid - which * kVec;
-    reinterpret_cast<uint4*>(static_cast<elem*>(which ? a.v_cache : a.k_cache) + pair_off + (size_t)e * D)[part] =
-        ins;
-  }
-  if (tid == 0) {
-    if (e >= 0) {
-      if (R > 0) a.ring[(size_t)pair * R + ring_pos] = e;
-      meta->t = t + 1;
-      meta->len = len < budget ? len + 1 : budget;
+}
+
+// Per wave: waits until every chunk of the pair has published this step's
+// (max, sum) of every head (giving up after `deadline` if `bounded`; else
+// `deadline` is only the safety bound, after which a fault bit is set), then
+// the global max M_h and normaliser L_h over the chunks and the incoming
+// token; lane c keeps chunk c's weight exp2(m_c,h - M_h) in wl[h].  Lane
+// `own` (this chunk, or -1) computes its values from this workgroup's wave
+// partials (s_part_w, LDS) instead of reading memory: its own words may not
+// be visible to it yet.  Every wave
+// of every chunk computes the same bits.
+template <int D, int G>
+__device__ __forceinline__ bool pair_stats(const StepArgs& a, int item0, int nchunk, uint32_t epoch, const float (&snew)[G],
+                           int own, const float* s_part_w, bool bounded, uint64_t deadline, float (&M)[G],
+                           float (&L)[G], float (&wl)[G]) {
+  const int lane = threadIdx.x & 63;
+  const bool mine = lane < nchunk && lane != own;
+  const uint64_t* cell = a.xcell + (size_t)(item0 + (lane < nchunk ? lane : 0)) * G * (D + 2) + D;
+  uint64_t mw[G], lw[G];
+  for (;;) {
+    bool ok = true;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      mw[h] = xload(cell + h * (D + 2));
+      lw[h] = xload(cell + h * (D + 2) + 1);
     }
-    a.evict_idx[pair] = ev;
-    meta->ticket = 0u;
+#pragma unroll
+    for (int h = 0; h < G; ++h) ok = ok && xfresh(mw[h], epoch) && xfresh(lw[h], epoch);
+    if (!__builtin_amdgcn_ballot_w64(mine && !ok)) break;
+    const uint64_t now = __builtin_amdgcn_s_memrealtime();
+    if (now > deadline) {
+      if (bounded) return false;
+      if (lane == 0) __hip_atomic_fetch_or(a.fault, kFaultStats, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
   }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    // The product is rounded before the butterfly (no contraction into an
+    // FMA, which would round differently in a lane and in its partner).
+#pragma clang fp contract(off)
+    float om = 0.f, ol = 0.f;
+    if (own >= 0) chunk_stat<D, G>(s_part_w, h, om, ol);
+    const bool me = lane == own;
+    const float m = lane < nchunk ? (me ? om : xval(mw[h])) : kNegBig;
+    const float l = lane < nchunk ? (me ? ol : xval(lw[h])) : 0.f;
+    const float Mh = fmaxf(wave_max(m), snew[h]);
+    const float w = fast_exp2(m - Mh);  // 0 past the chunks
+    M[h] = Mh;
+    wl[h] = w;
+    L[h] = wave_sum(l * w) + fast_exp2(snew[h] - Mh);
+  }
+  return true;
+}
+
+// Reduction over aligned groups of 2^k lanes (k <= 6) with the same pairing
+// order as wave_reduce: a group's lanes end with the same bits, and lanes of
+// a group beyond its values add nothing (0 for sums, kNegBig for maxima), so
+// the result equals wave_reduce over a wave holding only that group's values.
+template <class Op>
+__device__ __forceinline__ float group_reduce(float x, int k, Op op) {
+  if (k >= 1) x = op(x, dpp<0xB1>(x));   // lane ^ 1
+  if (k >= 2) x = op(x, dpp<0x4E>(x));   // lane ^ 2
+  if (k >= 3) x = op(x, dpp<0x141>(x));  // half-row mirror
+  if (k >= 4) x = op(x, dpp<0x140>(x));  // row mirror
+  if (k >= 5) x = op(x, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F)));  // lane ^ 16
+  if (k >= 6) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = op(__uint_as_float(sw[0]), __uint_as_float(sw[1]));  // lane ^ 32
+  }
+  return x;
+}
+
+// pair_stats with lane h * 2^k + c holding (head h, chunk c), 2^k >= nchunk,
+// 2^k * G <= 64: one segmented reduction serves every head.  The lane's head
+// gets Mh and Lh, the lane's chunk weight exp2(m_c,h - M_h) goes to w.  Same
+// bits as pair_stats (the same pairings, the extra lanes adding nothing).
+template <int D, int G>
+__device__ __forceinline__ bool pair_stats_hc(const StepArgs& a, int item0, int nchunk, int k, uint32_t epoch,
+                                              const float* s_snew, int own, const float* s_part_w, bool bounded,
+                                              uint64_t deadline, float& Mh, float& Lh, float& w) {
+  const int lane = threadIdx.x & 63;
+  const int h = lane >> k, c = lane & ((1 << k) - 1);
+  const bool valid = h < G && c < nchunk;
+  const bool mine = valid && c != own;
+  const uint64_t* cell = a.xcell + ((size_t)(item0 + (valid ? c : 0)) * G + (valid ? h : 0)) * (D + 2) + D;
+  uint64_t mw, lw;
+  for (;;) {
+    mw = xload(cell);
+    lw = xload(cell + 1);
+    const bool ok = xfresh(mw, epoch) && xfresh(lw, epoch);
+    if (!__builtin_amdgcn_ballot_w64(mine && !ok)) break;
+    if (__builtin_amdgcn_s_memrealtime() > deadline) {
+      if (bounded) return false;
+      if (lane == 0) __hip_atomic_fetch_or(a.fault, kFaultStats, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+  }
+  const float sn = s_snew[h < G ? h : 0];  // the incoming token's logit for the lane's head (LDS)
+  {
+    // The product is rounded before the reduction (no contraction into an
+    // FMA, which would round differently in a lane and in its partner).
+#pragma clang fp contract(off)
+    const bool me = c == own;
+    float om = 0.f, ol = 0.f;
+    if (own >= 0) chunk_stat<D, G>(s_part_w, h < G ? h : 0, om, ol);
+    const float m = valid ? (me ? om : xval(mw)) : kNegBig;
+    const float l = valid ? (me ? ol : xval(lw)) : 0.f;
+    Mh = fmaxf(group_reduce(m, k, [](float u, float v) { return fmaxf(u, v); }), sn);
+    w = fast_exp2(m - Mh);  // 0 past the chunks
+    Lh = group_reduce(l * w, k, [](float u, float v) { return u + v; }) + fast_exp2(sn - Mh);
+  }
+  return true;
+}
+
+// The statistics of a split pair for every head, every lane holding all of
+// them: M[h], L[h], and in lane c chunk c's weight wl[h] for head h when the
+// (head, chunk) layout is used (else per head, see pair_stats).
+template <int D, int G>
+__device__ __forceinline__ bool pair_stats_all(const StepArgs& a, int item0, int nchunk, uint32_t epoch,
+                                               const float (&snew)[G], const float* s_snew, int own,
+                                               const float* s_part_w, bool bounded, uint64_t deadline, float (&M)[G],
+                                               float (&L)[G], float (&invL)[G], float (&wl)[G]) {
+  int k = 0;
+  while ((1 << k) < nchunk) ++k;
+  if ((G << k) > 64) {
+    if (!pair_stats<D, G>(a, item0, nchunk, epoch, snew, own, s_part_w, bounded, deadline, M, L, wl)) return false;
+#pragma unroll
+    for (int h = 0; h < G; ++h) invL[h] = 1.0f / L[h];
+    return true;
+  }
+  float Mh, Lh, w;
+  if (!pair_stats_hc<D, G>(a, item0, nchunk, k, epoch, s_snew, own, s_part_w, bounded, deadline, Mh, Lh, w))
+    return false;
+  const int lane = threadIdx.x & 63;
+  const float il = 1.0f / Lh;  // one division per lane, read back per head
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    M[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Mh), h << k));
+    L[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Lh), h << k));
+    invL[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(il), h << k));
+    wl[h] = __shfl(w, (h << k) + (lane & ((1 << k) - 1)));  // lane c < 2^k takes (h, c)'s weight
+  }
+  return true;
+}
+
+// Output rows of the heads in `heads` (bit h): every chunk's weighted value
+// sum of head h, in chunk order, with weight wfn(h, k, c) = exp2(m_c,h - M_h)
+// (k: the head's rank in `heads`), plus the incoming token's value, over the
+// normaliser.  The value sums are exchange words of chunks whose statistics
+// were seen, so their stores were issued and waiting for them ends.  Also the
+// log-normaliser of those heads for the debug export.  Heads go to the
+// highest waves first, so wave 0 is the last to be busy here.
+template <class T, int D, int G, class WFn>
+__device__ __forceinline__ void split_output(const StepArgs& a, int pair, int item0, int nchunk, uint32_t epoch,
+                                             uint32_t heads, const float (&M)[G], const float (&L)[G],
+                                             const float (&invL)[G], const float (&snew)[G], const float* s_pre, int t0,
+                                             WFn wfn) {
+  using elem = typename T::elem;
+  const int kHeadsPerPass = (kThreads - t0) / D;  // threads t0 ..: D divides 64, a wave works on one head
+  const int tid = threadIdx.x - t0;
+  if (tid < 0 || kHeadsPerPass == 0) return;
+  const int b = pair / a.n_kv_heads, g = pair - b * a.n_kv_heads;
+  const int dim = tid % D;
+  const elem* vnp = T::kEpl == 8 ? reinterpret_cast<const elem*>(s_pre) + (G + 1) * D
+                                 : static_cast<const elem*>(a.v_new) + (size_t)pair * D;
+  const int slot = (kThreads - t0 - 1 - tid) / D;  // this wave's share: heads of rank slot, slot + kHeadsPerPass, ...
+  if (slot >= kHeadsPerPass) return;
+  // Heads unrolled, so each one's statistics are read at a fixed index.
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    if (!((heads >> h) & 1u)) continue;
+    const int k = __builtin_popcount(heads & ((1u << h) - 1u));  // rank of h in the set
+    if (k % kHeadsPerPass != slot) continue;
+    float acc = fast_exp2(snew[h] - M[h]) * load_elem<T>(vnp, dim);
+    for (int c0 = 0; c0 < nchunk; c0 += 8) {
+      uint64_t x[8];
+      const uint64_t deadline = __builtin_amdgcn_s_memrealtime() + kSafetyTicks;
+      for (;;) {
+        bool ok = true;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          x[j] = xload(a.xcell + ((size_t)(item0 + min(c0 + j, nchunk - 1)) * G + h) * (D + 2) + dim);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ok = ok && xfresh(x[j], epoch);
+        if (!__builtin_amdgcn_ballot_w64(!ok)) break;
+        if (__builtin_amdgcn_s_memrealtime() > deadline) {
+          if ((threadIdx.x & 63) == 0)
+            __hip_atomic_fetch_or(a.fault, kFaultValues, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (c0 + j < nchunk) acc = fmaf(xval(x[j]), wfn(h, k, c0 + j), acc);
+    }
+    store_elem<T>(a.out, ((size_t)b * a.n_q_heads + g * G + h) * D + dim, acc * invL[h]);
+    if (dim == 0 && a.dbg_lse)
+      a.dbg_lse[(size_t)b * a.n_q_heads + g * G + h] = (M[h] + __log2f(L[h])) * 0.6931471805599453f;
+  }
+}
+
+// Heads whose output rows chunk c writes: h = c, c + nchunk, ... (at most
+// ceil(G / 2) of them, a split pair having 2 chunks or more).
+template <int G>
+__device__ __forceinline__ uint32_t heads_of(int c, int nchunk) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int h = 0; h < G; ++h) m |= (h % nchunk == c ? 1u : 0u) << h;
+  return m;
+}
+
+// Writes a chunk's LDS logits to the pair's workspace rows: wave w's buffer
+// holds rows [start + w q, start + (w + 1) q) of the chunk (q = quarter), its
+// filled ones are copied (whole float4 cells: the slots past the filled ones
+// up to the next multiple of 4 are never read).
+template <int D, int G>
+__device__ __forceinline__ void spill_logits(const StepArgs& a, const PairMeta& pm, int start, int count, const float* s_logit) {
+  constexpr int LR = Shape<BF16T, D, G>::kLogitRows;
+  constexpr int NV = G * LR / 4;  // float4 cells of one wave's buffer
+  const int lane = threadIdx.x & 63, wave = wave_index();
+  const int quarter = ((count + kWaves - 1) / kWaves + 15) & ~15;
+  const int R0 = start + wave * quarter;
+  const int row_end = min(start + count, pm.len);
+  const int nrows = min(R0 + quarter, row_end) - R0;
+  const float* lbuf = s_logit + wave * G * LR;
+  const auto lrs = wt_rsrc(a.logits + (size_t)pm.slot0 * G, G * pm.lstride * 4);
+  for (int idx = lane; idx < NV; idx += 64) {
+    const int h = idx / (LR / 4), r4 = idx % (LR / 4);
+    if (4 * r4 < nrows)
+      store_wt4(lrs, 4 * (h * pm.lstride + R0 + 4 * r4), *reinterpret_cast<const float4*>(lbuf + h * LR + 4 * r4));
+  }
+}
+
+// Flags in LDS between the waves of a workgroup (set once per step, zeroed at
+// workgroup start): a wave waits for another with a bounded spin (the other
+// wave is running, so the wait ends; the bound is a safety net).
+__device__ __forceinline__ uint32_t lds_wait(uint32_t* f, const StepArgs& a) {
+  const uint64_t deadline = __builtin_amdgcn_s_memrealtime() + kSafetyTicks;
+  uint32_t v;
+  while ((v = __hip_atomic_load(f, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP)) == 0u) {
+    if (__builtin_amdgcn_s_memrealtime() > deadline) {
+      if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_or(a.fault, kFaultValues, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return 1u;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  return v;
+}
+__device__ __forceinline__ void lds_set(uint32_t* f, uint32_t v) {
+  if ((threadIdx.x & 63) == 0) __hip_atomic_store(f, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Finisher, cold path: a deferred chunk's slots are scored from the workspace
+// logits and its output rows written here; then the incoming token is
+// inserted.  Every wave of the workgroup runs it (it has barriers); `best` /
+// `besti` hold the fast chunks' minimum.  Every chunk published its
+// statistics and value sums before its ticket, so waiting for them ends.
+template <class T, int D, int G>
+__device__ __forceinline__ void finish_deferred(const StepArgs& a, int pair, const PairMeta& pm, uint64_t dmask, float best,
+                                int besti, int own, const float* s_part_w, const float* s_stat, const float* s_pre,
+                                float* s_arg, const uint32_t* s_bits) {
+  const int tid = threadIdx.x, wave = wave_index();
+  const int nchunk = pm.nchunk, item0 = pm.item0, len = pm.len;
+  const float ls = T::kEpl == 8 && !a.vl1 ? a.scale_log2 : 1.0f;
+  float* dbg = a.dbg_scores ? a.dbg_scores + (size_t)pair * a.max_budget : nullptr;
+  float snew[G], M[G], L[G], invL[G], wl[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) snew[h] = s_stat[h];
+  pair_stats_all<D, G>(a, item0, nchunk, pm.epoch, snew, s_stat, own, s_part_w, false,
+                       __builtin_amdgcn_s_memrealtime() + kSafetyTicks, M, L, invL, wl);
+  uint32_t dheads = 0;
+  for (uint64_t m = dmask; m; m &= m - 1) dheads |= heads_of<G>(__builtin_ctzll(m), nchunk);
+  split_output<T, D, G>(a, pair, item0, nchunk, pm.epoch, dheads, M, L, invL, snew, s_pre, 0, [&](int h, int, int c) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl[h]), c));
+  });
+  if (!a.score_none) {
+    const auto lg_rs = coh_rsrc(a.logits + (size_t)pm.slot0 * G, G * pm.lstride * 4);
+    float tb = INFINITY;
+    int ti = 0x7FFFFFFF;
+    for (uint64_t m = dmask; m; m &= m - 1) {
+      const WorkItem wi = a.items[item0 + __builtin_ctzll(m)];
+      const int end = min(wi.start + wi.count, len);
+      for (int base = wi.start + 4 * tid; base < end; base += 4 * kThreads) {
+        float4 lv[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) lv[h] = load_c4(lg_rs, (h * pm.lstride + base) * 4);
+        score4<G>(base, lv, M, invL, ls, s_bits, a.sink, len, dbg, tb, ti);
+      }
+    }
+    block_argmin(tb, ti, s_arg);
+    argmin_merge(best, besti, tb, ti);
+  }
+  if (wave == 0) insert_token<T, D>(a, pair, pm, besti, insert_piece<T, D, G>(a, pair, s_pre), true);
+}
+
+// End of the step for one chunk of a split pair (see the protocol above).
+// s_work holds the waves' partials [wave][G][D + 2] and the bitmap area,
+// s_logit the streaming waves' logits when lmode == kLogitsFull; s_flags
+// (LDS, zeroed at workgroup start) carries the hand-overs between the waves:
+// [0] bitmap ready, [1] statistics seen (1) or not (2), [2] finisher done (1)
+// or deferred chunks to finish (2), [3 ..] the finisher's fast minimum.
+// Wave 0 alone runs the critical path (statistics, scoring, ticket, finish);
+// waves 1-3 build the bitmap, publish the partial and write the output rows.
+template <class T, int D, int G>
+__device__ __forceinline__ void split_tail(const StepArgs& a, int pair, int item, int start, int count,
+                                           const PairMeta& pm, int lmode, float* s_work, const float* s_logit,
+                                           const float* s_pre, uint32_t* s_flags) {
+  using S = Shape<T, D, G>;
+  constexpr int kMaxOwnHeads = (G + 1) / 2;  // output heads of one chunk (2 chunks or more)
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
+  const int nchunk = pm.nchunk, item0 = pm.item0, chunk = item - item0, len = pm.len, budget = pm.budget;
+  const uint32_t epoch = pm.epoch;
+  uint32_t* s_bits = reinterpret_cast<uint32_t*>(s_work + S::kBitsOffset);
+  float* s_arg = s_work + S::kBitsOffset + kMaxBudget / 32;  // [kWaves] score, [kWaves] slot
+  // the new token's logit, max, normaliser and its inverse per head, then
+  // every chunk's weight for this chunk's output heads
+  __shared__ float s_stat[4 * G + kMaxOwnHeads * kMaxChunks];
+  const uint32_t my_heads = heads_of<G>(chunk, nchunk);
+  // Chunks whose logits stayed on chip wait for the pair's statistics (unless
+  // waiting is switched off).
+  const bool can_wait = a.wait_ticks > 0 && (a.score_none || lmode == kLogitsFull);
+  int own_c = -1;  // >= 0: the fast path's finisher has deferred chunks to finish (every wave joins)
+
+  if (wave == 0) {
+    float snew[G];
+    {
+      QReg<T, G> q;
+      uint4 kn;
+      new_token_logits<T, D, G>(a, pair, s_pre, q, kn, snew);
+    }
+    if (lane < G) {
+      float v = snew[0];
+#pragma unroll
+      for (int h = 1; h < G; ++h) v = lane == h ? snew[h] : v;
+      s_stat[lane] = v;
+    }
+    float M[G], L[G], invL[G], wl[G];
+    bool seen = false;
+    if (can_wait)
+      seen = pair_stats_all<D, G>(a, item0, nchunk, epoch, snew, s_stat, chunk, s_work, true,
+                                  __builtin_amdgcn_s_memrealtime() + a.wait_ticks, M, L, invL, wl);
+    if (seen) {
+      if (lane < G) {
+        float m = M[0], l = L[0], il = invL[0];
+#pragma unroll
+        for (int h = 1; h < G; ++h) {
+          m = lane == h ? M[h] : m;
+          l = lane == h ? L[h] : l;
+          il = lane == h ? invL[h] : il;
+        }
+        s_stat[G + lane] = m;
+        s_stat[2 * G + lane] = l;
+        s_stat[3 * G + lane] = il;
+      }
+      int k = 0;
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+        if ((my_heads >> h) & 1u) {
+          if (lane < nchunk) s_stat[4 * G + k * kMaxChunks + lane] = wl[h];
+          ++k;
+        }
+    }
+    lds_set(&s_flags[1], seen ? 1u : 2u);
+    if (seen) {
+      // ---- this chunk's slots, from the logits its waves kept in LDS: slot s
+      // of wave w = (s - start) / quarter at row s - start - w * quarter
+      float best = INFINITY;
+      int besti = 0x7FFFFFFF;
+      if (!a.score_none) {
+        constexpr int LR = S::kLogitRows;
+        const float ls = T::kEpl == 8 && !a.vl1 ? a.scale_log2 : 1.0f;
+        float* dbg = a.dbg_scores ? a.dbg_scores + (size_t)pair * a.max_budget : nullptr;
+        const int quarter = ((count + kWaves - 1) / kWaves + 15) & ~15;
+        const int end = min(start + count, len);
+        lds_wait(&s_flags[0], a);  // bitmap ready
+        for (int base = start + 4 * lane; base < end; base += 4 * 64) {
+          const int r = base - start;
+          int w = 0;
+#pragma unroll
+          for (int ww = 1; ww < kWaves; ++ww) w += r >= ww * quarter;
+          const float* src = s_logit + w * G * LR + (r - w * quarter);
+          float4 lv[G];
+#pragma unroll
+          for (int h = 0; h < G; ++h) lv[h] = *reinterpret_cast<const float4*>(src + h * LR);
+          score4<G>(base, lv, M, invL, ls, s_bits, a.sink, len, dbg, best, besti);
+        }
+        wave_argmin(best, besti);
+      }
+      // ---- candidate and ticket
+      uint32_t prev = 0;
+      if (lane == 0) {
+        xstore(a.xcand + 2 * (size_t)item, xword(best, epoch));
+        xstore(a.xcand + 2 * (size_t)item + 1, xword(static_cast<uint32_t>(besti & 0x7FFFFFFF), epoch));
+        prev = __hip_atomic_fetch_add(a.count + pair, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      prev = __builtin_amdgcn_readfirstlane(prev);
+      if (prev + 1u != static_cast<uint32_t>(nchunk)) {
+        lds_set(&s_flags[2], 1u);
+        return;
+      }
+      // ---- the finisher: every chunk's candidate (lane c: chunk c); without
+      // a deferred chunk it inserts right away
+      const bool mine = lane < nchunk;
+      const uint64_t* cc = a.xcand + 2 * (size_t)(item0 + (mine ? lane : 0));
+      uint64_t s0, s1;
+      const uint64_t deadline = __builtin_amdgcn_s_memrealtime() + kSafetyTicks;
+      for (;;) {
+        s0 = xload(cc);
+        s1 = xload(cc + 1);
+        if (!__builtin_amdgcn_ballot_w64(mine && !(xfresh(s0, epoch) && xfresh(s1, epoch)))) break;
+        if (__builtin_amdgcn_s_memrealtime() > deadline) {
+          if (lane == 0) __hip_atomic_fetch_or(a.fault, kFaultCandidates, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+      }
+      const uint32_t si = static_cast<uint32_t>(s1);
+      const bool deferred = mine && (si & 0x80000000u);
+      const uint64_t dmask = __builtin_amdgcn_ballot_w64(deferred);
+      float fb = mine && !deferred ? xval(s0) : INFINITY;
+      int fi = mine && !deferred ? static_cast<int>(si & 0x7FFFFFFF) : 0x7FFFFFFF;
+      wave_argmin(fb, fi);
+      if (dmask == 0) {
+        insert_token<T, D>(a, pair, pm, fi, insert_piece<T, D, G>(a, pair, s_pre), true);
+        lds_set(&s_flags[2], 1u);
+        return;
+      }
+      if (lane == 0) {
+        s_flags[3] = static_cast<uint32_t>(dmask);
+        s_flags[4] = static_cast<uint32_t>(dmask >> 32);
+        s_flags[5] = __float_as_uint(fb);
+        s_flags[6] = static_cast<uint32_t>(fi);
+      }
+      lds_set(&s_flags[2], 2u);
+      own_c = chunk;  // on to the cold path with the other waves
+    }
+  } else {
+    // ---- waves 1-3: the bitmap (wave 1), this chunk's statistics first (so
+    // the other chunks see them as early as possible), then its value sums
+    if (wave == 1) {
+      clear_protect_bits(s_bits, budget, 64, 64);
+      set_protect_bits<T, D, G>(a, pair, budget, s_bits, s_pre, 64, 64);
+      lds_set(&s_flags[0], 1u);
+    }
+    if (tid >= 128 && tid < 128 + G) {
+      const int h = tid - 128;
+      float mm, sl;
+      chunk_stat<D, G>(s_work, h, mm, sl);
+      uint64_t* xc = a.xcell + ((size_t)item * G + h) * (D + 2);
+      xstore(xc + D, xword(mm, epoch));
+      xstore(xc + D + 1, xword(sl, epoch));
+    }
+    for (int idx = tid - 64; idx < G * D; idx += kThreads - 64) {
+      const int h = idx / D, dim = idx - h * D;
+      float mm = kNegBig;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) mm = fmaxf(mm, s_work[(w * G + h) * (D + 2) + D]);
+      float sa = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float* src = s_work + (w * G + h) * (D + 2);
+        sa = fmaf(src[dim], fast_exp2(src[D] - mm), sa);
+      }
+      xstore(a.xcell + ((size_t)item * G + h) * (D + 2) + dim, xword(sa, epoch));
+    }
+    const uint32_t v = lds_wait(&s_flags[1], a);
+    if (v == 1u) {
+      // ---- this chunk's output rows
+      float snew[G], M[G], L[G], invL[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        snew[h] = s_stat[h];
+        M[h] = s_stat[G + h];
+        L[h] = s_stat[2 * G + h];
+        invL[h] = s_stat[3 * G + h];
+      }
+      split_output<T, D, G>(a, pair, item0, nchunk, epoch, my_heads, M, L, invL, snew, s_pre, 64,
+                            [&](int, int k, int c) { return s_stat[4 * G + k * kMaxChunks + c]; });
+      if (lds_wait(&s_flags[2], a) != 2u) return;
+      own_c = chunk;  // on to the cold path with wave 0
+    }
+  }
+  if (own_c < 0) {
+  // ---- deferred (every wave): the logits go to the workspace (the fp32
+  // stream and long chunks wrote them already) and every wave's stores
+  // complete before the candidate says so
+  if constexpr (T::kEpl == 8)
+    if (lmode == kLogitsFull && !a.score_none) spill_logits<D, G>(a, pm, start, count, s_logit);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tid == 0) {
+    xstore(a.xcand + 2 * (size_t)item, xword(INFINITY, epoch));
+    xstore(a.xcand + 2 * (size_t)item + 1, xword(0x80000000u | 0x7FFFFFFFu, epoch));
+    __hip_atomic_fetch_add(a.deferred, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t prev = __hip_atomic_fetch_add(a.count + pair, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_flags[7] = prev + 1u == static_cast<uint32_t>(nchunk) ? 1u : 2u;
+  }
+  __syncthreads();
+  if (s_flags[7] != 1u) return;
+  // the finisher of a pair whose last chunk was deferred: every candidate
+  if (wave == 0) {
+    const bool mine = lane < nchunk;
+    const uint64_t* cc = a.xcand + 2 * (size_t)(item0 + (mine ? lane : 0));
+    uint64_t s0, s1;
+    const uint64_t deadline = __builtin_amdgcn_s_memrealtime() + kSafetyTicks;
+    for (;;) {
+      s0 = xload(cc);
+      s1 = xload(cc + 1);
+      if (!__builtin_amdgcn_ballot_w64(mine && !(xfresh(s0, epoch) && xfresh(s1, epoch)))) break;
+      if (__builtin_amdgcn_s_memrealtime() > deadline) {
+        if (lane == 0) __hip_atomic_fetch_or(a.fault, kFaultCandidates, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+    }
+    const uint32_t si = static_cast<uint32_t>(s1);
+    const bool deferred = mine && (si & 0x80000000u);
+    const uint64_t dmask = __builtin_amdgcn_ballot_w64(deferred);
+    float fb = mine && !deferred ? xval(s0) : INFINITY;
+    int fi = mine && !deferred ? static_cast<int>(si & 0x7FFFFFFF) : 0x7FFFFFFF;
+    wave_argmin(fb, fi);
+    if (lane == 0) {
+      s_flags[3] = static_cast<uint32_t>(dmask);
+      s_flags[4] = static_cast<uint32_t>(dmask >> 32);
+      s_flags[5] = __float_as_uint(fb);
+      s_flags[6] = static_cast<uint32_t>(fi);
+    }
+  }
+  __syncthreads();
+  }
+  // ---- the finisher's cold path (every wave): deferred chunks to finish
+  const uint64_t dmask = static_cast<uint64_t>(s_flags[3]) | (static_cast<uint64_t>(s_flags[4]) << 32);
+  finish_deferred<T, D, G>(a, pair, pm, dmask, __uint_as_float(s_flags[5]), static_cast<int>(s_flags[6]), own_c,
+                           s_work, s_stat, s_pre, s_arg, s_bits);
 }
 
 // Streaming of one chunk on the vector ALUs (fp32 cache): 16-byte loads of one
@@ -881,7 +1431,7 @@ __device__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const
 // per row lineage, P.V by FMA.  Leaves the wave's partial (max, sum, weighted
 // value sum per head) in s_merge[wave][G][D + 2].
 template <class T, int D, int G>
-__device__ void stream_valu(const StepArgs& a, int pair, int start, int row_end, float* lg, int lstride,
+__device__ __forceinline__ void stream_valu(const StepArgs& a, int pair, int start, int row_end, float* lg, int lstride,
                             float* s_merge) {
   using S = Shape<T, D, G>;
   constexpr int EPL = S::kEpl, LPR = S::kLpr, RPL = S::kRpl, U = S::kU, TILE = S::kTile;
@@ -1042,7 +1592,7 @@ __device__ void stream_valu(const StepArgs& a, int pair, int start, int row_end,
 //    equal the eager form up to rounding.
 // Leaves the wave's partial in s_merge[wave][G][D + 2] like stream_valu.
 template <int D, int G>
-__device__ void stream_mfma(const StepArgs& a, int pair, int start, int count, PairMeta& pm, int& lmode,
+__device__ __forceinline__ void stream_mfma(const StepArgs& a, int pair, int start, int count, PairMeta& pm, int& lmode,
                             float* s_merge, unsigned char* s_stage, float* s_logit) {
   constexpr int KB = D / 32;  // q.k MFMAs per row group
   constexpr int EV = D / 16;  // value dims per lane per row = P.V MFMAs per value row
@@ -1272,7 +1822,7 @@ __device__ void stream_mfma(const StepArgs& a, int pair, int start, int count, P
     pm.nchunk = __builtin_amdgcn_readfirstlane(m0.w);
     pm.item0 = __builtin_amdgcn_readfirstlane(m1.x);
     pm.slot0 = __builtin_amdgcn_readfirstlane(m1.y);
-    pm.ticket = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(m1.z));
+    pm.epoch = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(m1.z));
     pm.lstride = __builtin_amdgcn_readfirstlane(m1.w);
     row_end = min(start + count, pm.len);
     Rend = min(R0 + quarter, row_end);
@@ -1281,9 +1831,9 @@ __device__ void stream_mfma(const StepArgs& a, int pair, int start, int count, P
     lstride = pm.lstride;
     lg = a.logits + (size_t)pm.slot0 * G;  // [G][lstride]
     lrs = wt_rsrc(lg, a.score_none ? 0 : G * lstride * 4);
-    // An unsplit pair whose wave ranges fit the buffers keeps its logits here,
-    // in fp32 up to LR rows per wave, in half precision up to 2 LR.
-    lmode = pm.nchunk != 1 ? kLogitsOut : quarter <= LR ? kLogitsFull : quarter <= 2 * LR ? kLogitsHalf : kLogitsOut;
+    // A chunk whose wave ranges fit the buffers keeps its logits here in fp32
+    // (LR rows per wave); an unsplit pair also in half precision up to 2 LR.
+    lmode = quarter <= LR ? kLogitsFull : pm.nchunk == 1 && quarter <= 2 * LR ? kLogitsHalf : kLogitsOut;
 #pragma unroll
     for (int s = 1; s < NS - 1; ++s) load_grp(kbuf[s], vbuf[s], s < nfull);
     auto step = [&](const uint4(&kk)[KB], const VLoad(&vv)[4]) {
@@ -1342,11 +1892,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Shape<
 void lf_step_kernel(StepArgs a) {
   using S = Shape<T, D, G>;
   __shared__ float smem[S::kSmemFloats];
-  __shared__ int s_last;
+  __shared__ uint32_t s_flags[8];  // hand-overs between the waves of a split pair's chunk (split_tail)
   float* s_part = smem;                   // [G][D + 2]: merged partial of this chunk
   float* s_work = smem + S::kPartFloats;  // cross-wave merge, then tail scratch
 
   const int tid = threadIdx.x;
+  if (tid < 8) s_flags[tid] = 0u;  // ordered before any use by the barrier after the stream
   // U (equal budgets): the item follows from the block index, so the first
   // K/V loads wait for no load of the work list.  A separate instantiation:
   // a run-time branch would make every scalar load of the prologue wait.
@@ -1360,7 +1911,7 @@ void lf_step_kernel(StepArgs a) {
     it = a.items[blockIdx.x];
   }
   const int pair = it.pair;
-  PairMeta* meta = a.meta + pair;  // written only by this pair's tail, after every chunk is done
+  PairMeta* meta = a.meta + pair;  // written only by the workgroup finishing the pair, after every chunk is done
   float* s_logit = s_work + S::kMergeFloats + S::kStageFloats;
   float* s_pre = smem + S::kSmemFloats - S::kPreFloats;  // prefetched tail inputs
   PairMeta pm;
@@ -1380,10 +1931,13 @@ void lf_step_kernel(StepArgs a) {
   const int nchunk = pm.nchunk;
   __syncthreads();
   uint32_t* s_bits = reinterpret_cast<uint32_t*>(s_work + S::kBitsOffset);
+  if (nchunk > 1) {
+    split_tail<T, D, G>(a, pair, (int)blockIdx.x, it.start, it.count, pm, lmode, s_work, s_logit, s_pre, s_flags);
+    return;
+  }
   clear_protect_bits(s_bits, pm.budget);
-
-  // Merge the waves' partials into this chunk's partial.
-  const size_t item = blockIdx.x;
+  // Merge the waves' partials into this chunk's partial, kept in LDS for the
+  // pair's tail.
   for (int idx = tid; idx < G * D; idx += kThreads) {
     const int h = idx / D, dim = idx - h * D;
     float mm = kNegBig;
@@ -1397,40 +1951,19 @@ void lf_step_kernel(StepArgs a) {
       sa += src[dim] * f;
       sl += src[D + 1] * f;
     }
-    if (nchunk == 1) {
-      s_part[h * (D + 2) + dim] = sa;
-      if (dim == 0) {
-        s_part[h * (D + 2) + D] = mm;
-        s_part[h * (D + 2) + D + 1] = sl;
-      }
-    } else {
-      store_wt(&a.part_acc[(item * G + h) * D + dim], sa);
-      if (dim == 0) store_wt(&reinterpret_cast<float2*>(a.part_ml)[item * G + h], make_float2(mm, sl));
+    s_part[h * (D + 2) + dim] = sa;
+    if (dim == 0) {
+      s_part[h * (D + 2) + D] = mm;
+      s_part[h * (D + 2) + D + 1] = sl;
     }
   }
-
-  if (nchunk == 1) {
-    // Logits this pair wrote to the workspace are read back by other waves of
-    // this workgroup with device-scope loads: every wave drains its stores
-    // before the barrier, as a split pair's chunks do before the ticket.
-    if (lmode == kLogitsOut) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // merged partial complete, bitmap cleared
-    set_protect_bits<T, D, G>(a, pair, pm.budget, s_bits, s_pre);
-    __syncthreads();
-  } else {
-    // Ticket (the hand-over protocol is described at store_wt): every wave
-    // drains its device-scope stores, the barrier orders that before thread
-    // 0's device-scope increment, and the last arrival runs the tail.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (tid == 0) {
-      const unsigned prev = __hip_atomic_fetch_add(&meta->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_last = prev + 1 == static_cast<unsigned>(nchunk);
-    }
-    set_protect_bits<T, D, G>(a, pair, pm.budget, s_bits, s_pre);  // while the ticket is in flight
-    __syncthreads();
-    if (!s_last) return;
-  }
+  // Logits this pair wrote to the workspace are read back by other waves of
+  // this workgroup with device-scope loads: every wave drains its stores
+  // before the barrier.
+  if (lmode == kLogitsOut) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();  // merged partial complete, bitmap cleared
+  set_protect_bits<T, D, G>(a, pair, pm.budget, s_bits, s_pre);
+  __syncthreads();
   pair_tail<T, D, G>(a, pair, pm, s_part, s_work, s_logit, lmode, s_pre);
 }
 

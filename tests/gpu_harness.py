@@ -36,6 +36,7 @@ class ParityReport:
     max_score_err: float = 0.0
     max_lse_err: float = 0.0
     diverged_at: int | None = None
+    deferred: int = 0  # split chunks that stopped waiting for their pair
     notes: list = field(default_factory=list)
 
 
@@ -46,7 +47,7 @@ def log(msg: str) -> None:
 
 def parity_run(w: Workload, steps: int, check=None, score: str = "attn", chunk_slots: int = 0,
                dbg_every: int = 0, free_running: bool = False, device="cuda:0", max_budget=None,
-               compare_cache: bool = True, tag: str = "") -> ParityReport:
+               compare_cache: bool = True, tag: str = "", split_wait_us=None) -> ParityReport:
     device = torch.device(device)
     check = list(range(w.batch)) if check is None else list(check)
     log(f"[parity{tag}] {w.name}: B={w.batch} Hq={w.n_q_heads} Hkv={w.n_kv_heads} d={w.head_dim} "
@@ -55,6 +56,8 @@ def parity_run(w: Workload, steps: int, check=None, score: str = "attn", chunk_s
     K, V, seq_len, bud = device_cache(w, device, max_budget=max_budget)
     cache = LongFlowCache(K, V, w.n_q_heads, w.sink, w.recent, seq_len, budgets=bud, score=score,
                           chunk_slots=chunk_slots)
+    if split_wait_us is not None:
+        cache.set_split_wait(split_wait_us)
     init = [initial_sequence(w, b) for b in check]
     oc = OracleCache([x[0] for x in init], [x[1] for x in init], [x[2] for x in init], [x[3] for x in init],
                      bud[check], w.n_q_heads, w.sink, w.recent,
@@ -113,6 +116,8 @@ def parity_run(w: Workload, steps: int, check=None, score: str = "attn", chunk_s
             nb = oc.budget[j]
             assert np.array_equal(Kh[j, :, :nb], oc.k[j]), f"K cache of sequence {check[j]} differs"
             assert np.array_equal(Vh[j, :, :nb], oc.v[j]), f"V cache of sequence {check[j]} differs"
+    st = cache.check_state()  # invariants of the state after the run
+    rep.deferred = st.deferred
     cache.close()
     log(f"[parity{tag}] ok: {rep}")
     return rep

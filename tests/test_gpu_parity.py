@@ -107,6 +107,26 @@ def test_edge_cases(kw):
     parity_run(w, steps, dbg_every=7, tag=f" {kw}")
 
 
+@pytest.mark.parametrize("name,steps,check,wait", [
+    ("llama8b_b8", 24, None, 0),            # 4 chunks per pair, G = 4: every chunk hands over
+    ("evict_stress", 24, [0, 5, 15], 0),    # 4 chunks per pair, G = 7
+    ("llama8b_b8", 24, [1, 6], 1),          # a 1 us wait: chunks waiting longer hand over
+])
+def test_split_chunks_that_do_not_wait(name, steps, check, wait):
+    # a split chunk that does not wait for its pair's statistics hands its
+    # logits over through memory and the pair's finisher scores them; the
+    # results are those of the chunks scoring on chip
+    rep = parity_run(get_workload(name), steps, check=check, dbg_every=4, split_wait_us=wait, tag=f" wait={wait}")
+    if wait == 0:
+        assert rep.deferred == steps * get_workload(name).batch * get_workload(name).n_kv_heads * 4
+
+
+def test_split_chunks_wait_by_default():
+    # the headline shape's 256 work items run at once: no chunk stops waiting
+    rep = parity_run(get_workload("llama8b_b8"), 32, check=[0, 7], dbg_every=8)
+    assert rep.deferred == 0, rep
+
+
 def test_small_chunks_and_cache_stride():
     # many chunks with a ragged last one, and a slot stride larger than every budget
     w = _small(budget_lo=333, budget_hi=333, batch=2)
@@ -118,10 +138,12 @@ def test_small_chunks_and_cache_stride():
     (dict(budget_lo=4096, budget_hi=4096, batch=1, prefill="full"), 64),         # 64 chunks, the most allowed
     (dict(budget_lo=900, budget_hi=900, batch=2, n_q_heads=14, n_kv_heads=2), 64),  # G = 7: 15 chunks
 ])
-def test_many_chunks(kw, chunk):
-    # more chunks than the tail takes per batch of partial loads, up to the limit
+@pytest.mark.parametrize("wait", [None, 0])
+def test_many_chunks(kw, chunk, wait):
+    # up to the most chunks a pair may have; with and without waiting for the
+    # pair's statistics (the finisher then scores every deferred chunk)
     w = _small(**kw)
-    parity_run(w, 40, chunk_slots=chunk, dbg_every=4, tag=f" {kw} chunk={chunk}")
+    parity_run(w, 40, chunk_slots=chunk, dbg_every=4, split_wait_us=wait, tag=f" {kw} chunk={chunk} wait={wait}")
 
 
 @pytest.mark.parametrize("kw", [
@@ -226,7 +248,7 @@ def test_vl1_on_ragged_small():
 
 # ---------------------------------------------------------------- determinism and resume
 
-def _run_steps(w, steps, device, state=None, attach=False, K=None, V=None, start=0):
+def _run_steps(w, steps, device, state=None, attach=False, K=None, V=None, start=0, split_wait_us=None):
     from kv_cache_eviction_lf_amd import LongFlowCache
     from workloads.device import device_cache, device_step
 
@@ -237,6 +259,8 @@ def _run_steps(w, steps, device, state=None, attach=False, K=None, V=None, start
     cache = LongFlowCache(K, V, w.n_q_heads, w.sink, w.recent,
                           seq_len if seq_len is not None else [0] * w.batch, budgets=bud,
                           state=state, attach=attach)
+    if split_wait_us is not None:
+        cache.set_split_wait(split_wait_us)
     outs, evs = [], []
     for s in range(start, start + steps):
         (qd, kd, vd), _ = device_step(w, s, device)
@@ -257,6 +281,25 @@ def test_bitwise_deterministic():
         assert torch.equal(a, b)
     for a, b in zip(e1, e2):
         assert torch.equal(a, b)
+    assert torch.equal(K1, K2) and torch.equal(V1, V2)
+    c1.close()
+    c2.close()
+
+
+@pytest.mark.parametrize("name", ["llama8b_b8", "evict_stress"])
+def test_split_paths_agree_bitwise(name):
+    # chunks scoring their slots on chip and chunks handing their logits to
+    # the finisher give the same bits (outputs, evictions, caches)
+    w = get_workload(name)
+    dev = torch.device("cuda:0")
+    log(f"[split paths] {name}: default wait against no wait, 30 steps")
+    c1, K1, V1, o1, e1 = _run_steps(w, 30, dev)
+    c2, K2, V2, o2, e2 = _run_steps(w, 30, dev, split_wait_us=0)
+    assert c2.check_state().deferred > 0
+    for a_, b_ in zip(o1, o2):
+        assert torch.equal(a_, b_)
+    for a_, b_ in zip(e1, e2):
+        assert torch.equal(a_, b_)
     assert torch.equal(K1, K2) and torch.equal(V1, V2)
     c1.close()
     c2.close()
