@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define LF_ABI_VERSION 1
+#define LF_ABI_VERSION 2
 
 typedef enum lf_status {
   LF_OK = 0,
@@ -134,7 +134,8 @@ lf_status lf_init_cache(const lf_config* cfg, const int32_t* budgets, const int6
  *              or -2 when the token was not stored (LF_SCORE_NONE, full).
  * Asynchronous and stream-ordered; no host synchronisation, no allocation.
  * Calls on one handle must be ordered on one stream.  Validation is limited to
- * null pointers and the handle; errors: LF_ERR_ARG, LF_ERR_STATE, LF_ERR_HIP.
+ * null pointers and the handle (a handle from lf_init_cache: one layer);
+ * errors: LF_ERR_ARG, LF_ERR_STATE, LF_ERR_HIP.
  */
 lf_status lf_decode_step(const void* q, const void* k_new, const void* v_new, lf_cache* cache,
                          void* out, int32_t* evict_idx, void* stream);
@@ -150,6 +151,47 @@ lf_status lf_decode_step(const void* q, const void* k_new, const void* v_new, lf
  */
 lf_status lf_decode_step_dbg(const void* q, const void* k_new, const void* v_new, lf_cache* cache,
                              void* out, int32_t* evict_idx, float* scores, float* lse, void* stream);
+
+/*
+ * lf_state_bytes_layers - size of the state buffer of lf_init_layers:
+ * n_layers (1 .. 4096) times lf_state_bytes.  Errors as lf_state_bytes.
+ */
+lf_status lf_state_bytes_layers(const lf_config* cfg, const int32_t* budgets, int32_t n_layers, size_t* bytes);
+
+/*
+ * lf_init_layers - one handle over the n_layers layer caches of a model (the
+ * statically pre-allocated cache of the LongFlow summary, section 2.C, for
+ * every layer; memory management across the layers is what section 4 credits
+ * for the larger batches).  Every layer shares cfg, budgets and seq_len;
+ * layer l's state occupies bytes [l * S, (l + 1) * S) of `state` with
+ * S = state_bytes / n_layers rounded down to a multiple of 256, which must be
+ * at least lf_state_bytes (the same S again when attaching with
+ * LF_INIT_ATTACH, so pass the same state_bytes).
+ *   k_caches, v_caches  host arrays of n_layers device pointers, each a
+ *            [B][Hkv][max_budget][d] cache laid out as lf_init_cache describes.
+ * Other arguments, the cache contract and errors as lf_init_cache.  The
+ * resets (lf_reset_sequences, lf_reset_sequences_budget), lf_set_split_wait and
+ * lf_check_state act on every layer of the handle; steps run per layer with
+ * lf_decode_step_layer (lf_decode_step rejects a handle of several layers).
+ */
+lf_status lf_init_layers(const lf_config* cfg, int32_t n_layers, const int32_t* budgets, const int64_t* seq_len,
+                         void* const* k_caches, void* const* v_caches, void* state, size_t state_bytes,
+                         int32_t flags, void* stream, lf_cache** out);
+
+/*
+ * lf_decode_step_layer - lf_decode_step on layer `layer` (0 .. n_layers - 1)
+ * of a handle, with that layer's q, k_new, v_new, out and evict_idx.  Layers
+ * are independent: their steps may run in any order, each layer's steps in
+ * sequence on one stream.  Errors: LF_ERR_ARG (also a layer out of range),
+ * LF_ERR_STATE, LF_ERR_HIP.
+ */
+lf_status lf_decode_step_layer(const void* q, const void* k_new, const void* v_new, lf_cache* cache, int32_t layer,
+                               void* out, int32_t* evict_idx, void* stream);
+
+/* lf_decode_step_layer_dbg - lf_decode_step_dbg on one layer of a handle. */
+lf_status lf_decode_step_layer_dbg(const void* q, const void* k_new, const void* v_new, lf_cache* cache,
+                                   int32_t layer, void* out, int32_t* evict_idx, float* scores, float* lse,
+                                   void* stream);
 
 /*
  * lf_set_split_wait - how long a chunk of a split (sequence, KV head) pair
@@ -171,15 +213,16 @@ lf_status lf_set_split_wait(lf_cache* cache, int32_t max_wait_us);
 
 /* Result of lf_check_state. */
 typedef struct {
-  uint32_t deferred; /* split chunks that handed their logits over through memory, since init */
-  int32_t n_pairs;   /* batch * n_kv_heads */
+  uint32_t deferred; /* split chunks that handed their logits over through memory, since init (all layers) */
+  int32_t n_pairs;   /* batch * n_kv_heads (per layer) */
   int32_t bad_pair;  /* first pair that failed a check, or -1 */
-  int32_t reserved;
+  int32_t bad_layer; /* layer of the failed check, or -1 */
 } lf_state_report;
 
 /*
  * lf_check_state - read the state back (after the steps queued on `stream`)
- * and check its invariants: the header matches the handle; per pair the
+ * and check its invariants, in every layer of the handle: the header matches
+ * the handle and no wait hit its safety bound; per pair the
  * layout fields are the handle's, the fill level is min(position, budget),
  * the epoch is non-zero, no chunk counter is left over from a step, and the
  * slots of the `recent` newest positions are distinct filled slots.
@@ -192,7 +235,8 @@ lf_status lf_check_state(const lf_cache* cache, void* stream, lf_state_report* r
 /*
  * lf_reset_sequences - restart some sequences of the batch in place (a finished
  * request's place taken by a new one under continuous batching) while the
- * others keep their state.  The decode step runs over a static, pre-allocated
+ * others keep their state.  On a handle over several layers
+ * (lf_init_layers) the listed sequences restart in every layer.  The decode step runs over a static, pre-allocated
  * cache (LongFlow summary, section 2.C); this only re-initialises the listed
  * sequences' position, fill level and recent-window ring, exactly as
  * lf_init_cache does for the whole batch.
@@ -223,9 +267,11 @@ lf_status lf_reset_sequences(lf_cache* cache, int32_t n, const int32_t* seqs, co
  *            (sink + recent, max_budget]; the listed sequence's cached tokens
  *            (seq_len, capped at the new budget) are already laid out in its
  *            k_cache/v_cache rows as lf_init_cache describes.
- * The state buffer passed to lf_init_cache (its state_bytes) must hold the
- * layout of the new budgets (lf_state_bytes with them); otherwise LF_ERR_ARG
- * and nothing changes.  Errors: LF_ERR_ARG, LF_ERR_STATE, LF_ERR_HIP.
+ * On a handle over several layers the listed sequences restart, with their
+ * new budgets, in every layer.  The state buffer passed at init (its
+ * state_bytes, divided by the number of layers) must hold the layout of the
+ * new budgets (lf_state_bytes with them); otherwise LF_ERR_ARG and nothing
+ * changes.  Errors: LF_ERR_ARG, LF_ERR_STATE, LF_ERR_HIP.
  */
 lf_status lf_reset_sequences_budget(lf_cache* cache, int32_t n, const int32_t* seqs, const int64_t* seq_len,
                                     const int32_t* budgets, void* stream);

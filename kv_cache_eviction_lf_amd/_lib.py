@@ -26,7 +26,7 @@ class LFError(RuntimeError):
 
 
 class lf_state_report(ctypes.Structure):
-    _fields_ = [("deferred", c_uint32), ("n_pairs", c_int32), ("bad_pair", c_int32), ("reserved", c_int32)]
+    _fields_ = [("deferred", c_uint32), ("n_pairs", c_int32), ("bad_pair", c_int32), ("bad_layer", c_int32)]
 
 
 class lf_config(ctypes.Structure):
@@ -56,6 +56,16 @@ PROTOTYPES = {
         [POINTER(lf_config), POINTER(c_int32), POINTER(c_int64), c_void_p, c_void_p, c_void_p, c_size_t, c_int32,
          c_void_p, POINTER(c_void_p)],
     ),
+    "lf_state_bytes_layers": (c_int32, [POINTER(lf_config), POINTER(c_int32), c_int32, POINTER(c_size_t)]),
+    "lf_init_layers": (
+        c_int32,
+        [POINTER(lf_config), c_int32, POINTER(c_int32), POINTER(c_int64), POINTER(c_void_p), POINTER(c_void_p),
+         c_void_p, c_size_t, c_int32, c_void_p, POINTER(c_void_p)],
+    ),
+    "lf_decode_step_layer": (
+        c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p]),
+    "lf_decode_step_layer_dbg": (
+        c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "lf_decode_step": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "lf_decode_step_dbg": (
         c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
@@ -151,6 +161,44 @@ def lf_init_cache(cfg: lf_config, budgets, seq_len, k_cache: int, v_cache: int, 
                                         c_void_p(v_cache), c_void_p(state), c_size_t(state_bytes), c_int32(flags),
                                         c_void_p(stream), ctypes.byref(handle)), "lf_init_cache")
     return int(handle.value)
+
+
+def lf_state_bytes_layers(cfg: lf_config, budgets, n_layers: int) -> int:
+    out = c_size_t(0)
+    _check(load_library().lf_state_bytes_layers(ctypes.byref(cfg), _i32_array(budgets), c_int32(n_layers),
+                                                ctypes.byref(out)), "lf_state_bytes_layers")
+    return int(out.value)
+
+
+def lf_init_layers(cfg: lf_config, budgets, seq_len, k_caches, v_caches, state: int, state_bytes: int,
+                   flags: int = 0, stream: int = 0) -> int:
+    sl = [int(x) for x in seq_len]
+    sl_arr = (c_int64 * len(sl))(*sl)
+    n = len(k_caches)
+    if len(v_caches) != n:
+        raise ValueError("k_caches and v_caches must have the same length")
+    ks = (c_void_p * max(1, n))(*[c_void_p(int(x)) for x in k_caches])
+    vs = (c_void_p * max(1, n))(*[c_void_p(int(x)) for x in v_caches])
+    handle = c_void_p(0)
+    _check(load_library().lf_init_layers(ctypes.byref(cfg), c_int32(n), _i32_array(budgets), sl_arr, ks, vs,
+                                         c_void_p(state), c_size_t(state_bytes), c_int32(flags), c_void_p(stream),
+                                         ctypes.byref(handle)), "lf_init_layers")
+    return int(handle.value)
+
+
+def lf_decode_step_layer(q: int, k_new: int, v_new: int, cache: int, layer: int, out: int, evict_idx: int,
+                         stream: int = 0) -> None:
+    _check(load_library().lf_decode_step_layer(c_void_p(q), c_void_p(k_new), c_void_p(v_new), c_void_p(cache),
+                                               c_int32(layer), c_void_p(out), c_void_p(evict_idx), c_void_p(stream)),
+           "lf_decode_step_layer")
+
+
+def lf_decode_step_layer_dbg(q: int, k_new: int, v_new: int, cache: int, layer: int, out: int, evict_idx: int,
+                             scores: int = 0, lse: int = 0, stream: int = 0) -> None:
+    _check(load_library().lf_decode_step_layer_dbg(c_void_p(q), c_void_p(k_new), c_void_p(v_new), c_void_p(cache),
+                                                   c_int32(layer), c_void_p(out), c_void_p(evict_idx),
+                                                   c_void_p(scores or None), c_void_p(lse or None),
+                                                   c_void_p(stream)), "lf_decode_step_layer_dbg")
 
 
 def lf_reset_sequences(cache: int, seqs, seq_len, stream: int = 0) -> None:

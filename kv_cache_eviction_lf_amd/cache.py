@@ -27,7 +27,55 @@ def _need(t: torch.Tensor, name: str, shape, dtype, device) -> None:
         raise ValueError(f"{name} must be a contiguous {dtype} tensor on {device}")
 
 
-class LongFlowCache:
+class _Handle:
+    """Calls shared by the single-layer and the multi-layer handle."""
+
+    handle = 0
+
+    def reset(self, seqs, seq_len, budgets=None) -> None:
+        """Restart sequences `seqs` in place (their K/V rows already hold the new
+        requests' cached tokens) with `seq_len` tokens seen, in every layer of the
+        handle; lf_reset_sequences, or lf_reset_sequences_budget when new
+        `budgets` are given for them."""
+        if not self.handle:
+            raise RuntimeError("cache is closed")
+        if budgets is None:
+            _lib.lf_reset_sequences(self.handle, list(seqs), list(seq_len), _stream_handle(self.device))
+            return
+        _lib.lf_reset_sequences_budget(self.handle, list(seqs), list(seq_len), list(budgets),
+                                       _stream_handle(self.device))
+        full = list(self.budgets) if self.budgets is not None else [self.max_budget] * self.B
+        for b, nb in zip(seqs, budgets):
+            full[int(b)] = int(nb)
+        self.budgets = full
+
+    def set_split_wait(self, max_wait_us: int) -> None:
+        """How long a chunk of a split pair waits for the pair's statistics
+        before handing its logits over through memory (lf_set_split_wait)."""
+        if not self.handle:
+            raise RuntimeError("cache is closed")
+        _lib.lf_set_split_wait(self.handle, int(max_wait_us))
+
+    def check_state(self):
+        """Read the state back and check its invariants in every layer
+        (lf_check_state); returns the report (deferred chunks since init, pairs)."""
+        if not self.handle:
+            raise RuntimeError("cache is closed")
+        return _lib.lf_check_state(self.handle, _stream_handle(self.device))
+
+    def close(self) -> None:
+        if self.handle:
+            _lib.lf_free(self.handle)
+            self.handle = 0
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class LongFlowCache(_Handle):
     """One layer's static KV cache with per-step LongFlow eviction.
 
     k_cache, v_cache: contiguous device tensors [B][Hkv][max_budget][d] (bf16 or
@@ -71,73 +119,94 @@ class LongFlowCache:
              evict_idx: torch.Tensor | None = None, scores: torch.Tensor | None = None,
              lse: torch.Tensor | None = None):
         """One fused decode step; returns (out [B][Hq][d], evict_idx int32 [B][Hkv])."""
-        if not self.handle:
-            raise RuntimeError("cache is closed")
-        _need(q, "q", (self.B, self.Hq, self.d), self.dtype, self.device)
-        _need(k_new, "k_new", (self.B, self.Hkv, self.d), self.dtype, self.device)
-        _need(v_new, "v_new", (self.B, self.Hkv, self.d), self.dtype, self.device)
-        if out is None:
-            out = torch.empty_like(q)
-        else:
-            _need(out, "out", (self.B, self.Hq, self.d), self.dtype, self.device)
-        if evict_idx is None:
-            evict_idx = torch.empty((self.B, self.Hkv), dtype=torch.int32, device=self.device)
-        else:
-            _need(evict_idx, "evict_idx", (self.B, self.Hkv), torch.int32, self.device)
-        stream = _stream_handle(self.device)
+        return _step(self, None, q, k_new, v_new, out, evict_idx, scores, lse)
+
+
+class LongFlowLayers(_Handle):
+    """The static KV caches of a model's layers behind one handle
+    (lf_init_layers): every layer shares the batch, heads, windows, budgets and
+    positions; steps run per layer, and reset() restarts sequences in every
+    layer at once (with new budgets when given).
+
+    k_caches, v_caches: lists of contiguous device tensors [B][Hkv][max_budget][d],
+    one per layer, each filled as the C ABI's lf_init_cache describes;
+    state_capacity: bytes for the state buffer when none is given (at least
+    what the budgets need for every layer); a larger one lets reset() give
+    sequences larger budgets later."""
+
+    def __init__(self, k_caches, v_caches, n_q_heads: int, sink: int, recent: int, seq_len, budgets=None,
+                 score: str = "attn", softmax_scale: float = 0.0, chunk_slots: int = 0,
+                 state: torch.Tensor | None = None, attach: bool = False, state_capacity: int = 0):
+        k_caches, v_caches = list(k_caches), list(v_caches)
+        if not k_caches or len(k_caches) != len(v_caches):
+            raise ValueError("k_caches and v_caches must be non-empty lists of the same length")
+        k0 = k_caches[0]
+        if k0.dim() != 4 or k0.dtype not in _DTYPES:
+            raise ValueError("caches must be [B][Hkv][max_budget][d] bf16 or fp32 tensors")
+        self.device = k0.device
+        B, Hkv, S, d = k0.shape
+        for i, (k, v) in enumerate(zip(k_caches, v_caches)):
+            _need(k, f"k_caches[{i}]", (B, Hkv, S, d), k0.dtype, self.device)
+            _need(v, f"v_caches[{i}]", (B, Hkv, S, d), k0.dtype, self.device)
+        self.n_layers = len(k_caches)
+        self.B, self.Hkv, self.max_budget, self.d = B, Hkv, S, d
+        self.Hq = int(n_q_heads)
+        self.dtype = k0.dtype
+        self.k_caches, self.v_caches = k_caches, v_caches
+        self.budgets = None if budgets is None else [int(x) for x in budgets]
+        self.cfg = _lib.make_config(B, self.Hq, Hkv, d, S, sink, recent, _DTYPES[self.dtype], _SCORES[score],
+                                    softmax_scale, chunk_slots)
+        self.state_bytes = _lib.lf_state_bytes_layers(self.cfg, self.budgets, self.n_layers)
+        if state is None:
+            if attach:
+                raise ValueError("attach needs the saved state tensor")
+            state = torch.empty(max(self.state_bytes, int(state_capacity)), dtype=torch.uint8, device=self.device)
+        elif state.numel() < self.state_bytes or state.device != self.device:
+            raise ValueError("state tensor too small or on another device")
+        self.state = state
+        self.handle = _lib.lf_init_layers(self.cfg, self.budgets, list(seq_len), [k.data_ptr() for k in k_caches],
+                                          [v.data_ptr() for v in v_caches], state.data_ptr(), state.numel(),
+                                          LF_INIT_ATTACH if attach else 0, _stream_handle(self.device))
+
+    def step(self, layer: int, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+             out: torch.Tensor | None = None, evict_idx: torch.Tensor | None = None,
+             scores: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+        """One fused decode step of layer `layer`; returns (out [B][Hq][d], evict_idx int32 [B][Hkv])."""
+        return _step(self, int(layer), q, k_new, v_new, out, evict_idx, scores, lse)
+
+
+def _step(c, layer, q, k_new, v_new, out, evict_idx, scores, lse):
+    if not c.handle:
+        raise RuntimeError("cache is closed")
+    _need(q, "q", (c.B, c.Hq, c.d), c.dtype, c.device)
+    _need(k_new, "k_new", (c.B, c.Hkv, c.d), c.dtype, c.device)
+    _need(v_new, "v_new", (c.B, c.Hkv, c.d), c.dtype, c.device)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need(out, "out", (c.B, c.Hq, c.d), c.dtype, c.device)
+    if evict_idx is None:
+        evict_idx = torch.empty((c.B, c.Hkv), dtype=torch.int32, device=c.device)
+    else:
+        _need(evict_idx, "evict_idx", (c.B, c.Hkv), torch.int32, c.device)
+    stream = _stream_handle(c.device)
+    ptrs = (q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), c.handle)
+    if scores is not None:
+        _need(scores, "scores", (c.B, c.Hkv, c.max_budget), torch.float32, c.device)
+    if lse is not None:
+        _need(lse, "lse", (c.B, c.Hq), torch.float32, c.device)
+    sp = 0 if scores is None else scores.data_ptr()
+    lp = 0 if lse is None else lse.data_ptr()
+    if layer is None:
         if scores is None and lse is None:
-            _lib.lf_decode_step(q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), self.handle, out.data_ptr(),
-                                evict_idx.data_ptr(), stream)
+            _lib.lf_decode_step(*ptrs, out.data_ptr(), evict_idx.data_ptr(), stream)
         else:
-            if scores is not None:
-                _need(scores, "scores", (self.B, self.Hkv, self.max_budget), torch.float32, self.device)
-            if lse is not None:
-                _need(lse, "lse", (self.B, self.Hq), torch.float32, self.device)
-            _lib.lf_decode_step_dbg(q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), self.handle, out.data_ptr(),
-                                    evict_idx.data_ptr(), 0 if scores is None else scores.data_ptr(),
-                                    0 if lse is None else lse.data_ptr(), stream)
-        return out, evict_idx
-
-    def reset(self, seqs, seq_len, budgets=None) -> None:
-        """Restart sequences `seqs` in place (their K/V rows already hold the new
-        requests' cached tokens) with `seq_len` tokens seen; lf_reset_sequences,
-        or lf_reset_sequences_budget when new `budgets` are given for them."""
-        if not self.handle:
-            raise RuntimeError("cache is closed")
-        if budgets is None:
-            _lib.lf_reset_sequences(self.handle, list(seqs), list(seq_len), _stream_handle(self.device))
-            return
-        _lib.lf_reset_sequences_budget(self.handle, list(seqs), list(seq_len), list(budgets),
-                                       _stream_handle(self.device))
-        full = list(self.budgets) if self.budgets is not None else [self.max_budget] * self.B
-        for b, nb in zip(seqs, budgets):
-            full[int(b)] = int(nb)
-        self.budgets = full
-
-    def set_split_wait(self, max_wait_us: int) -> None:
-        """How long a chunk of a split pair waits for the pair's statistics
-        before handing its logits over through memory (lf_set_split_wait)."""
-        if not self.handle:
-            raise RuntimeError("cache is closed")
-        _lib.lf_set_split_wait(self.handle, int(max_wait_us))
-
-    def check_state(self):
-        """Read the state back and check its invariants (lf_check_state);
-        returns the report (deferred chunks since init, pairs)."""
-        if not self.handle:
-            raise RuntimeError("cache is closed")
-        return _lib.lf_check_state(self.handle, _stream_handle(self.device))
-
-    def close(self) -> None:
-        if self.handle:
-            _lib.lf_free(self.handle)
-            self.handle = 0
-
-    def __del__(self):
-        try:
-            self.close()
-        except Exception:
-            pass
+            _lib.lf_decode_step_dbg(*ptrs, out.data_ptr(), evict_idx.data_ptr(), sp, lp, stream)
+    elif scores is None and lse is None:
+        _lib.lf_decode_step_layer(*ptrs, layer, out.data_ptr(), evict_idx.data_ptr(), stream)
+    else:
+        _lib.lf_decode_step_layer_dbg(*ptrs, layer, out.data_ptr(), evict_idx.data_ptr(), sp, lp, stream)
+    return out, evict_idx
 
 
 def compress_prefill(q_last: torch.Tensor, k_pre: torch.Tensor, v_pre: torch.Tensor, prefill, max_budget: int,

@@ -22,11 +22,13 @@ struct lf_cache {
   uint64_t magic;
   lf_config cfg;
   int group;
-  lf::StateLayout lay;
-  void* k_cache;
-  void* v_cache;
-  char* state;
-  size_t state_bytes;  // capacity of the caller's state buffer
+  int32_t n_layers;
+  lf::StateLayout lay;            // the layout of every layer's state
+  std::vector<void*> k_cache;     // per layer
+  std::vector<void*> v_cache;
+  char* state;                    // layer l's state at state + l * layer_stride
+  size_t state_bytes;             // capacity of the caller's state buffer
+  size_t layer_stride;            // state_bytes / n_layers, rounded down to the state alignment
   float scale_log2;
   uint32_t wait_ticks;  // split chunks' wait for their pair's statistics (s_memrealtime ticks)
   int32_t u_budget;  // the common budget when every sequence has the same one, else 0
@@ -84,22 +86,22 @@ lf_status validate_config(const lf_config* cfg) {
   return LF_OK;
 }
 
-// Metadata and ring of sequence b's pairs for a cache holding `t` tokens laid
-// out as lf_init_cache describes (meta and ring indexed by pair, the other
-// PairMeta fields already set by the layout).
-void start_sequence(const lf_config& cfg, int b, int64_t t, int32_t budget, lf::PairMeta* meta, int32_t* ring) {
+// Metadata and ring of one sequence's pairs for a cache holding `t` tokens
+// laid out as lf_init_cache describes: meta_b and ring_b point at the
+// sequence's first pair (the other PairMeta fields already set by the layout).
+void start_sequence(const lf_config& cfg, int64_t t, int32_t budget, lf::PairMeta* meta_b, int32_t* ring_b) {
   const int R = cfg.recent;
   const int64_t len = t < budget ? t : budget;
   for (int g = 0; g < cfg.n_kv_heads; ++g) {
-    const int p = b * cfg.n_kv_heads + g;
-    meta[p].t = (int32_t)t;
-    meta[p].len = (int32_t)len;
-    for (int j = 0; j < R; ++j) ring[(size_t)p * R + j] = -1;
+    meta_b[g].t = (int32_t)t;
+    meta_b[g].len = (int32_t)len;
+    int32_t* ring = ring_b + (size_t)g * R;
+    for (int j = 0; j < R; ++j) ring[j] = -1;
     // The R newest cached positions [t - R, t): slot = position while the
     // prefill fits, else they are the last R slots (layout contract).
     for (int64_t pos = t - R < 0 ? 0 : t - R; pos < t; ++pos) {
       const int64_t slot = t <= budget ? pos : budget - (t - pos);
-      ring[(size_t)p * R + pos % R] = (int32_t)slot;
+      ring[pos % R] = (int32_t)slot;
     }
   }
 }
@@ -239,10 +241,12 @@ lf_status check_reset_args(const lf_cache* cache, int32_t n, const int32_t* seqs
   return LF_OK;
 }
 
-lf_status step_impl(const void* q, const void* k_new, const void* v_new, lf_cache* cache, void* out,
-                    int32_t* evict_idx, float* scores, float* lse, void* stream) {
+lf_status step_impl(const void* q, const void* k_new, const void* v_new, lf_cache* cache, int32_t layer,
+                    void* out, int32_t* evict_idx, float* scores, float* lse, void* stream) {
   lf_status st = check_handle(cache);
   if (st != LF_OK) return st;
+  if (layer < 0 || layer >= cache->n_layers)
+    return fail(LF_ERR_ARG, "layer %d outside [0, %d)", layer, cache->n_layers);
   if (!q || !k_new || !v_new || !out || !evict_idx)
     return fail(LF_ERR_ARG, "q, k_new, v_new, out and evict_idx must be non-NULL");
   const lf_config& cfg = cache->cfg;
@@ -250,13 +254,13 @@ lf_status step_impl(const void* q, const void* k_new, const void* v_new, lf_cach
   a.q = q;
   a.k_new = k_new;
   a.v_new = v_new;
-  a.k_cache = cache->k_cache;
-  a.v_cache = cache->v_cache;
+  a.k_cache = cache->k_cache[layer];
+  a.v_cache = cache->v_cache[layer];
   a.out = out;
   a.evict_idx = evict_idx;
   a.dbg_scores = scores;
   a.dbg_lse = lse;
-  char* s = cache->state;
+  char* s = cache->state + (size_t)layer * cache->layer_stride;
   const lf::StateLayout& L = cache->lay;
   a.meta = reinterpret_cast<lf::PairMeta*>(s + L.meta);
   a.ring = reinterpret_cast<int32_t*>(s + L.ring);
@@ -349,6 +353,95 @@ lf_status prefill_impl(const lf_config* cfg, const int32_t* budgets, const int32
   return LF_OK;
 }
 
+constexpr int32_t kMaxLayers = 4096;
+
+// lf_init_cache over n_layers layer caches sharing the configuration and the
+// budgets: every layer's state has the same layout, layer l's at
+// state + l * stride with stride = state_bytes / n_layers rounded down to
+// the state alignment (so a later budget change never moves a layer).
+lf_status init_impl(const lf_config* cfg, int32_t n_layers, const int32_t* budgets, const int64_t* seq_len,
+                    void* const* k_caches, void* const* v_caches, void* state, size_t state_bytes, int32_t flags,
+                    void* stream, lf_cache** out) {
+  lf_status st = validate_config(cfg);
+  if (st != LF_OK) return st;
+  if (!out) return fail(LF_ERR_ARG, "out is NULL");
+  *out = nullptr;
+  if (n_layers < 1 || n_layers > kMaxLayers) return fail(LF_ERR_ARG, "n_layers %d outside [1, %d]", n_layers, kMaxLayers);
+  if (!seq_len || !state) return fail(LF_ERR_ARG, "seq_len and state must be non-NULL");
+  for (int l = 0; l < n_layers; ++l) {
+    if (!k_caches[l] || !v_caches[l])
+      return fail(LF_ERR_ARG, n_layers == 1 ? "k_cache and v_cache must be non-NULL"
+                                            : "k_caches[%d] and v_caches[%d] must be non-NULL", l, l);
+    if (reinterpret_cast<uintptr_t>(k_caches[l]) % 16 || reinterpret_cast<uintptr_t>(v_caches[l]) % 16)
+      return fail(LF_ERR_ARG, "k_cache and v_cache must be 16-byte aligned (layer %d)", l);
+  }
+  if (flags & ~LF_INIT_ATTACH) return fail(LF_ERR_ARG, "unknown flags 0x%x", (unsigned)flags);
+  if (reinterpret_cast<uintptr_t>(state) % lf::kAlign) return fail(LF_ERR_ARG, "state must be 256-byte aligned");
+  std::vector<int32_t> bud;
+  if ((st = validate_budgets(cfg, budgets, bud)) != LF_OK) return st;
+  for (int b = 0; b < cfg->batch; ++b)
+    if (seq_len[b] < 0 || seq_len[b] > 0x7FFFFFFFll - 0x10000000ll)
+      return fail(LF_ERR_ARG, "seq_len[%d] = %lld out of range", b, (long long)seq_len[b]);
+  lf::StateLayout L{};
+  std::vector<lf::WorkItem> items;
+  std::vector<lf::PairMeta> meta;
+  if ((st = make_layout(cfg, bud, L, &items, &meta)) != LF_OK) return st;
+  const size_t stride = state_bytes / (size_t)n_layers / lf::kAlign * lf::kAlign;
+  if (stride < L.total)
+    return fail(LF_ERR_ARG, "state_bytes %zu < %d layer(s) x %zu (see lf_state_bytes / lf_state_bytes_layers)",
+                state_bytes, n_layers, L.total);
+
+  if (!(flags & LF_INIT_ATTACH)) {
+    // Host image of header, meta, ring, work list and the zeroed exchange
+    // cells (no stale epoch tag may survive), the same for every layer.
+    std::vector<char> img(L.logits, 0);
+    lf::StateHeader h{lf::kStateMagic, L.n_pairs, L.n_items, L.total_slots, 0, 0, {0, 0}};
+    std::memcpy(img.data() + L.header, &h, sizeof(h));
+    int32_t* ring = reinterpret_cast<int32_t*>(img.data() + L.ring);
+    const int H = cfg->n_kv_heads;
+    for (int b = 0; b < cfg->batch; ++b)
+      start_sequence(*cfg, seq_len[b], bud[b], meta.data() + (size_t)b * H, ring + (size_t)b * H * cfg->recent);
+    std::memcpy(img.data() + L.meta, meta.data(), sizeof(lf::PairMeta) * meta.size());
+    std::memcpy(img.data() + L.items, items.data(), sizeof(lf::WorkItem) * items.size());
+    for (int l = 0; l < n_layers; ++l)
+      if (lf::upload_and_wait(static_cast<char*>(state) + (size_t)l * stride, img.data(), img.size(), stream, g_err,
+                              sizeof(g_err)))
+        return LF_ERR_HIP;
+  }
+
+  lf_cache* c = new (std::nothrow) lf_cache;
+  if (!c) return fail(LF_ERR_ARG, "out of host memory");
+  c->magic = lf::kHandleMagic;
+  c->cfg = *cfg;
+  c->group = cfg->n_q_heads / cfg->n_kv_heads;
+  c->n_layers = n_layers;
+  c->lay = L;
+  c->u_budget = bud[0];
+  for (int b = 1; b < cfg->batch; ++b)
+    if (bud[b] != bud[0]) c->u_budget = 0;
+  c->budgets = bud;
+  c->k_cache.assign(k_caches, k_caches + n_layers);
+  c->v_cache.assign(v_caches, v_caches + n_layers);
+  c->state = static_cast<char*>(state);
+  c->state_bytes = state_bytes;
+  c->layer_stride = stride;
+  c->wait_ticks = kDefaultWaitTicks;
+  const double scale = cfg->softmax_scale > 0 ? cfg->softmax_scale : 1.0 / std::sqrt((double)cfg->head_dim);
+  c->scale_log2 = (float)(scale * 1.4426950408889634);
+  *out = c;
+  g_err[0] = 0;
+  return LF_OK;
+}
+
+// lf_decode_step(_dbg) take single-layer handles only.
+lf_status check_single_layer(const lf_cache* c) {
+  lf_status st = check_handle(c);
+  if (st != LF_OK) return st;
+  if (c->n_layers != 1)
+    return fail(LF_ERR_ARG, "the handle spans %d layers: use lf_decode_step_layer", c->n_layers);
+  return LF_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -370,74 +463,52 @@ lf_status lf_state_bytes(const lf_config* cfg, const int32_t* budgets, size_t* b
   return LF_OK;
 }
 
+lf_status lf_state_bytes_layers(const lf_config* cfg, const int32_t* budgets, int32_t n_layers, size_t* bytes) {
+  if (n_layers < 1 || n_layers > kMaxLayers) return fail(LF_ERR_ARG, "n_layers %d outside [1, %d]", n_layers, kMaxLayers);
+  size_t one = 0;
+  lf_status st = lf_state_bytes(cfg, budgets, &one);
+  if (st != LF_OK) return st;
+  *bytes = one * (size_t)n_layers;  // each layer's state is a multiple of the alignment
+  return LF_OK;
+}
+
 lf_status lf_init_cache(const lf_config* cfg, const int32_t* budgets, const int64_t* seq_len, void* k_cache,
                         void* v_cache, void* state, size_t state_bytes, int32_t flags, void* stream,
                         lf_cache** out) {
-  lf_status st = validate_config(cfg);
-  if (st != LF_OK) return st;
-  if (!out) return fail(LF_ERR_ARG, "out is NULL");
-  *out = nullptr;
-  if (!seq_len || !k_cache || !v_cache || !state)
-    return fail(LF_ERR_ARG, "seq_len, k_cache, v_cache and state must be non-NULL");
-  if (flags & ~LF_INIT_ATTACH) return fail(LF_ERR_ARG, "unknown flags 0x%x", (unsigned)flags);
-  if (reinterpret_cast<uintptr_t>(state) % lf::kAlign) return fail(LF_ERR_ARG, "state must be 256-byte aligned");
-  if (reinterpret_cast<uintptr_t>(k_cache) % 16 || reinterpret_cast<uintptr_t>(v_cache) % 16)
-    return fail(LF_ERR_ARG, "k_cache and v_cache must be 16-byte aligned");
-  std::vector<int32_t> bud;
-  if ((st = validate_budgets(cfg, budgets, bud)) != LF_OK) return st;
-  for (int b = 0; b < cfg->batch; ++b)
-    if (seq_len[b] < 0 || seq_len[b] > 0x7FFFFFFFll - 0x10000000ll)
-      return fail(LF_ERR_ARG, "seq_len[%d] = %lld out of range", b, (long long)seq_len[b]);
-  lf::StateLayout L{};
-  std::vector<lf::WorkItem> items;
-  std::vector<lf::PairMeta> meta;
-  if ((st = make_layout(cfg, bud, L, &items, &meta)) != LF_OK) return st;
-  if (state_bytes < L.total)
-    return fail(LF_ERR_ARG, "state_bytes %zu < required %zu (see lf_state_bytes)", state_bytes, L.total);
+  return init_impl(cfg, 1, budgets, seq_len, &k_cache, &v_cache, state, state_bytes, flags, stream, out);
+}
 
-  if (!(flags & LF_INIT_ATTACH)) {
-    // Host image of header, meta, ring, work list and the zeroed exchange
-    // cells (no stale epoch tag may survive), uploaded in one copy.
-    std::vector<char> img(L.logits, 0);
-    lf::StateHeader h{lf::kStateMagic, L.n_pairs, L.n_items, L.total_slots, 0, 0, {0, 0}};
-    std::memcpy(img.data() + L.header, &h, sizeof(h));
-    int32_t* ring = reinterpret_cast<int32_t*>(img.data() + L.ring);
-    for (int b = 0; b < cfg->batch; ++b) start_sequence(*cfg, b, seq_len[b], bud[b], meta.data(), ring);
-    std::memcpy(img.data() + L.meta, meta.data(), sizeof(lf::PairMeta) * meta.size());
-    std::memcpy(img.data() + L.items, items.data(), sizeof(lf::WorkItem) * items.size());
-    if (lf::upload_and_wait(state, img.data(), img.size(), stream, g_err, sizeof(g_err))) return LF_ERR_HIP;
-  }
-
-  lf_cache* c = new (std::nothrow) lf_cache;
-  if (!c) return fail(LF_ERR_ARG, "out of host memory");
-  c->magic = lf::kHandleMagic;
-  c->cfg = *cfg;
-  c->group = cfg->n_q_heads / cfg->n_kv_heads;
-  c->lay = L;
-  c->u_budget = bud[0];
-  for (int b = 1; b < cfg->batch; ++b)
-    if (bud[b] != bud[0]) c->u_budget = 0;
-  c->budgets = bud;
-  c->k_cache = k_cache;
-  c->v_cache = v_cache;
-  c->state = static_cast<char*>(state);
-  c->state_bytes = state_bytes;
-  c->wait_ticks = kDefaultWaitTicks;
-  const double scale = cfg->softmax_scale > 0 ? cfg->softmax_scale : 1.0 / std::sqrt((double)cfg->head_dim);
-  c->scale_log2 = (float)(scale * 1.4426950408889634);
-  *out = c;
-  g_err[0] = 0;
-  return LF_OK;
+lf_status lf_init_layers(const lf_config* cfg, int32_t n_layers, const int32_t* budgets, const int64_t* seq_len,
+                         void* const* k_caches, void* const* v_caches, void* state, size_t state_bytes,
+                         int32_t flags, void* stream, lf_cache** out) {
+  if (out) *out = nullptr;
+  if (!k_caches || !v_caches) return fail(LF_ERR_ARG, "k_caches and v_caches must be non-NULL");
+  return init_impl(cfg, n_layers, budgets, seq_len, k_caches, v_caches, state, state_bytes, flags, stream, out);
 }
 
 lf_status lf_decode_step(const void* q, const void* k_new, const void* v_new, lf_cache* cache, void* out,
                          int32_t* evict_idx, void* stream) {
-  return step_impl(q, k_new, v_new, cache, out, evict_idx, nullptr, nullptr, stream);
+  lf_status st = check_single_layer(cache);
+  if (st != LF_OK) return st;
+  return step_impl(q, k_new, v_new, cache, 0, out, evict_idx, nullptr, nullptr, stream);
 }
 
 lf_status lf_decode_step_dbg(const void* q, const void* k_new, const void* v_new, lf_cache* cache, void* out,
                              int32_t* evict_idx, float* scores, float* lse, void* stream) {
-  return step_impl(q, k_new, v_new, cache, out, evict_idx, scores, lse, stream);
+  lf_status st = check_single_layer(cache);
+  if (st != LF_OK) return st;
+  return step_impl(q, k_new, v_new, cache, 0, out, evict_idx, scores, lse, stream);
+}
+
+lf_status lf_decode_step_layer(const void* q, const void* k_new, const void* v_new, lf_cache* cache, int32_t layer,
+                               void* out, int32_t* evict_idx, void* stream) {
+  return step_impl(q, k_new, v_new, cache, layer, out, evict_idx, nullptr, nullptr, stream);
+}
+
+lf_status lf_decode_step_layer_dbg(const void* q, const void* k_new, const void* v_new, lf_cache* cache,
+                                   int32_t layer, void* out, int32_t* evict_idx, float* scores, float* lse,
+                                   void* stream) {
+  return step_impl(q, k_new, v_new, cache, layer, out, evict_idx, scores, lse, stream);
 }
 
 void lf_free(lf_cache* cache) {
@@ -462,54 +533,69 @@ lf_status lf_check_state(const lf_cache* cache, void* stream, lf_state_report* r
   if (!report) return fail(LF_ERR_ARG, "report is NULL");
   const lf_config& cfg = cache->cfg;
   const lf::StateLayout& L = cache->lay;
-  std::vector<char> img(L.items);
-  if (lf::download_and_wait(img.data(), cache->state, L.items, stream, g_err, sizeof(g_err))) return LF_ERR_HIP;
-  const lf::StateHeader* h = reinterpret_cast<const lf::StateHeader*>(img.data() + L.header);
-  report->deferred = h->deferred;
+  const int NL = cache->n_layers;
+  // Everything before the work list, of every layer.
+  std::vector<char> all((size_t)NL * L.items);
+  if (lf::copy_rows_and_wait(all.data(), L.items, cache->state, cache->layer_stride, L.items, NL, false, stream, g_err,
+                             sizeof(g_err)))
+    return LF_ERR_HIP;
+  report->deferred = 0;
   report->n_pairs = L.n_pairs;
   report->bad_pair = -1;
-  report->reserved = 0;
-  if (h->magic != lf::kStateMagic || h->n_pairs != L.n_pairs || h->n_items != L.n_items)
-    return fail(LF_ERR_STATE, "state header does not match the handle (magic 0x%08x, %d pairs, %d items)", h->magic,
-                h->n_pairs, h->n_items);
-  if (h->fault)
-    return fail(LF_ERR_STATE, "a step's wait for another workgroup's published words hit its safety bound "
-                "(fault bits 0x%x: 1 statistics, 2 value sums, 4 candidates); results since are not valid", h->fault);
+  report->bad_layer = -1;
+  for (int l = 0; l < NL; ++l)
+    report->deferred += reinterpret_cast<const lf::StateHeader*>(all.data() + (size_t)l * L.items + L.header)->deferred;
   lf::StateLayout L2{};
   std::vector<lf::PairMeta> want;
   if ((st = make_layout(&cfg, cache->budgets, L2, nullptr, &want)) != LF_OK) return st;
-  const lf::PairMeta* meta = reinterpret_cast<const lf::PairMeta*>(img.data() + L.meta);
-  const int32_t* ring = reinterpret_cast<const int32_t*>(img.data() + L.ring);
-  const uint32_t* count = reinterpret_cast<const uint32_t*>(img.data() + L.count);
   const int R = cfg.recent;
   std::vector<char> seen;
-  for (int p = 0; p < L.n_pairs; ++p) {
-    const lf::PairMeta& m = meta[p];
-    const lf::PairMeta& w = want[p];
-    const char* why = nullptr;
-    if (m.budget != w.budget || m.nchunk != w.nchunk || m.item0 != w.item0 || m.slot0 != w.slot0 ||
-        m.lstride != w.lstride)
-      why = "layout fields differ from the handle's";
-    else if (m.t < 0 || m.len != (m.t < m.budget ? m.t : m.budget))
-      why = "fill level is not min(position, budget)";
-    else if (m.epoch == 0)
-      why = "epoch is 0";
-    else if (count[p] != 0)
-      why = "chunk counter is not 0 between steps";
-    if (!why && R > 0) {
-      seen.assign(m.budget, 0);
-      for (int64_t pos = m.t - R < 0 ? 0 : m.t - R; pos < m.t && !why; ++pos) {
-        const int32_t sl = ring[(size_t)p * R + pos % R];
-        if (sl < 0 || sl >= m.len)
-          why = "a recent position's slot is outside the filled slots";
-        else if (seen[sl]++)
-          why = "two recent positions share a slot";
-      }
+  for (int l = 0; l < NL; ++l) {
+    const char* img = all.data() + (size_t)l * L.items;
+    const lf::StateHeader* h = reinterpret_cast<const lf::StateHeader*>(img + L.header);
+    if (h->magic != lf::kStateMagic || h->n_pairs != L.n_pairs || h->n_items != L.n_items) {
+      report->bad_layer = l;
+      return fail(LF_ERR_STATE, "layer %d: state header does not match the handle (magic 0x%08x, %d pairs, %d items)",
+                  l, h->magic, h->n_pairs, h->n_items);
     }
-    if (why) {
-      report->bad_pair = p;
-      return fail(LF_ERR_STATE, "pair %d (sequence %d, KV head %d): %s", p, p / cfg.n_kv_heads, p % cfg.n_kv_heads,
-                  why);
+    if (h->fault) {
+      report->bad_layer = l;
+      return fail(LF_ERR_STATE, "layer %d: a step's wait for another workgroup's published words hit its safety "
+                  "bound (fault bits 0x%x: 1 statistics, 2 value sums, 4 candidates); results since are not valid",
+                  l, h->fault);
+    }
+    const lf::PairMeta* meta = reinterpret_cast<const lf::PairMeta*>(img + L.meta);
+    const int32_t* ring = reinterpret_cast<const int32_t*>(img + L.ring);
+    const uint32_t* count = reinterpret_cast<const uint32_t*>(img + L.count);
+    for (int p = 0; p < L.n_pairs; ++p) {
+      const lf::PairMeta& m = meta[p];
+      const lf::PairMeta& w = want[p];
+      const char* why = nullptr;
+      if (m.budget != w.budget || m.nchunk != w.nchunk || m.item0 != w.item0 || m.slot0 != w.slot0 ||
+          m.lstride != w.lstride)
+        why = "layout fields differ from the handle's";
+      else if (m.t < 0 || m.len != (m.t < m.budget ? m.t : m.budget))
+        why = "fill level is not min(position, budget)";
+      else if (m.epoch == 0)
+        why = "epoch is 0";
+      else if (count[p] != 0)
+        why = "chunk counter is not 0 between steps";
+      if (!why && R > 0) {
+        seen.assign(m.budget, 0);
+        for (int64_t pos = m.t - R < 0 ? 0 : m.t - R; pos < m.t && !why; ++pos) {
+          const int32_t sl = ring[(size_t)p * R + pos % R];
+          if (sl < 0 || sl >= m.len)
+            why = "a recent position's slot is outside the filled slots";
+          else if (seen[sl]++)
+            why = "two recent positions share a slot";
+        }
+      }
+      if (why) {
+        report->bad_pair = p;
+        report->bad_layer = l;
+        return fail(LF_ERR_STATE, "layer %d, pair %d (sequence %d, KV head %d): %s", l, p, p / cfg.n_kv_heads,
+                    p % cfg.n_kv_heads, why);
+      }
     }
   }
   g_err[0] = 0;
@@ -521,26 +607,26 @@ lf_status lf_reset_sequences(lf_cache* cache, int32_t n, const int32_t* seqs, co
   lf_status st = check_reset_args(cache, n, seqs, seq_len);
   if (st != LF_OK || n == 0) return st;
   const lf_config& cfg = cache->cfg;
-  lf::StateLayout L{};
-  std::vector<lf::PairMeta> meta;
-  if ((st = make_layout(&cfg, cache->budgets, L, nullptr, &meta)) != LF_OK) return st;
-  const int H = cfg.n_kv_heads, R = cfg.recent;
-  std::vector<int32_t> ring((size_t)L.n_pairs * (R > 0 ? R : 1));
+  const lf::StateLayout& L = cache->lay;
+  const int H = cfg.n_kv_heads, R = cfg.recent, NL = cache->n_layers;
+  const size_t stride = cache->layer_stride, mrow = sizeof(lf::PairMeta) * H, rrow = sizeof(int32_t) * H * R;
+  std::vector<lf::PairMeta> meta((size_t)NL * H);  // [layer][KV head] of one sequence
+  std::vector<int32_t> ring((size_t)NL * H * (R > 0 ? R : 1));
   for (int i = 0; i < n; ++i) {
     const int b = seqs[i];
-    // The pairs' epochs tag their exchange cells: read the metadata back so
-    // they carry on (a restarted epoch could match a stale tag).
-    if (lf::download_and_wait(meta.data() + (size_t)b * H, cache->state + L.meta + sizeof(lf::PairMeta) * (size_t)b * H,
-                              sizeof(lf::PairMeta) * H, stream, g_err, sizeof(g_err)))
+    // The pairs' epochs tag their exchange cells: read the metadata back (every
+    // layer's rows of this sequence, one strided copy) so they carry on (a
+    // restarted epoch could match a stale tag).  A sequence's pairs are
+    // contiguous in the metadata and in the ring.
+    char* m0 = cache->state + L.meta + mrow * b;
+    char* r0 = cache->state + L.ring + rrow * b;
+    if (lf::copy_rows_and_wait(meta.data(), mrow, m0, stride, mrow, NL, false, stream, g_err, sizeof(g_err)))
       return LF_ERR_HIP;
-    start_sequence(cfg, b, seq_len[i], cache->budgets[b], meta.data(), ring.data());
-    // A sequence's pairs are contiguous in the metadata and in the ring.
-    if (lf::upload_and_wait(cache->state + L.meta + sizeof(lf::PairMeta) * (size_t)b * H, meta.data() + (size_t)b * H,
-                            sizeof(lf::PairMeta) * H, stream, g_err, sizeof(g_err)))
+    for (int l = 0; l < NL; ++l)
+      start_sequence(cfg, seq_len[i], cache->budgets[b], meta.data() + (size_t)l * H, ring.data() + (size_t)l * H * R);
+    if (lf::copy_rows_and_wait(m0, stride, meta.data(), mrow, mrow, NL, true, stream, g_err, sizeof(g_err)))
       return LF_ERR_HIP;
-    if (R > 0 && lf::upload_and_wait(cache->state + L.ring + sizeof(int32_t) * (size_t)b * H * R,
-                                     ring.data() + (size_t)b * H * R, sizeof(int32_t) * H * R, stream, g_err,
-                                     sizeof(g_err)))
+    if (R > 0 && lf::copy_rows_and_wait(r0, stride, ring.data(), rrow, rrow, NL, true, stream, g_err, sizeof(g_err)))
       return LF_ERR_HIP;
   }
   g_err[0] = 0;
@@ -561,33 +647,63 @@ lf_status lf_reset_sequences_budget(lf_cache* cache, int32_t n, const int32_t* s
   std::vector<lf::WorkItem> items;
   std::vector<lf::PairMeta> meta;
   if ((st = make_layout(&cfg, nb, L, &items, &meta)) != LF_OK) return st;
-  if (L.total > cache->state_bytes)
-    return fail(LF_ERR_ARG, "the new budgets need %zu state bytes, the buffer holds %zu", L.total,
-                cache->state_bytes);
+  if (L.total > cache->layer_stride)
+    return fail(LF_ERR_ARG, "the new budgets need %zu state bytes per layer, the buffer holds %zu per layer", L.total,
+                cache->layer_stride);
   // Header, metadata and rings lie before the work list at offsets that depend
   // only on the numbers of pairs and ring entries, so the old and the new
-  // layout place them alike.  Read them back (after the queued steps), keep
-  // every other sequence's position, fill level and ring, restart the listed
-  // ones, and write header, metadata, rings and the new work list back.
+  // layout place them alike.  Read them back for every layer (after the queued
+  // steps), keep every other sequence's position, fill level and ring, restart
+  // the listed ones, and write header, metadata, rings, chunk counters and the
+  // new work list back.
   const lf::StateLayout& old = cache->lay;
-  // The new work list moves the exchange cells: they are zeroed (no stale
-  // epoch tag may survive); the pairs' epochs and the chunk counters carry on.
-  std::vector<char> img(L.logits, 0);
-  if (lf::download_and_wait(img.data(), cache->state, old.items, stream, g_err, sizeof(g_err))) return LF_ERR_HIP;
-  const lf::PairMeta* cur = reinterpret_cast<const lf::PairMeta*>(img.data() + L.meta);
-  for (int p = 0; p < L.n_pairs; ++p) {
-    meta[p].t = cur[p].t;
-    meta[p].len = cur[p].len;
-    meta[p].epoch = cur[p].epoch;
+  const int NL = cache->n_layers;
+  const size_t stride = cache->layer_stride;
+  // The new work list moves the exchange cells.  Instead of clearing them, the
+  // pairs of a layer continue from one epoch past the largest of the layer:
+  // every word in the cells was written under an epoch below that, so none
+  // can look fresh.  Only at the end of the epoch range are the cells zeroed.
+  std::vector<char> img((size_t)NL * L.xcell, 0);
+  if (lf::copy_rows_and_wait(img.data(), L.xcell, cache->state, stride, old.items, NL, false, stream, g_err,
+                             sizeof(g_err)))
+    return LF_ERR_HIP;
+  bool wrap = false;
+  for (int l = 0; l < NL && !wrap; ++l) {
+    const lf::PairMeta* cur = reinterpret_cast<const lf::PairMeta*>(img.data() + (size_t)l * L.xcell + L.meta);
+    for (int p = 0; p < L.n_pairs; ++p) wrap = wrap || cur[p].epoch == 0xFFFFFFFFu;
   }
-  int32_t* ring = reinterpret_cast<int32_t*>(img.data() + L.ring);
-  for (int i = 0; i < n; ++i) start_sequence(cfg, seqs[i], seq_len[i], nb[seqs[i]], meta.data(), ring);
-  const lf::StateHeader* oldh = reinterpret_cast<const lf::StateHeader*>(img.data() + L.header);
-  lf::StateHeader h{lf::kStateMagic, L.n_pairs, L.n_items, L.total_slots, oldh->deferred, oldh->fault, {0, 0}};
-  std::memcpy(img.data() + L.header, &h, sizeof(h));
-  std::memcpy(img.data() + L.meta, meta.data(), sizeof(lf::PairMeta) * meta.size());
-  std::memcpy(img.data() + L.items, items.data(), sizeof(lf::WorkItem) * items.size());
-  if (lf::upload_and_wait(cache->state, img.data(), img.size(), stream, g_err, sizeof(g_err))) return LF_ERR_HIP;
+  for (int l = 0; l < NL; ++l) {
+    char* li = img.data() + (size_t)l * L.xcell;
+    const lf::PairMeta* cur = reinterpret_cast<const lf::PairMeta*>(li + L.meta);
+    uint32_t top = 0;
+    for (int p = 0; p < L.n_pairs; ++p) top = cur[p].epoch > top ? cur[p].epoch : top;
+    std::vector<lf::PairMeta> lm = meta;
+    for (int p = 0; p < L.n_pairs; ++p) {
+      lm[p].t = cur[p].t;
+      lm[p].len = cur[p].len;
+      lm[p].epoch = wrap ? 1u : top + 1u;
+    }
+    int32_t* ring = reinterpret_cast<int32_t*>(li + L.ring);
+    const int H = cfg.n_kv_heads, R = cfg.recent;
+    for (int i = 0; i < n; ++i)
+      start_sequence(cfg, seq_len[i], nb[seqs[i]], lm.data() + (size_t)seqs[i] * H, ring + (size_t)seqs[i] * H * R);
+    const lf::StateHeader* oldh = reinterpret_cast<const lf::StateHeader*>(li + L.header);
+    lf::StateHeader h{lf::kStateMagic, L.n_pairs, L.n_items, L.total_slots, oldh->deferred, oldh->fault, {0, 0}};
+    std::memcpy(li + L.header, &h, sizeof(h));
+    std::memcpy(li + L.meta, lm.data(), sizeof(lf::PairMeta) * lm.size());
+    std::memset(li + L.count, 0, sizeof(uint32_t) * L.n_pairs);
+    std::memcpy(li + L.items, items.data(), sizeof(lf::WorkItem) * items.size());
+  }
+  if (lf::copy_rows_and_wait(cache->state, stride, img.data(), L.xcell, L.xcell, NL, true, stream, g_err,
+                             sizeof(g_err)))
+    return LF_ERR_HIP;
+  if (wrap) {
+    // Zeroed exchange cells for the restarted epochs.
+    std::vector<char> zero((size_t)NL * (L.logits - L.xcell), 0);
+    if (lf::copy_rows_and_wait(cache->state + L.xcell, stride, zero.data(), L.logits - L.xcell, L.logits - L.xcell, NL,
+                               true, stream, g_err, sizeof(g_err)))
+      return LF_ERR_HIP;
+  }
   cache->lay = L;
   cache->budgets = nb;
   cache->u_budget = nb[0];

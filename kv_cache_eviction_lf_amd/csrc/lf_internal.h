@@ -151,5 +151,10 @@ int launch_prefill(int dtype, int head_dim, const PrefillArgs& a, int n_pairs, v
 int prefill_scratch(void** ptr, char* err, size_t errlen);
 int upload_and_wait(void* dst, const void* src, size_t bytes, void* stream, char* err, size_t errlen);
 int download_and_wait(void* dst, const void* src, size_t bytes, void* stream, char* err, size_t errlen);
+// `rows` rows of `width` bytes, row r from src + r * spitch to dst + r * dpitch
+// (host to device when to_device, else device to host), ordered on `stream`;
+// returns once the copy completed.  0 on success.
+int copy_rows_and_wait(void* dst, size_t dpitch, const void* src, size_t spitch, size_t width, size_t rows,
+                       bool to_device, void* stream, char* err, size_t errlen);
 
 }  // namespace lf

@@ -316,7 +316,8 @@ __device__ __forceinline__ float qk_part(const QReg<T, G>& q, int h, const uint4
 
 // (score, slot) lexicographic minimum of two candidates.
 __device__ __forceinline__ void argmin_merge(float& s, int& i, float so, int io) {
-  const bool lt = so < s || (so == s && io < i);  // selects, no branch
+  // Bitwise, not short-circuit: the compiler keeps it free of branches.
+  const bool lt = (so < s) | ((so == s) & (io < i));
   s = lt ? so : s;
   i = lt ? io : i;
 }
@@ -441,35 +442,49 @@ __device__ __forceinline__ float wave_sum(float x) {
 // head; masked (filled, past the sink window, not among the recent slots) into
 // the running first-index minimum.  Optionally exports every filled slot's
 // score.
-template <int G>
-__device__ __forceinline__ void score4(int base, const float4 (&lv)[G], const float (&M)[G], const float (&invL)[G],
-                                       float ls, const uint32_t* s_bits, int sink, int len, float* dbg, float& best,
-                                       int& besti) {
+template <int G, int NR>
+__device__ __forceinline__ void score_rows(int base, const float (&lv)[G][NR], const float (&M)[G],
+                                           const float (&invL)[G], float ls, const uint32_t* s_bits, int sink, int len,
+                                           float* dbg, float& best, int& besti) {
+  static_assert(NR == 1 || NR == 2 || NR == 4, "rows per call: base is a multiple of NR");
   const uint32_t bits = s_bits[base >> 5] >> (base & 31);
-  float sc[4] = {0.f, 0.f, 0.f, 0.f};
+  float sc[NR];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    sc[0] = fmaf(fast_exp2(fmaf(lv[h].x, ls, -M[h])), invL[h], sc[0]);
-    sc[1] = fmaf(fast_exp2(fmaf(lv[h].y, ls, -M[h])), invL[h], sc[1]);
-    sc[2] = fmaf(fast_exp2(fmaf(lv[h].z, ls, -M[h])), invL[h], sc[2]);
-    sc[3] = fmaf(fast_exp2(fmaf(lv[h].w, ls, -M[h])), invL[h], sc[3]);
-  }
+  for (int j = 0; j < NR; ++j) sc[j] = 0.f;
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int j = 0; j < NR; ++j) sc[j] = fmaf(fast_exp2(fmaf(lv[h][j], ls, -M[h])), invL[h], sc[j]);
   if (dbg) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NR; ++j)
       if (base + j < len) dbg[base + j] = sc[j];
   }
   // Branch-free masked minimum; slots increase per thread, so the strict
   // comparison keeps the first index on ties.
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < NR; ++j) {
     const int i = base + j;
-    const bool ok = i < len && i >= sink && !((bits >> j) & 1u);
+    const bool ok = (i < len) & (i >= sink) & !((bits >> j) & 1u);
     const float v = ok ? sc[j] : INFINITY;
     const bool lt = v < best;
     best = lt ? v : best;
     besti = lt ? i : besti;
   }
+}
+template <int G>
+__device__ __forceinline__ void score4(int base, const float4 (&lv)[G], const float (&M)[G], const float (&invL)[G],
+                                       float ls, const uint32_t* s_bits, int sink, int len, float* dbg, float& best,
+                                       int& besti) {
+  float x[G][4];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    x[h][0] = lv[h].x;
+    x[h][1] = lv[h].y;
+    x[h][2] = lv[h].z;
+    x[h][3] = lv[h].w;
+  }
+  score_rows<G, 4>(base, x, M, invL, ls, s_bits, sink, len, dbg, best, besti);
 }
 
 // Logit of the incoming token for every head of the group (every lane holds
@@ -1019,14 +1034,14 @@ __device__ __forceinline__ bool pair_stats_all(const StepArgs& a, int item0, int
   if ((G << k) > 64) {
     if (!pair_stats<D, G>(a, item0, nchunk, epoch, snew, own, s_part_w, bounded, deadline, M, L, wl)) return false;
 #pragma unroll
-    for (int h = 0; h < G; ++h) invL[h] = 1.0f / L[h];
+    for (int h = 0; h < G; ++h) invL[h] = __builtin_amdgcn_rcpf(L[h]);
     return true;
   }
   float Mh, Lh, w;
   if (!pair_stats_hc<D, G>(a, item0, nchunk, k, epoch, s_snew, own, s_part_w, bounded, deadline, Mh, Lh, w))
     return false;
   const int lane = threadIdx.x & 63;
-  const float il = 1.0f / Lh;  // one division per lane, read back per head
+  const float il = __builtin_amdgcn_rcpf(Lh);  // one reciprocal per lane, read back per head
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     M[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Mh), h << k));
@@ -1187,46 +1202,102 @@ __device__ __forceinline__ void finish_deferred(const StepArgs& a, int pair, con
   if (wave == 0) insert_token<T, D>(a, pair, pm, besti, insert_piece<T, D, G>(a, pair, s_pre), true);
 }
 
+// A wave's count of waves that are done with something (workgroup scope):
+// waits until it reaches n, with the safety bound of lds_wait.
+__device__ __forceinline__ void lds_wait_count(uint32_t* f, uint32_t n, const StepArgs& a) {
+  const uint64_t deadline = __builtin_amdgcn_s_memrealtime() + kSafetyTicks;
+  while (__hip_atomic_load(f, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < n) {
+    if (__builtin_amdgcn_s_memrealtime() > deadline) {
+      if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_or(a.fault, kFaultValues, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+__device__ __forceinline__ void lds_count(uint32_t* f) {
+  if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_add(f, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
 // End of the step for one chunk of a split pair (see the protocol above).
 // s_work holds the waves' partials [wave][G][D + 2] and the bitmap area,
-// s_logit the streaming waves' logits when lmode == kLogitsFull; s_flags
-// (LDS, zeroed at workgroup start) carries the hand-overs between the waves:
-// [0] bitmap ready, [1] statistics seen (1) or not (2), [2] finisher done (1)
-// or deferred chunks to finish (2), [3 ..] the finisher's fast minimum.
-// Wave 0 alone runs the critical path (statistics, scoring, ticket, finish);
-// waves 1-3 build the bitmap, publish the partial and write the output rows.
+// s_logit the streaming waves' logits when lmode == kLogitsFull, s_stat
+// (bf16) the incoming token's logits from the stream.  s_flags (LDS, zeroed
+// at workgroup start) carries the hand-overs between the waves: [0] bitmap
+// ready, [1] statistics seen (1) or not (2), [2] finisher done (1) or
+// deferred chunks to finish (2), [3 .. 6] the finisher's fast minimum, [7]
+// the deferred ticket, [8] waves 1-3 done scoring.
+// Wave 0 runs the critical path (statistics, ticket, finish); every wave
+// scores a share of the chunk's slots; waves 1-3 build the bitmap, publish the
+// partial and write the output rows.
 template <class T, int D, int G>
 __device__ __forceinline__ void split_tail(const StepArgs& a, int pair, int item, int start, int count,
                                            const PairMeta& pm, int lmode, float* s_work, const float* s_logit,
-                                           const float* s_pre, uint32_t* s_flags) {
+                                           const float* s_pre, uint32_t* s_flags, float* s_stat) {
   using S = Shape<T, D, G>;
-  constexpr int kMaxOwnHeads = (G + 1) / 2;  // output heads of one chunk (2 chunks or more)
+  using elem = typename T::elem;
+  constexpr int kOutPre = 4;  // chunks whose value sums the output requests before scoring
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
   const int nchunk = pm.nchunk, item0 = pm.item0, chunk = item - item0, len = pm.len, budget = pm.budget;
   const uint32_t epoch = pm.epoch;
   uint32_t* s_bits = reinterpret_cast<uint32_t*>(s_work + S::kBitsOffset);
   float* s_arg = s_work + S::kBitsOffset + kMaxBudget / 32;  // [kWaves] score, [kWaves] slot
-  // the new token's logit, max, normaliser and its inverse per head, then
-  // every chunk's weight for this chunk's output heads
-  __shared__ float s_stat[4 * G + kMaxOwnHeads * kMaxChunks];
   const uint32_t my_heads = heads_of<G>(chunk, nchunk);
   // Chunks whose logits stayed on chip wait for the pair's statistics (unless
   // waiting is switched off).
   const bool can_wait = a.wait_ticks > 0 && (a.score_none || lmode == kLogitsFull);
   int own_c = -1;  // >= 0: the fast path's finisher has deferred chunks to finish (every wave joins)
 
+  // This thread's share of the chunk's slots (2 per thread and pass, from the
+  // logits the streaming waves kept in LDS: slot s of stream wave
+  // w = (s - start) / quarter at row s - start - w * quarter), scored with the
+  // step's statistics from s_stat, into a wave minimum.
+  auto score_share = [&](float& best, int& besti) {
+    if constexpr (T::kEpl == 8) {
+      constexpr int LR = S::kLogitRows;
+      float M[G], invL[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        M[h] = s_stat[G + h];
+        invL[h] = s_stat[3 * G + h];
+      }
+      const float ls = a.vl1 ? 1.0f : a.scale_log2;
+      float* dbg = a.dbg_scores ? a.dbg_scores + (size_t)pair * a.max_budget : nullptr;
+      const int quarter = ((count + kWaves - 1) / kWaves + 15) & ~15;
+      const int end = min(start + count, len);
+      for (int base = start + 2 * tid; base < end; base += 2 * kThreads) {
+        const int r = base - start;
+        int w = 0;
+#pragma unroll
+        for (int ww = 1; ww < kWaves; ++ww) w += r >= ww * quarter;
+        const float* src = s_logit + w * G * LR + (r - w * quarter);
+        float lv[G][2];
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float2 x = *reinterpret_cast<const float2*>(src + h * LR);
+          lv[h][0] = x.x;
+          lv[h][1] = x.y;
+        }
+        score_rows<G, 2>(base, lv, M, invL, ls, s_bits, a.sink, len, dbg, best, besti);
+      }
+    }
+    wave_argmin(best, besti);
+  };
+
   if (wave == 0) {
     float snew[G];
-    {
+    if constexpr (T::kEpl == 8) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) snew[h] = s_stat[h];  // this wave wrote them after its stream
+    } else {
       QReg<T, G> q;
       uint4 kn;
       new_token_logits<T, D, G>(a, pair, s_pre, q, kn, snew);
-    }
-    if (lane < G) {
-      float v = snew[0];
+      if (lane < G) {
+        float v = snew[0];
 #pragma unroll
-      for (int h = 1; h < G; ++h) v = lane == h ? snew[h] : v;
-      s_stat[lane] = v;
+        for (int h = 1; h < G; ++h) v = lane == h ? snew[h] : v;
+        s_stat[lane] = v;
+      }
     }
     float M[G], L[G], invL[G], wl[G];
     bool seen = false;
@@ -1256,61 +1327,49 @@ __device__ __forceinline__ void split_tail(const StepArgs& a, int pair, int item
     }
     lds_set(&s_flags[1], seen ? 1u : 2u);
     if (seen) {
-      // ---- this chunk's slots, from the logits its waves kept in LDS: slot s
-      // of wave w = (s - start) / quarter at row s - start - w * quarter
       float best = INFINITY;
       int besti = 0x7FFFFFFF;
       if (!a.score_none) {
-        constexpr int LR = S::kLogitRows;
-        const float ls = T::kEpl == 8 && !a.vl1 ? a.scale_log2 : 1.0f;
-        float* dbg = a.dbg_scores ? a.dbg_scores + (size_t)pair * a.max_budget : nullptr;
-        const int quarter = ((count + kWaves - 1) / kWaves + 15) & ~15;
-        const int end = min(start + count, len);
         lds_wait(&s_flags[0], a);  // bitmap ready
-        for (int base = start + 4 * lane; base < end; base += 4 * 64) {
-          const int r = base - start;
-          int w = 0;
+        score_share(best, besti);
+        lds_wait_count(&s_flags[8], kWaves - 1, a);  // the other waves' minima
 #pragma unroll
-          for (int ww = 1; ww < kWaves; ++ww) w += r >= ww * quarter;
-          const float* src = s_logit + w * G * LR + (r - w * quarter);
-          float4 lv[G];
-#pragma unroll
-          for (int h = 0; h < G; ++h) lv[h] = *reinterpret_cast<const float4*>(src + h * LR);
-          score4<G>(base, lv, M, invL, ls, s_bits, a.sink, len, dbg, best, besti);
-        }
-        wave_argmin(best, besti);
+        for (int w = 1; w < kWaves; ++w) argmin_merge(best, besti, s_arg[w], reinterpret_cast<const int*>(s_arg)[kWaves + w]);
       }
-      // ---- candidate and ticket
+      // ---- candidate and ticket; every chunk's candidate is requested with
+      // the ticket (for the chunk taking the last one they are mostly there)
+      const bool other = lane < nchunk && lane != chunk;
+      const uint64_t* cc = a.xcand + 2 * (size_t)(item0 + (lane < nchunk ? lane : 0));
       uint32_t prev = 0;
       if (lane == 0) {
         xstore(a.xcand + 2 * (size_t)item, xword(best, epoch));
         xstore(a.xcand + 2 * (size_t)item + 1, xword(static_cast<uint32_t>(besti & 0x7FFFFFFF), epoch));
         prev = __hip_atomic_fetch_add(a.count + pair, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
+      uint64_t s0 = xload(cc), s1 = xload(cc + 1);
       prev = __builtin_amdgcn_readfirstlane(prev);
       if (prev + 1u != static_cast<uint32_t>(nchunk)) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load left in flight
         lds_set(&s_flags[2], 1u);
         return;
       }
-      // ---- the finisher: every chunk's candidate (lane c: chunk c); without
-      // a deferred chunk it inserts right away
-      const bool mine = lane < nchunk;
-      const uint64_t* cc = a.xcand + 2 * (size_t)(item0 + (mine ? lane : 0));
-      uint64_t s0, s1;
+      // ---- the finisher: lane c holds chunk c's candidate (its own from
+      // registers); without a deferred chunk it inserts right away
       const uint64_t deadline = __builtin_amdgcn_s_memrealtime() + kSafetyTicks;
-      for (;;) {
-        s0 = xload(cc);
-        s1 = xload(cc + 1);
-        if (!__builtin_amdgcn_ballot_w64(mine && !(xfresh(s0, epoch) && xfresh(s1, epoch)))) break;
+      while (__builtin_amdgcn_ballot_w64(other && !(xfresh(s0, epoch) && xfresh(s1, epoch)))) {
         if (__builtin_amdgcn_s_memrealtime() > deadline) {
           if (lane == 0) __hip_atomic_fetch_or(a.fault, kFaultCandidates, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           break;
         }
+        s0 = xload(cc);
+        s1 = xload(cc + 1);
       }
-      const uint32_t si = static_cast<uint32_t>(s1);
+      const uint32_t si = lane == chunk ? static_cast<uint32_t>(besti & 0x7FFFFFFF) : static_cast<uint32_t>(s1);
+      const float sv = lane == chunk ? best : xval(s0);
+      const bool mine = lane < nchunk;
       const bool deferred = mine && (si & 0x80000000u);
       const uint64_t dmask = __builtin_amdgcn_ballot_w64(deferred);
-      float fb = mine && !deferred ? xval(s0) : INFINITY;
+      float fb = mine && !deferred ? sv : INFINITY;
       int fi = mine && !deferred ? static_cast<int>(si & 0x7FFFFFFF) : 0x7FFFFFFF;
       wave_argmin(fb, fi);
       if (dmask == 0) {
@@ -1358,17 +1417,87 @@ __device__ __forceinline__ void split_tail(const StepArgs& a, int pair, int item
     }
     const uint32_t v = lds_wait(&s_flags[1], a);
     if (v == 1u) {
-      // ---- this chunk's output rows
-      float snew[G], M[G], L[G], invL[G];
+      // ---- this chunk's output rows.  With few chunks, unit u = tid - 64
+      // (+ 192 per pass) writes dims d, d + 1 (d = 2 (u % (D / 2))) of the head
+      // of rank u / (D / 2); the first pass's value sums are requested before
+      // the chunk scores its slots.  The arithmetic is split_output's, in the
+      // same order: the rows have the same bits whichever path writes them.
+      const int nh = __builtin_popcount(my_heads), units = nh * (D / 2);
+      const bool fast_out = nchunk <= kOutPre;
+      const int b = pair / a.n_kv_heads, g = pair - b * a.n_kv_heads;
+      auto unit_cells = [&](int u, uint64_t (&x)[kOutPre][2]) {
+        const int k = u < units ? u / (D / 2) : 0, d = 2 * (u % (D / 2));
+        const int h = min(chunk + k * nchunk, G - 1);  // in range for lanes past the units
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        snew[h] = s_stat[h];
-        M[h] = s_stat[G + h];
-        L[h] = s_stat[2 * G + h];
-        invL[h] = s_stat[3 * G + h];
+        for (int j = 0; j < kOutPre; ++j) {
+          const uint64_t* cell = a.xcell + ((size_t)(item0 + min(j, nchunk - 1)) * G + h) * (D + 2) + d;
+          x[j][0] = xload(cell);
+          x[j][1] = xload(cell + 1);
+        }
+      };
+      auto unit_write = [&](int u, uint64_t (&x)[kOutPre][2]) {
+        const bool act = u < units;
+        const uint64_t deadline = __builtin_amdgcn_s_memrealtime() + kSafetyTicks;
+        for (;;) {
+          bool ok = true;
+#pragma unroll
+          for (int j = 0; j < kOutPre; ++j) ok = ok && (j >= nchunk || (xfresh(x[j][0], epoch) && xfresh(x[j][1], epoch)));
+          if (!__builtin_amdgcn_ballot_w64(act && !ok)) break;
+          if (__builtin_amdgcn_s_memrealtime() > deadline) {
+            if (lane == 0) __hip_atomic_fetch_or(a.fault, kFaultValues, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
+          unit_cells(u, x);
+        }
+        if (!act) return;
+        const int k = u / (D / 2), d = 2 * (u % (D / 2));
+        const int h = chunk + k * nchunk;
+        const float sn = s_stat[h], Mh = s_stat[G + h], Lh = s_stat[2 * G + h], il = s_stat[3 * G + h];
+        const elem* vnp = T::kEpl == 8 ? reinterpret_cast<const elem*>(s_pre) + (G + 1) * D
+                                       : static_cast<const elem*>(a.v_new) + (size_t)pair * D;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          float acc = fast_exp2(sn - Mh) * load_elem<T>(vnp, d + e);
+#pragma unroll
+          for (int j = 0; j < kOutPre; ++j)
+            if (j < nchunk) acc = fmaf(xval(x[j][e]), s_stat[4 * G + k * kMaxChunks + j], acc);
+          store_elem<T>(a.out, ((size_t)b * a.n_q_heads + g * G + h) * D + d + e, acc * il);
+        }
+        if (d == 0 && a.dbg_lse)
+          a.dbg_lse[(size_t)b * a.n_q_heads + g * G + h] = (Mh + __log2f(Lh)) * 0.6931471805599453f;
+      };
+      uint64_t x0[kOutPre][2];
+      if (fast_out) unit_cells(tid - 64, x0);
+      if (!a.score_none) {
+        float best = INFINITY;
+        int besti = 0x7FFFFFFF;
+        lds_wait(&s_flags[0], a);  // bitmap ready
+        score_share(best, besti);
+        if (lane == 0) {
+          s_arg[wave] = best;
+          reinterpret_cast<int*>(s_arg)[kWaves + wave] = besti;
+        }
+        lds_count(&s_flags[8]);
       }
-      split_output<T, D, G>(a, pair, item0, nchunk, epoch, my_heads, M, L, invL, snew, s_pre, 64,
-                            [&](int, int k, int c) { return s_stat[4 * G + k * kMaxChunks + c]; });
+      if (fast_out) {
+        unit_write(tid - 64, x0);
+        for (int u = tid - 64 + (kThreads - 64); u - lane < units; u += kThreads - 64) {
+          uint64_t x[kOutPre][2];
+          unit_cells(u, x);
+          unit_write(u, x);
+        }
+      } else {
+        float snew[G], M[G], L[G], invL[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          snew[h] = s_stat[h];
+          M[h] = s_stat[G + h];
+          L[h] = s_stat[2 * G + h];
+          invL[h] = s_stat[3 * G + h];
+        }
+        split_output<T, D, G>(a, pair, item0, nchunk, epoch, my_heads, M, L, invL, snew, s_pre, 64,
+                              [&](int, int k, int c) { return s_stat[4 * G + k * kMaxChunks + c]; });
+      }
       if (lds_wait(&s_flags[2], a) != 2u) return;
       own_c = chunk;  // on to the cold path with wave 0
     }
@@ -1591,9 +1720,12 @@ __device__ __forceinline__ void stream_valu(const StepArgs& a, int pair, int sta
 //    rarely; every quantity stays relative to the same reference, so results
 //    equal the eager form up to rounding.
 // Leaves the wave's partial in s_merge[wave][G][D + 2] like stream_valu.
+// For a split pair wave 0 also leaves the incoming token's logit of every
+// head (log2 domain) in s_snew[G].
 template <int D, int G>
 __device__ __forceinline__ void stream_mfma(const StepArgs& a, int pair, int start, int count, PairMeta& pm, int& lmode,
-                            float* s_merge, unsigned char* s_stage, float* s_logit) {
+                            float* s_merge, unsigned char* s_stage, float* s_logit, const float* s_pre,
+                            float* s_snew) {
   constexpr int KB = D / 32;  // q.k MFMAs per row group
   constexpr int EV = D / 16;  // value dims per lane per row = P.V MFMAs per value row
   constexpr float kLazy = 8.0f;
@@ -1885,6 +2017,21 @@ __device__ __forceinline__ void stream_mfma(const StepArgs& a, int pair, int sta
       dst[D + 1] = lsum;
     }
   }
+  // The incoming token's logits, for a split pair's tail: one more row group
+  // of products with k_new as every row (from wave 0's LDS copy, complete once
+  // any of its stream loads was waited for; without a row, waited for here),
+  // so lane h of row group 0 holds q_h . k_new.
+  if (wave == 0 && pm.nchunk > 1) {
+    if (Rend <= R0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const uint16_t* kn = reinterpret_cast<const uint16_t*>(s_pre) + G * D + 8 * j;
+    f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(kn + 32 * kb)),
+          __builtin_bit_cast(bf16x8_t, qb[kb]), sacc, 0, 0, 0);
+    if (j == 0 && n < G) s_snew[n] = sacc[0] * scale;
+  }
 }
 
 template <class T, int D, int G, bool U>
@@ -1892,12 +2039,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Shape<
 void lf_step_kernel(StepArgs a) {
   using S = Shape<T, D, G>;
   __shared__ float smem[S::kSmemFloats];
-  __shared__ uint32_t s_flags[8];  // hand-overs between the waves of a split pair's chunk (split_tail)
+  __shared__ uint32_t s_flags[12];  // hand-overs between the waves of a split pair's chunk (split_tail)
+  // A split pair's incoming-token logits, max, normaliser and its inverse per
+  // head, then every chunk's weight for this chunk's output heads.
+  __shared__ float s_stat[4 * G + (G + 1) / 2 * kMaxChunks];
   float* s_part = smem;                   // [G][D + 2]: merged partial of this chunk
   float* s_work = smem + S::kPartFloats;  // cross-wave merge, then tail scratch
 
   const int tid = threadIdx.x;
-  if (tid < 8) s_flags[tid] = 0u;  // ordered before any use by the barrier after the stream
+  if (tid < 12) s_flags[tid] = 0u;  // ordered before any use by the barrier after the stream
   // U (equal budgets): the item follows from the block index, so the first
   // K/V loads wait for no load of the work list.  A separate instantiation:
   // a run-time branch would make every scalar load of the prologue wait.
@@ -1919,7 +2069,7 @@ void lf_step_kernel(StepArgs a) {
   if constexpr (T::kEpl == 8) {
     if (tid < 64) prefetch_tail<D, G>(a, pair, s_pre);
     stream_mfma<D, G>(a, pair, it.start, it.count, pm, lmode, s_work,
-                      reinterpret_cast<unsigned char*>(s_work + S::kMergeFloats), s_logit);
+                      reinterpret_cast<unsigned char*>(s_work + S::kMergeFloats), s_logit, s_pre, s_stat);
     // The prefetch completed before wave 0's first stream wait (loads return in
     // order); without a row to stream, wave 0 waits for it here.
     if (tid < 64 && min(it.start + it.count, pm.len) <= it.start) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -1932,7 +2082,8 @@ void lf_step_kernel(StepArgs a) {
   __syncthreads();
   uint32_t* s_bits = reinterpret_cast<uint32_t*>(s_work + S::kBitsOffset);
   if (nchunk > 1) {
-    split_tail<T, D, G>(a, pair, (int)blockIdx.x, it.start, it.count, pm, lmode, s_work, s_logit, s_pre, s_flags);
+    split_tail<T, D, G>(a, pair, (int)blockIdx.x, it.start, it.count, pm, lmode, s_work, s_logit, s_pre, s_flags,
+                        s_stat);
     return;
   }
   clear_protect_bits(s_bits, pm.budget);
@@ -2018,26 +2169,29 @@ int launch_step(int dtype, int head_dim, int group, const StepArgs& a, void* str
   return 0;
 }
 
-int upload_and_wait(void* dst, const void* src, size_t bytes, void* stream, char* err, size_t errlen) {
+int copy_rows_and_wait(void* dst, size_t dpitch, const void* src, size_t spitch, size_t width, size_t rows,
+                       bool to_device, void* stream, char* err, size_t errlen) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, s);
+  const hipMemcpyKind kind = to_device ? hipMemcpyHostToDevice : hipMemcpyDeviceToHost;
+  hipError_t e = hipSuccess;
+  if (rows == 1)
+    e = hipMemcpyAsync(dst, src, width, kind, s);
+  else if (rows > 1)
+    e = hipMemcpy2DAsync(dst, dpitch, src, spitch, width, rows, kind, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) {
-    snprintf(err, errlen, "state upload failed: %s", hipGetErrorString(e));
+    snprintf(err, errlen, "state %s failed: %s", to_device ? "upload" : "download", hipGetErrorString(e));
     return 1;
   }
   return 0;
 }
 
+int upload_and_wait(void* dst, const void* src, size_t bytes, void* stream, char* err, size_t errlen) {
+  return copy_rows_and_wait(dst, bytes, src, bytes, bytes, 1, true, stream, err, errlen);
+}
+
 int download_and_wait(void* dst, const void* src, size_t bytes, void* stream, char* err, size_t errlen) {
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToHost, s);
-  if (e == hipSuccess) e = hipStreamSynchronize(s);
-  if (e != hipSuccess) {
-    snprintf(err, errlen, "state download failed: %s", hipGetErrorString(e));
-    return 1;
-  }
-  return 0;
+  return copy_rows_and_wait(dst, bytes, src, bytes, bytes, 1, false, stream, err, errlen);
 }
 
 }  // namespace lf

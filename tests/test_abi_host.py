@@ -46,7 +46,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version():
-    assert _lib.lf_abi_version() == 1
+    assert _lib.lf_abi_version() == 2
 
 
 def _cfg(**kw):
@@ -179,3 +179,34 @@ def test_prefill_noalloc_rejects_batches_beyond_its_scratch():
         _lib.lf_prefill_compress_noalloc(cfg, [8192] * 128, [16384] * 128, 16384, 16, 16, 16, 16, 16, 16)
     assert ei.value.status == LF_ERR_ARG
     assert "static scratch" in _lib.lf_last_error()
+
+
+def test_layers_state_bytes_and_init_validation_before_any_device_call():
+    cfg = _cfg()
+    one = _lib.lf_state_bytes(cfg)
+    assert _lib.lf_state_bytes_layers(cfg, None, 3) == 3 * one
+    with pytest.raises(LFError) as ei:
+        _lib.lf_state_bytes_layers(cfg, None, 0)
+    assert ei.value.status == LF_ERR_ARG
+    ks, vs = [4096, 8192, 12288], [16384, 20480, 24576]
+    with pytest.raises(LFError) as ei:  # room for two layers only
+        _lib.lf_init_layers(cfg, None, [512, 512], ks, vs, 1 << 20, 3 * one - 256)
+    assert ei.value.status == LF_ERR_ARG
+    with pytest.raises(LFError) as ei:  # a NULL layer cache
+        _lib.lf_init_layers(cfg, None, [512, 512], [4096, 0, 12288], vs, 1 << 20, 3 * one)
+    assert ei.value.status == LF_ERR_ARG
+    with pytest.raises(LFError) as ei:  # a misaligned layer cache
+        _lib.lf_init_layers(cfg, None, [512, 512], [4096, 8192 + 4, 12288], vs, 1 << 20, 3 * one)
+    assert ei.value.status == LF_ERR_ARG
+    with pytest.raises(ValueError):
+        _lib.lf_init_layers(cfg, None, [512, 512], ks, vs[:2], 1 << 20, 3 * one)
+
+
+def test_layer_steps_reject_bad_handles_without_launching():
+    with pytest.raises(LFError) as ei:
+        _lib.lf_decode_step_layer(1, 1, 1, 0, 0, 1, 1)
+    assert ei.value.status == LF_ERR_ARG
+    fake = (ctypes.c_uint64 * 64)()
+    with pytest.raises(LFError) as ei:
+        _lib.lf_decode_step_layer_dbg(1, 1, 1, ctypes.addressof(fake), 0, 1, 1)
+    assert ei.value.status == LF_ERR_STATE
