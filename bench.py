@@ -52,7 +52,36 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true", help="skip the HBM read/copy probes and the launch floor")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the short runs of the other GPU workloads reported under 'workloads'")
+    ap.add_argument("--other-steps", type=int, default=1000, help="timed steps of each other workload")
     return ap.parse_args()
+
+
+OTHER_WORKLOADS = ("llama8b_b8", "throughput_b64", "evict_stress", "ragged_b128")
+
+
+def fast_caches(w, bud, L, dev, torch):
+    """L layer caches of workload w for timing only: K/V drawn N(0,1) on the
+    device (the key outlier channels scaled), filled to each sequence's
+    prefill length or budget, instead of the seeded host recipe (whose values
+    only parity runs need)."""
+    from workloads import prefill_lengths
+    from workloads.generate import outlier_channels
+
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    gen = torch.Generator(device=dev).manual_seed(w.seed + 1)
+    ch = torch.as_tensor(outlier_channels(w), device=dev)
+    S = int(bud.max())
+    seq_len = prefill_lengths(w)
+    out = []
+    for _ in range(L):
+        K = torch.randn((w.batch, w.n_kv_heads, S, w.head_dim), generator=gen, device=dev)
+        if ch.numel():
+            K[..., ch] *= w.outlier_scale
+        V = torch.randn((w.batch, w.n_kv_heads, S, w.head_dim), generator=gen, device=dev)
+        out.append((K.to(dt), V.to(dt), seq_len))
+    return out
 
 
 def algorithmic_bytes(w, bud, stored: bool = True) -> int:
@@ -170,50 +199,34 @@ def bench_compress(args, w, torch, dev):
                    "budget": [int(bud.min()), int(bud.max())], "sink": w.sink, "recent": w.recent},
         "kv_GBps": round(gbps, 1), "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "bytes_per_call": nbytes,
-        "note": "bytes: every prefill K row read once (the statistics pass stores the logits the importance "
+        "note": "bytes: every prefill K row read once (the statistics pass stores the logits the selection "
                 "pass reads) plus the kept K and V rows read and written",
     }), flush=True)
 
 
-def main():
-    args = parse()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: the decode step has no cross-GPU exchange, and this build "
-              "runs on a single MI355X; run it with --gpus 1", file=sys.stderr)
-        sys.exit(2)
-
-    import torch
-
+def time_steps(args, w, bud, steps, warmup, torch, dev, lib, fast=False):
+    """Times `steps` decode steps of workload w (after `warmup`) over L rotating
+    layer caches; returns (ms per step, wall seconds of the timed region, L,
+    chunk slots)."""
     from kv_cache_eviction_lf_amd import LongFlowCache, _lib
-    from workloads import budgets, get_workload
     from workloads.device import device_cache, device_step_pool
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    lib = _lib.load_library()
-    dev = torch.device("cuda:0")
-    w = get_workload(args.workload)
-    if args.budget:
-        w = w.with_(budget_lo=args.budget, budget_hi=args.budget, prefill="full")
-    if args.compress:
-        bench_compress(args, w, torch, dev)
-        return
-    bud = budgets(w)
-    step_bytes = algorithmic_bytes(w, bud, stored=args.score != "none")
     layer_kv = int(np.sum(bud)) * w.n_kv_heads * w.head_dim * 2 * (2 if w.dtype == "bf16" else 4)
-    L = args.layers or max(1, math.ceil(2 * MALL_BYTES / layer_kv))
-
+    L = (args.layers if not fast else 0) or max(1, math.ceil(2 * MALL_BYTES / layer_kv))
     # L independent layer caches (distinct seeds) and fresh inputs for every
     # step (a repeated input would fill the caches with copies of its tokens).
     caches = []
-    for layer in range(L):
-        wl = w.with_(seed=w.seed + 7919 * layer)
-        K, V, seq_len, _ = device_cache(wl, dev)
-        caches.append(LongFlowCache(K, V, w.n_q_heads, w.sink, w.recent, seq_len, budgets=bud,
-                                    score=args.score, chunk_slots=args.chunk))
+    if fast:
+        for K, V, seq_len in fast_caches(w, bud, L, dev, torch):
+            caches.append(LongFlowCache(K, V, w.n_q_heads, w.sink, w.recent, seq_len, budgets=bud))
+    else:
+        for layer in range(L):
+            wl = w.with_(seed=w.seed + 7919 * layer)
+            K, V, seq_len, _ = device_cache(wl, dev)
+            caches.append(LongFlowCache(K, V, w.n_q_heads, w.sink, w.recent, seq_len, budgets=bud,
+                                        score=args.score, chunk_slots=args.chunk))
     step_in = 2 * (w.batch * w.n_q_heads + 2 * w.batch * w.n_kv_heads) * w.head_dim * (2 if w.dtype == "bf16" else 4)
-    P = max(1, min(args.warmup + args.steps, (16 << 30) // step_in))
+    P = max(1, min(warmup + steps, (16 << 30) // step_in))
     pool = device_step_pool(w, P, dev)
     outs = [torch.empty_like(pool[0][0]) for _ in range(L)]
     evs = [torch.empty((w.batch, w.n_kv_heads), dtype=torch.int32, device=dev) for _ in range(L)]
@@ -257,7 +270,7 @@ def main():
 
     # pre-capture what warm-up and the timed region replay (capture launches nothing)
     if not args.eager:
-        for n, b in pieces(args.warmup, 0) + pieces(args.steps, args.warmup):
+        for n, b in pieces(warmup, 0) + pieces(steps, warmup):
             graph_for(n, b)
 
     def run(n, base):
@@ -267,22 +280,68 @@ def main():
         for m, b in pieces(n, base):
             graph_for(m, b).replay()
 
-    run(args.warmup, 0)
+    run(warmup, 0)
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record(cur)
-    run(args.steps, args.warmup)
+    run(steps, warmup)
     ev1.record(cur)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = ev0.elapsed_time(ev1)
-    ms_per_step = ms / args.steps
-    steps_per_s = 1e3 / ms_per_step
-    achieved = step_bytes / (ms_per_step * 1e-3) / 1e9  # GB/s
+    ms_per_step = ms / steps
+    chunk_slots = caches[0].cfg.chunk_slots or "auto"
     for c in caches:
         c.close()
+    return ms_per_step, wall, L, chunk_slots
 
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the decode step has no cross-GPU exchange, and this build "
+              "runs on a single MI355X; run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from kv_cache_eviction_lf_amd import _lib
+    from workloads import budgets, get_workload
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    lib = _lib.load_library()
+    dev = torch.device("cuda:0")
+    w = get_workload(args.workload)
+    if args.budget:
+        w = w.with_(budget_lo=args.budget, budget_hi=args.budget, prefill="full")
+    if args.compress:
+        bench_compress(args, w, torch, dev)
+        return
+    bud = budgets(w)
+    step_bytes = algorithmic_bytes(w, bud, stored=args.score != "none")
+    ms_per_step, wall, L, chunk_slots = time_steps(args, w, bud, args.steps, args.warmup, torch, dev, lib)
+    steps_per_s = 1e3 / ms_per_step
+    achieved = step_bytes / (ms_per_step * 1e-3) / 1e9  # GB/s
+    others = None
+    if not args.no_others and args.score == "attn" and not args.budget and not args.chunk and not args.layers:
+        others = {}
+        for name in OTHER_WORKLOADS:
+            if name == w.name:
+                continue
+            wo = get_workload(name)
+            bo = budgets(wo)
+            mo, _, Lo, _ = time_steps(args, wo, bo, args.other_steps, min(args.warmup, 200), torch, dev, lib,
+                                      fast=True)
+            bo_bytes = algorithmic_bytes(wo, bo)
+            gb = bo_bytes / (mo * 1e-3) / 1e9
+            others[name] = {"ms_per_step": round(mo, 6), "steps_per_s": round(1e3 / mo, 1), "kv_GBps": round(gb, 1),
+                            "frac": round(gb / HBM_PEAK_GBPS, 4), "steps": args.other_steps, "layer_caches": Lo,
+                            "bytes_per_launch": bo_bytes}
+
+    cur = torch.cuda.current_stream()
     probe = None
     if not args.no_probe:
         n = 1 << 30
@@ -360,7 +419,7 @@ def main():
             "score": args.score,
             "layer_caches": L,
             "launch": "eager" if args.eager else "hip-graph",
-            "chunk_slots": caches[0].cfg.chunk_slots or "auto",
+            "chunk_slots": chunk_slots,
         },
         "kv_GBps": round(achieved, 1),
         "pct_hbm_peak": round(100 * achieved / HBM_PEAK_GBPS, 2),
@@ -380,6 +439,8 @@ def main():
     }
     if probe:
         line["hbm_probe"] = probe
+    if others:
+        line["workloads"] = others
     print(json.dumps(line), flush=True)
 
 

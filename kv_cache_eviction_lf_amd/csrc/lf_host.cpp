@@ -171,6 +171,8 @@ lf_status make_layout(const lf_config* cfg, const std::vector<int32_t>& bud, lf:
   off = align_up(off + sizeof(uint64_t) * (size_t)group * (cfg->head_dim + 2) * W);
   L.xcand = off;
   off = align_up(off + sizeof(uint64_t) * 2 * W);
+  L.xstat = off;
+  off = align_up(off + sizeof(uint64_t) * 2 * (lf::kThreads / 64) * (size_t)group * W);
   L.logits = off;  // none without importance (LF_SCORE_NONE)
   if (cfg->score != LF_SCORE_NONE) off = align_up(off + sizeof(float) * (size_t)group * S);
   L.total = off;
@@ -267,6 +269,7 @@ lf_status step_impl(const void* q, const void* k_new, const void* v_new, lf_cach
   a.items = reinterpret_cast<const lf::WorkItem*>(s + L.items);
   a.xcell = reinterpret_cast<uint64_t*>(s + L.xcell);
   a.xcand = reinterpret_cast<uint64_t*>(s + L.xcand);
+  a.xstat = reinterpret_cast<uint64_t*>(s + L.xstat);
   a.count = reinterpret_cast<uint32_t*>(s + L.count);
   a.deferred = reinterpret_cast<uint32_t*>(s + L.header + offsetof(lf::StateHeader, deferred));
   a.fault = reinterpret_cast<uint32_t*>(s + L.header + offsetof(lf::StateHeader, fault));

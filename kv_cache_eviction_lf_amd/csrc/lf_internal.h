@@ -64,7 +64,7 @@ constexpr uint32_t kFaultStats = 1, kFaultValues = 2, kFaultCandidates = 4;
 // Byte offsets of the regions of the caller's state buffer.  Everything before
 // `items` depends only on the numbers of pairs and ring entries.
 struct StateLayout {
-  size_t header, meta, ring, count, items, xcell, xcand, logits, total;
+  size_t header, meta, ring, count, items, xcell, xcand, xstat, logits, total;
   int32_t n_pairs, n_items, total_slots, chunk, max_nchunk;
 };
 
@@ -84,8 +84,9 @@ struct StepArgs {
   const WorkItem* items;
   // Exchange between the chunks of a split pair, every value a 64-bit word
   // whose high half is the pair's epoch of the step that wrote it:
-  uint64_t* xcell;   // [n_items][G][d + 2]: the chunk's weighted value sums, then (max, sum) per head
+  uint64_t* xcell;   // [n_items][G][d + 2]: the chunk's weighted value sums (max, sum slots unused)
   uint64_t* xcand;   // [n_items][2]: the chunk's (score) and (slot | deferred << 31) candidate
+  uint64_t* xstat;   // [n_items][kThreads / 64][G][2]: (max, sum) of every wave of the chunk, per head
   uint32_t* count;   // [n_pairs]: chunks of the pair done with the step (reset by the finisher)
   uint32_t* deferred;  // header counter of deferred chunks
   uint32_t* fault;     // header fault bits (kFault*)
@@ -116,7 +117,7 @@ int tile_rows(int dtype, int head_dim, int group);
 // Arguments of the one-shot prefill compression (lf_prefill.hip).  Pair p =
 // b * n_kv_heads + g; the caller's scratch holds [pairs][max_prefill]
 // importances, the per-chunk statistics, the device copies of the prefill
-// lengths and budgets, then [pairs][max_prefill][group] logits.
+// lengths and budgets, then [pairs][group][max_prefill] logits.
 struct PrefillArgs {
   const void* q_last;  // [B][Hq][d]
   const void* k_pre;   // [B][Hkv][max_prefill][d]
@@ -126,7 +127,7 @@ struct PrefillArgs {
   int32_t* kept;       // [B][Hkv][max_budget]: kept positions, increasing
   float* work;         // [pairs][max_prefill]
   float* stats;        // [pairs][n_chunks][8][2]: per-chunk (max, sum) per head
-  float* logits;       // [pairs][max_prefill][group]: log2-domain logits of the last query
+  float* logits;       // [pairs][group][max_prefill]: log2-domain logits of the last query
   const int32_t* prefill;  // device [B]
   const int32_t* budget;   // device [B]
   int32_t n_chunks;    // score chunks per pair (max_prefill / 512, rounded up)

@@ -908,32 +908,55 @@ __device__ __forceinline__ void chunk_stat(const float* s_part_w, int h, float& 
   }
 }
 
-// Per wave: waits until every chunk of the pair has published this step's
-// (max, sum) of every head (giving up after `deadline` if `bounded`; else
-// `deadline` is only the safety bound, after which a fault bit is set), then
-// the global max M_h and normaliser L_h over the chunks and the incoming
-// token; lane c keeps chunk c's weight exp2(m_c,h - M_h) in wl[h].  Lane
-// `own` (this chunk, or -1) computes its values from this workgroup's wave
-// partials (s_part_w, LDS) instead of reading memory: its own words may not
-// be visible to it yet.  Every wave
-// of every chunk computes the same bits.
+// A chunk's (max, sum) of one head from its waves' exchange words x (wave w's
+// max at 2 w, its sum at 2 w + 1), combined in the order chunk_stat combines
+// the waves' partials: the bits are those the chunk computes itself.
+__device__ __forceinline__ void combine_waves(const uint64_t (&x)[2 * kWaves], float& mm, float& sl) {
+  mm = kNegBig;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) mm = fmaxf(mm, xval(x[2 * w]));
+  sl = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) sl = fmaf(xval(x[2 * w + 1]), fast_exp2(xval(x[2 * w]) - mm), sl);
+}
+__device__ __forceinline__ bool all_fresh(const uint64_t (&x)[2 * kWaves], uint32_t epoch) {
+  bool ok = true;
+#pragma unroll
+  for (int i = 0; i < 2 * kWaves; ++i) ok = ok & xfresh(x[i], epoch);
+  return ok;
+}
+// Loads one chunk's words of one head (xstat layout [item][G][wave][2]).
+__device__ __forceinline__ void load_stats(const uint64_t* cell, uint64_t (&x)[2 * kWaves]) {
+#pragma unroll
+  for (int i = 0; i < 2 * kWaves; ++i) x[i] = xload(cell + i);
+}
+
+// Per wave: waits until every wave of every chunk of the pair has published
+// this step's (max, sum) of every head (giving up after `deadline` if
+// `bounded`; else `deadline` is only the safety bound, after which a fault
+// bit is set), then the global max M_h and normaliser L_h over the chunks and
+// the incoming token; lane c keeps chunk c's weight exp2(m_c,h - M_h) in
+// wl[h].  Lane `own` (this chunk, or -1) computes its values from this
+// workgroup's wave partials (s_part_w, LDS) instead of reading memory.  Every
+// wave of every chunk computes the same bits.  (Pairs with many chunks; the
+// (head, chunk) layout of pair_stats_hc serves the others.)
 template <int D, int G>
 __device__ __forceinline__ bool pair_stats(const StepArgs& a, int item0, int nchunk, uint32_t epoch, const float (&snew)[G],
                            int own, const float* s_part_w, bool bounded, uint64_t deadline, float (&M)[G],
                            float (&L)[G], float (&wl)[G]) {
   const int lane = threadIdx.x & 63;
   const bool mine = lane < nchunk && lane != own;
-  const uint64_t* cell = a.xcell + (size_t)(item0 + (lane < nchunk ? lane : 0)) * G * (D + 2) + D;
-  uint64_t mw[G], lw[G];
+  const uint64_t* cell = a.xstat + (size_t)(item0 + (lane < nchunk ? lane : 0)) * G * (2 * kWaves);
+  float cm[G], cl[G];
   for (;;) {
     bool ok = true;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      mw[h] = xload(cell + h * (D + 2));
-      lw[h] = xload(cell + h * (D + 2) + 1);
+      uint64_t x[2 * kWaves];
+      load_stats(cell + h * (2 * kWaves), x);
+      ok = ok & all_fresh(x, epoch);
+      combine_waves(x, cm[h], cl[h]);
     }
-#pragma unroll
-    for (int h = 0; h < G; ++h) ok = ok && xfresh(mw[h], epoch) && xfresh(lw[h], epoch);
     if (!__builtin_amdgcn_ballot_w64(mine && !ok)) break;
     const uint64_t now = __builtin_amdgcn_s_memrealtime();
     if (now > deadline) {
@@ -950,8 +973,8 @@ __device__ __forceinline__ bool pair_stats(const StepArgs& a, int item0, int nch
     float om = 0.f, ol = 0.f;
     if (own >= 0) chunk_stat<D, G>(s_part_w, h, om, ol);
     const bool me = lane == own;
-    const float m = lane < nchunk ? (me ? om : xval(mw[h])) : kNegBig;
-    const float l = lane < nchunk ? (me ? ol : xval(lw[h])) : 0.f;
+    const float m = lane < nchunk ? (me ? om : cm[h]) : kNegBig;
+    const float l = lane < nchunk ? (me ? ol : cl[h]) : 0.f;
     const float Mh = fmaxf(wave_max(m), snew[h]);
     const float w = fast_exp2(m - Mh);  // 0 past the chunks
     M[h] = Mh;
@@ -983,6 +1006,8 @@ __device__ __forceinline__ float group_reduce(float x, int k, Op op) {
 // 2^k * G <= 64: one segmented reduction serves every head.  The lane's head
 // gets Mh and Lh, the lane's chunk weight exp2(m_c,h - M_h) goes to w.  Same
 // bits as pair_stats (the same pairings, the extra lanes adding nothing).
+// Two polls are kept in flight, so a word that lands is seen about half a
+// round trip sooner than by a poll that waits for the previous one.
 template <int D, int G>
 __device__ __forceinline__ bool pair_stats_hc(const StepArgs& a, int item0, int nchunk, int k, uint32_t epoch,
                                               const float* s_snew, int own, const float* s_part_w, bool bounded,
@@ -991,13 +1016,23 @@ __device__ __forceinline__ bool pair_stats_hc(const StepArgs& a, int item0, int 
   const int h = lane >> k, c = lane & ((1 << k) - 1);
   const bool valid = h < G && c < nchunk;
   const bool mine = valid && c != own;
-  const uint64_t* cell = a.xcell + ((size_t)(item0 + (valid ? c : 0)) * G + (valid ? h : 0)) * (D + 2) + D;
-  uint64_t mw, lw;
+  const uint64_t* cell = a.xstat + ((size_t)(item0 + (valid ? c : 0)) * G + (valid ? h : 0)) * (2 * kWaves);
+  uint64_t xa[2 * kWaves], xb[2 * kWaves];
+  load_stats(cell, xa);
   for (;;) {
-    mw = xload(cell);
-    lw = xload(cell + 1);
-    const bool ok = xfresh(mw, epoch) && xfresh(lw, epoch);
-    if (!__builtin_amdgcn_ballot_w64(mine && !ok)) break;
+    load_stats(cell, xb);
+    if (!__builtin_amdgcn_ballot_w64(mine && !all_fresh(xa, epoch))) break;
+    if (__builtin_amdgcn_s_memrealtime() > deadline) {
+      if (bounded) return false;
+      if (lane == 0) __hip_atomic_fetch_or(a.fault, kFaultStats, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+    load_stats(cell, xa);
+    if (!__builtin_amdgcn_ballot_w64(mine && !all_fresh(xb, epoch))) {
+#pragma unroll
+      for (int i = 0; i < 2 * kWaves; ++i) xa[i] = xb[i];
+      break;
+    }
     if (__builtin_amdgcn_s_memrealtime() > deadline) {
       if (bounded) return false;
       if (lane == 0) __hip_atomic_fetch_or(a.fault, kFaultStats, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1012,8 +1047,10 @@ __device__ __forceinline__ bool pair_stats_hc(const StepArgs& a, int item0, int 
     const bool me = c == own;
     float om = 0.f, ol = 0.f;
     if (own >= 0) chunk_stat<D, G>(s_part_w, h < G ? h : 0, om, ol);
-    const float m = valid ? (me ? om : xval(mw)) : kNegBig;
-    const float l = valid ? (me ? ol : xval(lw)) : 0.f;
+    float cm, cl;
+    combine_waves(xa, cm, cl);
+    const float m = valid ? (me ? om : cm) : kNegBig;
+    const float l = valid ? (me ? ol : cl) : 0.f;
     Mh = fmaxf(group_reduce(m, k, [](float u, float v) { return fmaxf(u, v); }), sn);
     w = fast_exp2(m - Mh);  // 0 past the chunks
     Lh = group_reduce(l * w, k, [](float u, float v) { return u + v; }) + fast_exp2(sn - Mh);
@@ -1246,6 +1283,17 @@ __device__ __forceinline__ void split_tail(const StepArgs& a, int pair, int item
   // waiting is switched off).
   const bool can_wait = a.wait_ticks > 0 && (a.score_none || lmode == kLogitsFull);
   int own_c = -1;  // >= 0: the fast path's finisher has deferred chunks to finish (every wave joins)
+  if constexpr (T::kEpl != 8) {
+    // The vector-ALU stream leaves every wave's (max, sum) in the merge area;
+    // the matrix-core stream published them itself.
+    if (tid < kWaves * G) {
+      const int w = tid / G, h = tid - w * G;
+      const float* src = s_work + (w * G + h) * (D + 2);
+      uint64_t* xs = a.xstat + (((size_t)item * G + h) * kWaves + w) * 2;
+      xstore(xs, xword(src[D], epoch));
+      xstore(xs + 1, xword(src[D + 1], epoch));
+    }
+  }
 
   // This thread's share of the chunk's slots (2 per thread and pass, from the
   // logits the streaming waves kept in LDS: slot s of stream wave
@@ -1394,26 +1442,27 @@ __device__ __forceinline__ void split_tail(const StepArgs& a, int pair, int item
       set_protect_bits<T, D, G>(a, pair, budget, s_bits, s_pre, 64, 64);
       lds_set(&s_flags[0], 1u);
     }
-    if (tid >= 128 && tid < 128 + G) {
-      const int h = tid - 128;
-      float mm, sl;
-      chunk_stat<D, G>(s_work, h, mm, sl);
-      uint64_t* xc = a.xcell + ((size_t)item * G + h) * (D + 2);
-      xstore(xc + D, xword(mm, epoch));
-      xstore(xc + D + 1, xword(sl, epoch));
-    }
-    for (int idx = tid - 64; idx < G * D; idx += kThreads - 64) {
-      const int h = idx / D, dim = idx - h * D;
-      float mm = kNegBig;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) mm = fmaxf(mm, s_work[(w * G + h) * (D + 2) + D]);
-      float sa = 0.f;
+    // Value sums two dimensions at a time: the waves' weights exp2(m_w - mm)
+    // once per pair of dimensions, the sums in wave order as before.
+    for (int u = tid - 64; u < G * D / 2; u += kThreads - 64) {
+      const int h = u / (D / 2), dim = 2 * (u - h * (D / 2));
+      float mw[kWaves], mm = kNegBig;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
-        const float* src = s_work + (w * G + h) * (D + 2);
-        sa = fmaf(src[dim], fast_exp2(src[D] - mm), sa);
+        mw[w] = s_work[(w * G + h) * (D + 2) + D];
+        mm = fmaxf(mm, mw[w]);
       }
-      xstore(a.xcell + ((size_t)item * G + h) * (D + 2) + dim, xword(sa, epoch));
+      float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float f = fast_exp2(mw[w] - mm);
+        const float2 x = *reinterpret_cast<const float2*>(s_work + (w * G + h) * (D + 2) + dim);
+        s0 = fmaf(x.x, f, s0);
+        s1 = fmaf(x.y, f, s1);
+      }
+      uint64_t* xc = a.xcell + ((size_t)item * G + h) * (D + 2) + dim;
+      xstore(xc, xword(s0, epoch));
+      xstore(xc + 1, xword(s1, epoch));
     }
     const uint32_t v = lds_wait(&s_flags[1], a);
     if (v == 1u) {
@@ -2017,6 +2066,13 @@ __device__ __forceinline__ void stream_mfma(const StepArgs& a, int pair, int sta
       dst[D + 1] = lsum;
     }
   }
+  // A split pair's chunks read every wave's (max, sum) per head: published
+  // here, as soon as the wave is done (see pair_stats_hc).
+  if (pm.nchunk > 1 && n < G && j == 0) {
+    uint64_t* xs = a.xstat + (((size_t)blockIdx.x * G + n) * kWaves + wave) * 2;
+    xstore(xs, xword(m, pm.epoch));
+    xstore(xs + 1, xword(lsum, pm.epoch));
+  }
   // The incoming token's logits, for a split pair's tail: one more row group
   // of products with k_new as every row (from wave 0's LDS copy, complete once
   // any of its stream loads was waited for; without a row, waited for here),
@@ -2038,7 +2094,7 @@ template <class T, int D, int G, bool U>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Shape<T, D, G>::kMinWavesPerSimd, 8)))
 void lf_step_kernel(StepArgs a) {
   using S = Shape<T, D, G>;
-  __shared__ float smem[S::kSmemFloats];
+  __shared__ __attribute__((aligned(16))) float smem[S::kSmemFloats];  // 16-byte cells are read from it
   __shared__ uint32_t s_flags[12];  // hand-overs between the waves of a split pair's chunk (split_tail)
   // A split pair's incoming-token logits, max, normaliser and its inverse per
   // head, then every chunk's weight for this chunk's output heads.

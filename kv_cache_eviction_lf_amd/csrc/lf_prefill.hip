@@ -9,18 +9,18 @@
 // to other methods; this selection is the plainest reading that keeps the
 // decode step's importance.
 //
-// Four launches on the caller's stream:
+// Three launches on the caller's stream:
 //   prefill_stats_kernel       a workgroup per (pair, 512-row chunk): the
-//                              chunk's logits (stored, G per position) and
-//                              their per-head maximum and normaliser.
-//   prefill_importance_kernel  same grid: the pair's statistics combined in
-//                              chunk order, then every row's importance from
-//                              its stored logits (no second pass over K).
-//   prefill_select_kernel      a workgroup per pair: radix selection of the
+//                              chunk's logits (stored head-major, [G][position])
+//                              and their per-head maximum and normaliser.
+//   prefill_select_kernel      a workgroup per pair: the pair's statistics
+//                              combined in chunk order, every position's
+//                              importance from its stored logits (no second
+//                              pass over K), then radix selection of the
 //                              threshold over 48-bit keys (importance, then the
 //                              complement of the position, so keys are unique
 //                              and the lower position ranks first on equal
-//                              importance), then position-ordered compaction.
+//                              importance) and position-ordered compaction.
 //   prefill_copy_kernel        a workgroup per (pair, 256 kept rows): the
 //                              kept K/V rows copied in order.
 #include <hip/hip_runtime.h>
@@ -150,9 +150,9 @@ struct ScoreCore {
   }
 };
 
-// Pass 1: the chunk's logits, stored [position][G] (lane c of a row lineage
-// stores head c, so a wave's stores are contiguous), and per head their
-// maximum and normaliser (log2 domain).
+// Pass 1: the chunk's logits, stored head-major [G][max_prefill] (lane c of a
+// row lineage stores head c), and per head their maximum and normaliser (log2
+// domain).
 template <class E, int D, int G>
 __global__ __launch_bounds__(kPT) void prefill_stats_kernel(PrefillArgs a) {
   const int pair = blockIdx.x / a.n_chunks, chunk = blockIdx.x - pair * a.n_chunks;
@@ -182,7 +182,7 @@ __global__ __launch_bounds__(kPT) void prefill_stats_kernel(PrefillArgs a) {
     float mine = s[0];
 #pragma unroll
     for (int h = 1; h < G; ++h) mine = core.c == h ? s[h] : mine;
-    if (core.c < G) lg[(size_t)row * G + core.c] = mine;
+    if (core.c < G) lg[(size_t)core.c * a.max_prefill + row] = mine;
   });
   __shared__ float s_m[kPW][kMaxG], s_l[kPW][kMaxG];
 #pragma unroll
@@ -218,8 +218,10 @@ template <int D, int G>
 __global__ __launch_bounds__(kPT) void prefill_stats_mfma_kernel(PrefillArgs a) {
   typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
   typedef float f32x4_t __attribute__((ext_vector_type(4)));
+  typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
   constexpr int KB = D / 32;
   constexpr int kWaveRows = kChunkRows / kPW;  // 128
+  constexpr int NS = 4;                        // 16-row groups in flight per wave (current one included)
   const int pair = blockIdx.x / a.n_chunks, chunk = blockIdx.x - pair * a.n_chunks;
   const int b = pair / a.n_kv_heads, g = pair - b * a.n_kv_heads;
   const int P = a.prefill[b];
@@ -234,12 +236,13 @@ __global__ __launch_bounds__(kPT) void prefill_stats_mfma_kernel(PrefillArgs a) 
     for (int kb = 0; kb < KB; ++kb) qb[kb] = *reinterpret_cast<const uint4*>(qh + 32 * kb);
   }
   const uint16_t* kp = static_cast<const uint16_t*>(a.k_pre) + (size_t)pair * a.max_prefill * D + 8 * j;
-  // Logit stores go through a buffer resource over the pair's P * G logits;
-  // lanes without a logit to store (heads past G, rows past the wave's range)
-  // aim past it and the hardware drops the store, so no store (and no load
-  // below) sits under a branch and the loop's waits stay exact.
-  const auto lrs = __builtin_amdgcn_make_buffer_rsrc(a.logits + (size_t)pair * a.max_prefill * G, (short)0, P * G * 4,
-                                                     0x00020000);
+  // Logit stores go through a buffer resource over the pair's [G][max_prefill]
+  // logits; lanes without a logit to store (heads past G, rows past the wave's
+  // range) aim past it and the hardware drops the store, so no store (and no
+  // load below) sits under a divergent branch and the loop's waits stay exact.
+  // A whole group stores each lane's 4 rows of its head as one 16-byte cell.
+  const auto lrs = __builtin_amdgcn_make_buffer_rsrc(a.logits + (size_t)pair * a.max_prefill * G, (short)0,
+                                                     G * a.max_prefill * 4, 0x00020000);
   float m = -INFINITY, l = 0.f;
   const int last = max(r1 - 1, 0);
   auto load = [&](int R, uint4(&kk)[KB]) {  // rows clamped to the wave's last valid row
@@ -247,14 +250,11 @@ __global__ __launch_bounds__(kPT) void prefill_stats_mfma_kernel(PrefillArgs a) 
     for (int kb = 0; kb < KB; ++kb)
       kk[kb] = load_once(reinterpret_cast<const uint4*>(kp + (size_t)min(R + n, last) * D + 32 * kb));
   };
-  uint4 cur[KB], nxt[KB];
-  load(r0, cur);
-  for (int R = r0; R < r1; R += 16) {
-    load(R + 16, nxt);
+  auto process = [&](int R, const uint4(&kk)[KB]) {
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, cur[kb]),
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kk[kb]),
                                                     __builtin_bit_cast(bf16x8_t, qb[kb]), acc, 0, 0, 0);
     float sv[4];
     float mx = -INFINITY;
@@ -263,8 +263,19 @@ __global__ __launch_bounds__(kPT) void prefill_stats_mfma_kernel(PrefillArgs a) 
       const int row = R + 4 * j + i;
       sv[i] = row < r1 ? acc[i] * a.scale_log2 : -INFINITY;
       mx = fmaxf(mx, sv[i]);
-      const int off = n < G && row < r1 ? (row * G + n) * 4 : 0x7FFFFFF0;
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sv[i]), lrs, off, 0, 0);
+    }
+    if (R + 16 <= r1) {
+      const u32x4_t x = {__float_as_uint(sv[0]), __float_as_uint(sv[1]), __float_as_uint(sv[2]),
+                         __float_as_uint(sv[3])};
+      const int off = n < G ? (n * a.max_prefill + R + 4 * j) * 4 : 0x7FFFFFF0;
+      __builtin_amdgcn_raw_buffer_store_b128(x, lrs, off, 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = R + 4 * j + i;
+        const int off = n < G && row < r1 ? (n * a.max_prefill + row) * 4 : 0x7FFFFFF0;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sv[i]), lrs, off, 0, 0);
+      }
     }
     if (mx > m) {
       l *= __builtin_amdgcn_exp2f(m - mx);
@@ -272,9 +283,30 @@ __global__ __launch_bounds__(kPT) void prefill_stats_mfma_kernel(PrefillArgs a) 
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) l += sv[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[i] - m);
+  };
+  // A ring of NS group buffers: while group t is processed, groups up to
+  // t + NS - 1 are in flight.  Loads are unconditional (rows clamped to the
+  // wave's last row) and the loop has one exit, so the waits stay exact.
+  const int ng = r1 > r0 ? (r1 - r0 + 15) / 16 : 0;
+  uint4 buf[NS][KB];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) cur[kb] = nxt[kb];
+  for (int s = 0; s < NS - 1; ++s) load(r0 + 16 * s, buf[s]);
+  int t = 0;
+  while (t + NS <= ng) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      load(r0 + 16 * (t + NS - 1), buf[(s + NS - 1) % NS]);
+      process(r0 + 16 * t, buf[s]);
+      ++t;
+    }
   }
+  // Fewer than NS groups left, all of them already loaded.
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (t < ng) {
+      process(r0 + 16 * t, buf[s]);
+      ++t;
+    }
   // Combine the 4 lane groups of each head (lanes n, n + 16, n + 32, n + 48),
   // then the waves.
   ml_merge(m, l, __shfl_xor(m, 16), __shfl_xor(l, 16));
@@ -296,36 +328,6 @@ __global__ __launch_bounds__(kPT) void prefill_stats_mfma_kernel(PrefillArgs a) 
   }
 }
 
-// Pass 2: the pair's chunk statistics combined in chunk order (the same bits
-// in every chunk), then the importance of the chunk's rows from their stored
-// logits, one row per thread.
-template <class E, int D, int G>
-__global__ __launch_bounds__(kPT) void prefill_importance_kernel(PrefillArgs a) {
-  const int pair = blockIdx.x / a.n_chunks, chunk = blockIdx.x - pair * a.n_chunks;
-  const int b = pair / a.n_kv_heads;
-  const int P = a.prefill[b];
-  const int r0 = chunk * kChunkRows, r1 = min(P, r0 + kChunkRows);
-  if (r0 >= r1) return;
-  const int nck = (P + kChunkRows - 1) / kChunkRows;
-  float M[G], invL[G];
-  const float* st = a.stats + (size_t)pair * a.n_chunks * kMaxG * 2;
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float mm = -INFINITY, ll = 0.f;
-    for (int k = 0; k < nck; ++k) ml_merge(mm, ll, st[k * kMaxG * 2 + 2 * h], st[k * kMaxG * 2 + 2 * h + 1]);
-    M[h] = mm;
-    invL[h] = 1.0f / ll;
-  }
-  float* imp = a.work + (size_t)pair * a.max_prefill;
-  const float* lg = a.logits + (size_t)pair * a.max_prefill * G;
-  for (int row = r0 + (int)threadIdx.x; row < r1; row += kPT) {
-    float x = 0.f;
-#pragma unroll
-    for (int h = 0; h < G; ++h) x = fmaf(__builtin_amdgcn_exp2f(lg[(size_t)row * G + h] - M[h]), invL[h], x);
-    imp[row] = x;
-  }
-}
-
 // Key of a middle position: importance bits (non-negative floats order as
 // their bit patterns), then the complement of the position (positions are
 // below 65536): 48 bits, unique per position.
@@ -333,19 +335,43 @@ __device__ __forceinline__ uint64_t rank_key(float x, int pos) {
   return (static_cast<uint64_t>(__float_as_uint(fmaxf(x, 0.f))) << 16) | (0xFFFFu - static_cast<uint32_t>(pos));
 }
 
-template <class E, int D>
+template <int G>
 __global__ __launch_bounds__(kPT) void prefill_select_kernel(PrefillArgs a) {
   const int pair = blockIdx.x;
   const int b = pair / a.n_kv_heads;
   const int P = a.prefill[b], budget = a.budget[b];
   const int sink = a.sink, R = a.recent;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const float* imp = a.work + (size_t)pair * a.max_prefill;
+  float* imp = a.work + (size_t)pair * a.max_prefill;
   int32_t* kept = a.kept + (size_t)pair * a.max_budget;
   const int nkeep = min(P, budget);
   __shared__ uint32_t s_hist[256];
   __shared__ uint32_t s_digit, s_want;
   __shared__ uint32_t s_scan[kPT];
+
+  // The pair's statistics combined in chunk order, then every position's
+  // importance from its stored logits (written out: the call's importance
+  // output, read back by the selection below from L2).
+  {
+    const int nck = (P + kChunkRows - 1) / kChunkRows;
+    float M[G], invL[G];
+    const float* st = a.stats + (size_t)pair * a.n_chunks * kMaxG * 2;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float mm = -INFINITY, ll = 0.f;
+      for (int k = 0; k < nck; ++k) ml_merge(mm, ll, st[k * kMaxG * 2 + 2 * h], st[k * kMaxG * 2 + 2 * h + 1]);
+      M[h] = mm;
+      invL[h] = 1.0f / ll;
+    }
+    const float* lg = a.logits + (size_t)pair * a.max_prefill * G;
+    for (int i = tid; i < P; i += kPT) {
+      float x = 0.f;
+#pragma unroll
+      for (int h = 0; h < G; ++h) x = fmaf(__builtin_amdgcn_exp2f(lg[(size_t)h * a.max_prefill + i] - M[h]), invL[h], x);
+      imp[i] = x;
+    }
+    __syncthreads();  // every position's importance written (same workgroup)
+  }
 
   uint64_t thr = 0;  // a middle position is kept when its key is >= thr
   if (P > budget) {
@@ -447,7 +473,7 @@ __global__ __launch_bounds__(kPT) void prefill_copy_kernel(PrefillArgs a) {
   // any store; source rows are read once, so the loads are non-temporal.
   const int n = r1 - r0;
   if (n <= 0) return;
-  constexpr int kU = 4;
+  constexpr int kU = 8;
   constexpr int kStep = kPW * kRowsPerWave * kU;  // rows per pass of the workgroup
   constexpr int kPasses = (kCopyRows + kStep - 1) / kStep;
   int pos[kPasses][kU];
@@ -484,7 +510,7 @@ void launch_scores(const PrefillArgs& a, int n_pairs, hipStream_t s) {
     hipLaunchKernelGGL((prefill_stats_mfma_kernel<D, G>), dim3(n_pairs * a.n_chunks), dim3(kPT), 0, s, a);
   else
     hipLaunchKernelGGL((prefill_stats_kernel<E, D, G>), dim3(n_pairs * a.n_chunks), dim3(kPT), 0, s, a);
-  hipLaunchKernelGGL((prefill_importance_kernel<E, D, G>), dim3(n_pairs * a.n_chunks), dim3(kPT), 0, s, a);
+  hipLaunchKernelGGL((prefill_select_kernel<G>), dim3(n_pairs), dim3(kPT), 0, s, a);
 }
 
 template <class E, int D>
@@ -494,7 +520,6 @@ void launch_prefill(const PrefillArgs& a, int n_pairs, hipStream_t s) {
                                  launch_scores<E, D, 4>, launch_scores<E, D, 5>, launch_scores<E, D, 6>,
                                  launch_scores<E, D, 7>, launch_scores<E, D, 8>};
   kScores[a.group - 1](a, n_pairs, s);
-  hipLaunchKernelGGL((prefill_select_kernel<E, D>), dim3(n_pairs), dim3(kPT), 0, s, a);
   hipLaunchKernelGGL((prefill_copy_kernel<E, D>), dim3(n_pairs * a.n_copy), dim3(kPT), 0, s, a);
 }
 
