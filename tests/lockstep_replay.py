@@ -26,7 +26,7 @@ def replay(job: dict) -> dict:
     from threadpoolctl import threadpool_limits
 
     from oracle import OracleCache, TIE_TOLERANCE
-    from workloads import anchor_event, budgets, get_workload, initial_sequence, step_inputs
+    from workloads import anchor_event, anchor_positions, budgets, get_workload, initial_sequence, step_inputs
 
     w = get_workload(job["workload"])
     b, steps, dbg_every = job["seq"], job["steps"], job["dbg_every"]
@@ -38,8 +38,14 @@ def replay(job: dict) -> dict:
     k, v, pos, t = initial_sequence(w, b)
     bud = int(budgets(w)[b])
     res = dict(workload=w.name, seq=b, steps=0, exempt_ties=0, max_out_err=0.0, max_score_err=0.0,
-               max_lse_err=0.0, dbg_steps=0, anchor_steps=0, error=None)
+               max_lse_err=0.0, dbg_steps=0, anchor_steps=0, anchor_mass=None, anchors_kept=None, error=None)
     progress = job.get("progress")
+    # Diagnostics of the anchor workload (the caches are the GPU's: the replay
+    # follows its evictions): the share of the group's attention that lands on
+    # cached anchor tokens at the anchor events, and how many anchors are still
+    # cached at the end.
+    anchor_pos = anchor_positions(w, bud) if w.anchors else None
+    mass = []
     t0 = time.time()
     with threadpool_limits(1):
         oc = OracleCache([k], [v], [pos], [t], bud, w.n_q_heads, w.sink, w.recent)
@@ -78,12 +84,19 @@ def replay(job: dict) -> dict:
             if bad:
                 res["error"] = bad
                 break
+            if anchor_pos is not None and anchor_event(w, s) is not None:
+                n = oc.n[0]
+                on = np.isin(oc.pos[0][:, :n], anchor_pos)
+                mass.append(float((dec.scores[0] * on).sum() / (w.group * w.n_kv_heads)))
             oc.commit(slots, kn, vn)
             res["steps"] = s + 1
             res["anchor_steps"] += anchor_event(w, s) is not None
             if progress and (s + 1) % 512 == 0:
                 with open(progress, "w") as f:
                     f.write(f"{s + 1} {time.time() - t0:.1f}\n")
+    if anchor_pos is not None:
+        res["anchor_mass"] = float(np.mean(mass)) if mass else None
+        res["anchors_kept"] = float(np.isin(oc.pos[0][:, :oc.n[0]], anchor_pos).sum() / w.n_kv_heads)
     if res["error"] is None:
         kf, vf = rec["k_final"], rec["v_final"]
         if bf16:

@@ -55,7 +55,10 @@ def lockstep_results(tmp_path_factory, request):
     for r in sorted(results, key=lambda r: (r["workload"], r["seq"])):
         say(f"[lockstep] {r['workload']} seq {r['seq']}: {r['steps']} steps, {r['exempt_ties']} accepted ties, "
             f"max out err {r['max_out_err']:.2e}, max score err {r['max_score_err']:.2e}, "
-            f"max lse err {r['max_lse_err']:.2e}, {r['dbg_steps']} debug steps, {r['anchor_steps']} anchor events")
+            f"max lse err {r['max_lse_err']:.2e}, {r['dbg_steps']} debug steps, {r['anchor_steps']} anchor events"
+            + (f", attention on cached anchors at the events {r['anchor_mass']:.3f}, "
+               f"anchors cached at the end {r['anchors_kept']:.1f} of {get_workload(r['workload']).anchors}"
+               if r["anchor_mass"] is not None else ""))
     set_reporter(None)
     return {(r["workload"], r["seq"]): r for r in results}
 
