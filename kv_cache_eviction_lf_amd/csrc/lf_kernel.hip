@@ -229,16 +229,13 @@ __device__ __forceinline__ uint2 load_nt(const uint2* p) {
 
 // Logits one workgroup hands to another in the same launch (a deferred chunk
 // of a split pair, see split_tail) move through device-scope stores and loads:
-// relaxed agent-scope atomics, or buffer stores and loads with the same "sc1"
-// cache policy (on gfx950: written through the non-coherent per-XCD L2 to
-// memory, and read past it).  The writer drains its stores (s_waitcnt
-// vmcnt(0): a device-scope store has then reached memory) before it publishes
-// the word that tells the reader to look, and the reader issues its
-// device-scope loads after it has seen that word.  This is the ordering a
-// release/acquire pair would give, without the L2 write-back and invalidate
-// that only plain (non-atomic) stores and loads need.  An unsplit pair whose
-// logits go to the workspace reads them back the same way within its own
-// workgroup (a drain, then a barrier).
+// buffer stores and loads with the "sc1" cache policy of agent-scope atomics
+// (on gfx950: written through the non-coherent per-XCD L2 to memory, and read
+// past it).  The writing waves release at agent scope before the barrier
+// after which the deferred candidate word is published, and the finisher
+// acquires at agent scope after it has read that word, before its loads.  An
+// unsplit pair whose logits go to the workspace reads them back within its own
+// workgroup (its stores drained, then a barrier).
 __device__ __forceinline__ void store_wt(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -1220,6 +1217,9 @@ __device__ __forceinline__ void finish_deferred(const StepArgs& a, int pair, con
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl[h]), c));
   });
   if (!a.score_none) {
+    // The deferred chunks' logits: published before their candidates, which
+    // this workgroup has read (device-scope acquire).
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     const auto lg_rs = coh_rsrc(a.logits + (size_t)pm.slot0 * G, G * pm.lstride * 4);
     float tb = INFINITY;
     int ti = 0x7FFFFFFF;
@@ -1553,11 +1553,12 @@ __device__ __forceinline__ void split_tail(const StepArgs& a, int pair, int item
   }
   if (own_c < 0) {
   // ---- deferred (every wave): the logits go to the workspace (the fp32
-  // stream and long chunks wrote them already) and every wave's stores
-  // complete before the candidate says so
+  // stream and long chunks wrote them already); every wave releases its
+  // stores at device scope before the barrier after which thread 0 publishes
+  // the deferred candidate, and the finisher acquires after reading it.
   if constexpr (T::kEpl == 8)
     if (lmode == kLogitsFull && !a.score_none) spill_logits<D, G>(a, pm, start, count, s_logit);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   __syncthreads();
   if (tid == 0) {
     xstore(a.xcand + 2 * (size_t)item, xword(INFINITY, epoch));
