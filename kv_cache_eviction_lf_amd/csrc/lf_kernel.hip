@@ -1071,19 +1071,25 @@ __device__ __forceinline__ bool pair_stats_all(const StepArgs& a, int item0, int
     for (int h = 0; h < G; ++h) invL[h] = __builtin_amdgcn_rcpf(L[h]);
     return true;
   }
-  float Mh, Lh, w;
-  if (!pair_stats_hc<D, G>(a, item0, nchunk, k, epoch, s_snew, own, s_part_w, bounded, deadline, Mh, Lh, w))
-    return false;
-  const int lane = threadIdx.x & 63;
-  const float il = __builtin_amdgcn_rcpf(Lh);  // one reciprocal per lane, read back per head
+  auto run = [&](auto kc) -> bool {
+    const int kk = kc;
+    float Mh, Lh, w;
+    if (!pair_stats_hc<D, G>(a, item0, nchunk, kk, epoch, s_snew, own, s_part_w, bounded, deadline, Mh, Lh, w))
+      return false;
+    const int lane = threadIdx.x & 63;
+    const float il = __builtin_amdgcn_rcpf(Lh);  // one reciprocal per lane, read back per head
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    M[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Mh), h << k));
-    L[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Lh), h << k));
-    invL[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(il), h << k));
-    wl[h] = __shfl(w, (h << k) + (lane & ((1 << k) - 1)));  // lane c < 2^k takes (h, c)'s weight
-  }
-  return true;
+    for (int h = 0; h < G; ++h) {
+      M[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Mh), h << kk));
+      L[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Lh), h << kk));
+      invL[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(il), h << kk));
+      wl[h] = __shfl(w, (h << kk) + (lane & ((1 << kk) - 1)));  // lane c < 2^k takes (h, c)'s weight
+    }
+    return true;
+  };
+  // four chunks per pair (the usual split) get the lane arithmetic with k fixed
+  if (k == 2) return run(std::integral_constant<int, 2>{});
+  return run(k);
 }
 
 // Output rows of the heads in `heads` (bit h): every chunk's weighted value
@@ -1468,9 +1474,9 @@ __device__ __forceinline__ void split_tail(const StepArgs& a, int pair, int item
     if (v == 1u) {
       // ---- this chunk's output rows.  With few chunks, unit u = tid - 64
       // (+ 192 per pass) writes dims d, d + 1 (d = 2 (u % (D / 2))) of the head
-      // of rank u / (D / 2); the first pass's value sums are requested before
-      // the chunk scores its slots.  The arithmetic is split_output's, in the
-      // same order: the rows have the same bits whichever path writes them.
+      // of rank u / (D / 2), once the chunk has scored its slots.  The
+      // arithmetic is split_output's, in the same order: the rows have the
+      // same bits whichever path writes them.
       const int nh = __builtin_popcount(my_heads), units = nh * (D / 2);
       const bool fast_out = nchunk <= kOutPre;
       const int b = pair / a.n_kv_heads, g = pair - b * a.n_kv_heads;
@@ -1515,8 +1521,9 @@ __device__ __forceinline__ void split_tail(const StepArgs& a, int pair, int item
         if (d == 0 && a.dbg_lse)
           a.dbg_lse[(size_t)b * a.n_q_heads + g * G + h] = (Mh + __log2f(Lh)) * 0.6931471805599453f;
       };
+      // (value sums loaded before scoring would only delay the slots' scores,
+      // which the candidate waits on)
       uint64_t x0[kOutPre][2];
-      if (fast_out) unit_cells(tid - 64, x0);
       if (!a.score_none) {
         float best = INFINITY;
         int besti = 0x7FFFFFFF;
@@ -1529,6 +1536,7 @@ __device__ __forceinline__ void split_tail(const StepArgs& a, int pair, int item
         lds_count(&s_flags[8]);
       }
       if (fast_out) {
+        unit_cells(tid - 64, x0);
         unit_write(tid - 64, x0);
         for (int u = tid - 64 + (kThreads - 64); u - lane < units; u += kThreads - 64) {
           uint64_t x[kOutPre][2];
