@@ -168,7 +168,7 @@ lf_status make_layout(const lf_config* cfg, const std::vector<int32_t>& bud, lf:
   L.items = off;
   off = align_up(off + sizeof(lf::WorkItem) * W);
   L.xcell = off;
-  off = align_up(off + sizeof(uint64_t) * (size_t)group * (cfg->head_dim + 2) * W);
+  off = align_up(off + sizeof(uint64_t) * (size_t)group * cfg->head_dim * W);
   L.xcand = off;
   off = align_up(off + sizeof(uint64_t) * 2 * W);
   L.xstat = off;

@@ -84,7 +84,7 @@ struct StepArgs {
   const WorkItem* items;
   // Exchange between the chunks of a split pair, every value a 64-bit word
   // whose high half is the pair's epoch of the step that wrote it:
-  uint64_t* xcell;   // [n_items][G][d + 2]: the chunk's weighted value sums (max, sum slots unused)
+  uint64_t* xcell;   // [n_items][G][d]: the chunk's weighted value sums
   uint64_t* xcand;   // [n_items][2]: the chunk's (score) and (slot | deferred << 31) candidate
   uint64_t* xstat;   // [n_items][kThreads / 64][G][2]: (max, sum) of every wave of the chunk, per head
   uint32_t* count;   // [n_pairs]: chunks of the pair done with the step (reset by the finisher)

@@ -1128,7 +1128,7 @@ __device__ __forceinline__ void split_output(const StepArgs& a, int pair, int it
         bool ok = true;
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-          x[j] = xload(a.xcell + ((size_t)(item0 + min(c0 + j, nchunk - 1)) * G + h) * (D + 2) + dim);
+          x[j] = xload(a.xcell + ((size_t)(item0 + min(c0 + j, nchunk - 1)) * G + h) * D + dim);
 #pragma unroll
         for (int j = 0; j < 8; ++j) ok = ok && xfresh(x[j], epoch);
         if (!__builtin_amdgcn_ballot_w64(!ok)) break;
@@ -1448,10 +1448,11 @@ __device__ __forceinline__ void split_tail(const StepArgs& a, int pair, int item
       set_protect_bits<T, D, G>(a, pair, budget, s_bits, s_pre, 64, 64);
       lds_set(&s_flags[0], 1u);
     }
-    // Value sums two dimensions at a time: the waves' weights exp2(m_w - mm)
-    // once per pair of dimensions, the sums in wave order as before.
+    // Value sums two dimensions at a time, dim and dim + D / 2 (so that each
+    // store instruction of a wave fills whole lines): the waves' weights
+    // exp2(m_w - mm) once per pair of dimensions, the sums in wave order.
     for (int u = tid - 64; u < G * D / 2; u += kThreads - 64) {
-      const int h = u / (D / 2), dim = 2 * (u - h * (D / 2));
+      const int h = u / (D / 2), dim = u - h * (D / 2);
       float mw[kWaves], mm = kNegBig;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
@@ -1462,18 +1463,18 @@ __device__ __forceinline__ void split_tail(const StepArgs& a, int pair, int item
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
         const float f = fast_exp2(mw[w] - mm);
-        const float2 x = *reinterpret_cast<const float2*>(s_work + (w * G + h) * (D + 2) + dim);
-        s0 = fmaf(x.x, f, s0);
-        s1 = fmaf(x.y, f, s1);
+        const float* x = s_work + (w * G + h) * (D + 2) + dim;
+        s0 = fmaf(x[0], f, s0);
+        s1 = fmaf(x[D / 2], f, s1);
       }
-      uint64_t* xc = a.xcell + ((size_t)item * G + h) * (D + 2) + dim;
+      uint64_t* xc = a.xcell + ((size_t)item * G + h) * D + dim;
       xstore(xc, xword(s0, epoch));
-      xstore(xc + 1, xword(s1, epoch));
+      xstore(xc + D / 2, xword(s1, epoch));
     }
     const uint32_t v = lds_wait(&s_flags[1], a);
     if (v == 1u) {
       // ---- this chunk's output rows.  With few chunks, unit u = tid - 64
-      // (+ 192 per pass) writes dims d, d + 1 (d = 2 (u % (D / 2))) of the head
+      // (+ 192 per pass) writes dims d, d + D / 2 (d = u % (D / 2)) of the head
       // of rank u / (D / 2), once the chunk has scored its slots.  The
       // arithmetic is split_output's, in the same order: the rows have the
       // same bits whichever path writes them.
@@ -1481,13 +1482,13 @@ __device__ __forceinline__ void split_tail(const StepArgs& a, int pair, int item
       const bool fast_out = nchunk <= kOutPre;
       const int b = pair / a.n_kv_heads, g = pair - b * a.n_kv_heads;
       auto unit_cells = [&](int u, uint64_t (&x)[kOutPre][2]) {
-        const int k = u < units ? u / (D / 2) : 0, d = 2 * (u % (D / 2));
+        const int k = u < units ? u / (D / 2) : 0, d = u % (D / 2);
         const int h = min(chunk + k * nchunk, G - 1);  // in range for lanes past the units
 #pragma unroll
         for (int j = 0; j < kOutPre; ++j) {
-          const uint64_t* cell = a.xcell + ((size_t)(item0 + min(j, nchunk - 1)) * G + h) * (D + 2) + d;
+          const uint64_t* cell = a.xcell + ((size_t)(item0 + min(j, nchunk - 1)) * G + h) * D + d;
           x[j][0] = xload(cell);
-          x[j][1] = xload(cell + 1);
+          x[j][1] = xload(cell + D / 2);
         }
       };
       auto unit_write = [&](int u, uint64_t (&x)[kOutPre][2]) {
@@ -1505,18 +1506,18 @@ __device__ __forceinline__ void split_tail(const StepArgs& a, int pair, int item
           unit_cells(u, x);
         }
         if (!act) return;
-        const int k = u / (D / 2), d = 2 * (u % (D / 2));
+        const int k = u / (D / 2), d = u % (D / 2);
         const int h = chunk + k * nchunk;
         const float sn = s_stat[h], Mh = s_stat[G + h], Lh = s_stat[2 * G + h], il = s_stat[3 * G + h];
         const elem* vnp = T::kEpl == 8 ? reinterpret_cast<const elem*>(s_pre) + (G + 1) * D
                                        : static_cast<const elem*>(a.v_new) + (size_t)pair * D;
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          float acc = fast_exp2(sn - Mh) * load_elem<T>(vnp, d + e);
+          float acc = fast_exp2(sn - Mh) * load_elem<T>(vnp, d + e * (D / 2));
 #pragma unroll
           for (int j = 0; j < kOutPre; ++j)
             if (j < nchunk) acc = fmaf(xval(x[j][e]), s_stat[4 * G + k * kMaxChunks + j], acc);
-          store_elem<T>(a.out, ((size_t)b * a.n_q_heads + g * G + h) * D + d + e, acc * il);
+          store_elem<T>(a.out, ((size_t)b * a.n_q_heads + g * G + h) * D + d + e * (D / 2), acc * il);
         }
         if (d == 0 && a.dbg_lse)
           a.dbg_lse[(size_t)b * a.n_q_heads + g * G + h] = (Mh + __log2f(Lh)) * 0.6931471805599453f;
