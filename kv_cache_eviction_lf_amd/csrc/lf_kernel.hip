@@ -1245,30 +1245,15 @@ __device__ __forceinline__ void finish_deferred(const StepArgs& a, int pair, con
   if (wave == 0) insert_token<T, D>(a, pair, pm, besti, insert_piece<T, D, G>(a, pair, s_pre), true);
 }
 
-// A wave's count of waves that are done with something (workgroup scope):
-// waits until it reaches n, with the safety bound of lds_wait.
-__device__ __forceinline__ void lds_wait_count(uint32_t* f, uint32_t n, const StepArgs& a) {
-  const uint64_t deadline = __builtin_amdgcn_s_memrealtime() + kSafetyTicks;
-  while (__hip_atomic_load(f, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < n) {
-    if (__builtin_amdgcn_s_memrealtime() > deadline) {
-      if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_or(a.fault, kFaultValues, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      return;
-    }
-    __builtin_amdgcn_s_sleep(1);
-  }
-}
-__device__ __forceinline__ void lds_count(uint32_t* f) {
-  if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_add(f, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
-
 // End of the step for one chunk of a split pair (see the protocol above).
 // s_work holds the waves' partials [wave][G][D + 2] and the bitmap area,
 // s_logit the streaming waves' logits when lmode == kLogitsFull, s_stat
-// (bf16) the incoming token's logits from the stream.  s_flags (LDS, zeroed
-// at workgroup start) carries the hand-overs between the waves: [0] bitmap
-// ready, [1] statistics seen (1) or not (2), [2] finisher done (1) or
-// deferred chunks to finish (2), [3 .. 6] the finisher's fast minimum, [7]
-// the deferred ticket, [8] waves 1-3 done scoring.
+// (bf16) the incoming token's logits from the stream.  Two workgroup
+// barriers hand over between the waves: the first once wave 0 has the pair's
+// statistics in s_stat (or gave up waiting), the second once every wave has
+// left its minimum in s_arg.  s_flags (LDS, zeroed at workgroup start) carries
+// [1] statistics seen (1) or not (2), [2] finisher done (1) or deferred chunks
+// to finish (2), [3 .. 6] the finisher's fast minimum, [7] the deferred ticket.
 // Wave 0 runs the critical path (statistics, ticket, finish); every wave
 // scores a share of the chunk's slots; waves 1-3 build the bitmap, publish the
 // partial and write the output rows.
@@ -1379,14 +1364,14 @@ __device__ __forceinline__ void split_tail(const StepArgs& a, int pair, int item
           ++k;
         }
     }
-    lds_set(&s_flags[1], seen ? 1u : 2u);
+    if (lane == 0) s_flags[1] = seen ? 1u : 2u;
+    __syncthreads();  // first hand-over: the statistics to waves 1-3 (the bitmap is complete)
     if (seen) {
       float best = INFINITY;
       int besti = 0x7FFFFFFF;
       if (!a.score_none) {
-        lds_wait(&s_flags[0], a);  // bitmap ready
         score_share(best, besti);
-        lds_wait_count(&s_flags[8], kWaves - 1, a);  // the other waves' minima
+        __syncthreads();  // second hand-over: the other waves' minima
 #pragma unroll
         for (int w = 1; w < kWaves; ++w) argmin_merge(best, besti, s_arg[w], reinterpret_cast<const int*>(s_arg)[kWaves + w]);
       }
@@ -1446,7 +1431,6 @@ __device__ __forceinline__ void split_tail(const StepArgs& a, int pair, int item
     if (wave == 1) {
       clear_protect_bits(s_bits, budget, 64, 64);
       set_protect_bits<T, D, G>(a, pair, budget, s_bits, s_pre, 64, 64);
-      lds_set(&s_flags[0], 1u);
     }
     // Value sums two dimensions at a time, dim and dim + D / 2 (so that each
     // store instruction of a wave fills whole lines): the waves' weights
@@ -1471,7 +1455,8 @@ __device__ __forceinline__ void split_tail(const StepArgs& a, int pair, int item
       xstore(xc, xword(s0, epoch));
       xstore(xc + D / 2, xword(s1, epoch));
     }
-    const uint32_t v = lds_wait(&s_flags[1], a);
+    __syncthreads();  // first hand-over (wave 0 passes it once the statistics are in s_stat)
+    const uint32_t v = s_flags[1];
     if (v == 1u) {
       // ---- this chunk's output rows.  With few chunks, unit u = tid - 64
       // (+ 192 per pass) writes dims d, d + D / 2 (d = u % (D / 2)) of the head
@@ -1528,13 +1513,12 @@ __device__ __forceinline__ void split_tail(const StepArgs& a, int pair, int item
       if (!a.score_none) {
         float best = INFINITY;
         int besti = 0x7FFFFFFF;
-        lds_wait(&s_flags[0], a);  // bitmap ready
         score_share(best, besti);
         if (lane == 0) {
           s_arg[wave] = best;
           reinterpret_cast<int*>(s_arg)[kWaves + wave] = besti;
         }
-        lds_count(&s_flags[8]);
+        __syncthreads();  // second hand-over
       }
       if (fast_out) {
         unit_cells(tid - 64, x0);
