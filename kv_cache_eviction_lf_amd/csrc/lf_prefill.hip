@@ -87,6 +87,14 @@ __device__ __forceinline__ uint4 load_once(const uint4* p) {
   return make_uint4(x[0], x[1], x[2], x[3]);
 }
 
+// 16-byte non-temporal store (rows written once here; the copy of the kept
+// rows measured 2.5 % faster than with plain stores).
+__device__ __forceinline__ void store_once(uint4* p, const uint4& v) {
+  typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+  const u32x4_t x = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(x, reinterpret_cast<u32x4_t*>(p));
+}
+
 // (max, sum of exp2(x - max)) pairs combined.
 __device__ __forceinline__ void ml_merge(float& m, float& l, float m2, float l2) {
   const float mn = fmaxf(m, m2);
@@ -97,6 +105,7 @@ __device__ __forceinline__ void ml_merge(float& m, float& l, float m2, float l2)
 // Rows of one chunk of the score passes: pairs are split so that short
 // batches still fill the device.
 constexpr int kChunkRows = kPrefillChunk;
+constexpr int kSel = 8;  // positions per thread whose loads the selection pass issues together
 
 template <class E, int D, int G>
 struct ScoreCore {
@@ -158,6 +167,7 @@ __global__ __launch_bounds__(kPT) void prefill_stats_kernel(PrefillArgs a) {
   const int pair = blockIdx.x / a.n_chunks, chunk = blockIdx.x - pair * a.n_chunks;
   const int b = pair / a.n_kv_heads;
   const int P = a.prefill[b];
+  if (chunk * kChunkRows >= P) return;  // past this prefill (the grid covers the longest)
   const int r0 = chunk * kChunkRows, r1 = min(P, r0 + kChunkRows);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   float m[G], l[G];
@@ -225,6 +235,7 @@ __global__ __launch_bounds__(kPT) void prefill_stats_mfma_kernel(PrefillArgs a) 
   const int pair = blockIdx.x / a.n_chunks, chunk = blockIdx.x - pair * a.n_chunks;
   const int b = pair / a.n_kv_heads, g = pair - b * a.n_kv_heads;
   const int P = a.prefill[b];
+  if (chunk * kChunkRows >= P) return;  // past this prefill (the grid covers the longest)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, n = lane & 15, j = lane >> 4;
   const int r0 = chunk * kChunkRows + wave * kWaveRows;
   const int r1 = min(P, r0 + kWaveRows);  // this wave's rows [r0, r1)
@@ -363,12 +374,25 @@ __global__ __launch_bounds__(kPT) void prefill_select_kernel(PrefillArgs a) {
       M[h] = mm;
       invL[h] = 1.0f / ll;
     }
+    // kSel positions per thread and pass, their logits loaded before any
+    // store (the compiler cannot move a load above a store it cannot tell
+    // apart), so a pass costs one memory round trip rather than kSel.
     const float* lg = a.logits + (size_t)pair * a.max_prefill * G;
-    for (int i = tid; i < P; i += kPT) {
-      float x = 0.f;
+    for (int i0 = tid; i0 < P; i0 += kSel * kPT) {
+      float x[kSel][G];
 #pragma unroll
-      for (int h = 0; h < G; ++h) x = fmaf(__builtin_amdgcn_exp2f(lg[(size_t)h * a.max_prefill + i] - M[h]), invL[h], x);
-      imp[i] = x;
+      for (int u = 0; u < kSel; ++u) {
+        const int i = min(i0 + u * kPT, P - 1);
+#pragma unroll
+        for (int h = 0; h < G; ++h) x[u][h] = lg[(size_t)h * a.max_prefill + i];
+      }
+#pragma unroll
+      for (int u = 0; u < kSel; ++u) {
+        float y = 0.f;
+#pragma unroll
+        for (int h = 0; h < G; ++h) y = fmaf(__builtin_amdgcn_exp2f(x[u][h] - M[h]), invL[h], y);
+        if (i0 + u * kPT < P) imp[i0 + u * kPT] = y;
+      }
     }
     __syncthreads();  // every position's importance written (same workgroup)
   }
@@ -382,9 +406,16 @@ __global__ __launch_bounds__(kPT) void prefill_select_kernel(PrefillArgs a) {
       const int shift = 40 - 8 * pass;
       for (int i = tid; i < 256; i += kPT) s_hist[i] = 0u;
       __syncthreads();
-      for (int i = lo + tid; i < hi; i += kPT) {
-        const uint64_t key = rank_key(imp[i], i);
-        if ((key & mask) == prefix) atomicAdd(&s_hist[(key >> shift) & 255u], 1u);
+      for (int i0 = lo + tid; i0 < hi; i0 += kSel * kPT) {
+        float v[kSel];
+#pragma unroll
+        for (int u = 0; u < kSel; ++u) v[u] = imp[min(i0 + u * kPT, hi - 1)];
+#pragma unroll
+        for (int u = 0; u < kSel; ++u) {
+          const int i = i0 + u * kPT;
+          const uint64_t key = rank_key(v[u], i);
+          if (i < hi && (key & mask) == prefix) atomicAdd(&s_hist[(key >> shift) & 255u], 1u);
+        }
       }
       __syncthreads();
       if (wave == 0) {
@@ -429,11 +460,18 @@ __global__ __launch_bounds__(kPT) void prefill_select_kernel(PrefillArgs a) {
   // Position-ordered compaction: thread t scans positions [t per, (t+1) per).
   const int per = (P + kPT - 1) / kPT;
   const int p0 = min(P, tid * per), p1 = min(P, p0 + per);
-  auto keep = [&](int pos) {
-    return P <= budget || pos < sink || pos >= P - R || rank_key(imp[pos], pos) >= thr;
+  auto keep = [&](int pos, float x) {
+    return P <= budget || pos < sink || pos >= P - R || rank_key(x, pos) >= thr;
   };
+  // The thread's keep flags, kSel positions per load batch.
   uint32_t n = 0;
-  for (int pos = p0; pos < p1; ++pos) n += keep(pos) ? 1u : 0u;
+  for (int q0 = p0; q0 < p1; q0 += kSel) {
+    float v[kSel];
+#pragma unroll
+    for (int u = 0; u < kSel; ++u) v[u] = imp[min(q0 + u, p1 - 1)];
+#pragma unroll
+    for (int u = 0; u < kSel; ++u) n += q0 + u < p1 && keep(q0 + u, v[u]) ? 1u : 0u;
+  }
   s_scan[tid] = n;
   __syncthreads();
   for (int o = 1; o < kPT; o <<= 1) {  // inclusive scan (Hillis-Steele)
@@ -443,8 +481,14 @@ __global__ __launch_bounds__(kPT) void prefill_select_kernel(PrefillArgs a) {
     __syncthreads();
   }
   uint32_t j = s_scan[tid] - n;
-  for (int pos = p0; pos < p1; ++pos)
-    if (keep(pos) && j < static_cast<uint32_t>(nkeep)) kept[j++] = pos;  // exactly nkeep are kept
+  for (int q0 = p0; q0 < p1; q0 += kSel) {
+    float v[kSel];
+#pragma unroll
+    for (int u = 0; u < kSel; ++u) v[u] = imp[min(q0 + u, p1 - 1)];
+#pragma unroll
+    for (int u = 0; u < kSel; ++u)
+      if (q0 + u < p1 && keep(q0 + u, v[u]) && j < static_cast<uint32_t>(nkeep)) kept[j++] = q0 + u;  // exactly nkeep are kept
+  }
   __syncthreads();  // kept[] of this pair complete (same workgroup)
 }
 
@@ -470,7 +514,8 @@ __global__ __launch_bounds__(kPT) void prefill_copy_kernel(PrefillArgs a) {
   uint4* vdst = reinterpret_cast<uint4*>(static_cast<elem*>(a.v_cache) + (size_t)pair * a.max_budget * D);
   // Each lane's kept positions first (independent loads, one round trip),
   // then kU rows per lane group per pass with all their loads issued before
-  // any store; source rows are read once, so the loads are non-temporal.
+  // any store; rows are read once and written once, so loads and stores are
+  // non-temporal.
   const int n = r1 - r0;
   if (n <= 0) return;
   constexpr int kU = 8;
@@ -497,8 +542,8 @@ __global__ __launch_bounds__(kPT) void prefill_copy_kernel(PrefillArgs a) {
     for (int u = 0; u < kU; ++u) {
       const int i = ps * kStep + wave * kRowsPerWave * kU + u * kRowsPerWave + sub;
       if (i < n) {
-        kdst[(size_t)(r0 + i) * kPieces + piece] = kx[u];
-        vdst[(size_t)(r0 + i) * kPieces + piece] = vx[u];
+        store_once(kdst + (size_t)(r0 + i) * kPieces + piece, kx[u]);
+        store_once(vdst + (size_t)(r0 + i) * kPieces + piece, vx[u]);
       }
     }
   }
