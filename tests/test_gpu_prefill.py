@@ -29,6 +29,10 @@ CASES = [
     _case("pf_f32_g5", 2, 10, 2, 128, "f32", [200, 250], [600, 100], 4, 8, 640, 22),
     _case("pf_bf16_g8_d64", 2, 16, 2, 64, "bf16", [128, 128], [4000, 129], 2, 8, 4096, 23),
     _case("pf_bf16_g1_nowin", 1, 4, 4, 128, "bf16", [1000], [3000], 0, 0, 3072, 24),
+    # The ragged batch's shape (G 5, d 128, sink 4, recent 64): its smallest and
+    # largest budgets with prefills up to twice the budget, so the decode leg
+    # starts from the method's own compression at full size (split pairs).
+    _case("pf_ragged_shape", 3, 40, 8, 128, "bf16", [1024, 4096, 8192], [2048, 4100, 16384], 4, 64, 16384, 25),
 ]
 
 
