@@ -20,6 +20,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -95,17 +96,26 @@ def algorithmic_bytes(w, bud, stored: bool = True) -> int:
     return kv + new + qo
 
 
+def code_sha256(text: str) -> str:
+    """sha256 of C++/HIP source with its comments, trailing blanks and empty
+    lines removed: it changes with the code and not with its comments (the
+    kernel sources hold no string literal that contains a comment marker)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*", "", line).rstrip() for line in text.splitlines())
+    return hashlib.sha256("\n".join(line for line in lines if line).encode()).hexdigest()
+
+
 def profiled_traffic(workload: str):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
-    summary of this workload, if it was taken on the current kernel source."""
+    summary of this workload, if it was taken on the current kernel code."""
     path = os.path.join(ROOT, "profiles", f"lf_step_kernel_{workload}_traffic.json")
     src = os.path.join(ROOT, "kv_cache_eviction_lf_amd", "csrc", "lf_kernel.hip")
     try:
         rec = json.load(open(path))
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        sha = code_sha256(open(src).read())
     except (OSError, ValueError):
         return None
-    return rec.get("traffic_bytes_per_launch") if rec.get("kernel_source_sha256") == sha else None
+    return rec.get("traffic_bytes_per_launch") if rec.get("kernel_code_sha256") == sha else None
 
 
 def host_cores() -> int:

@@ -867,8 +867,9 @@ __device__ __forceinline__ void pair_tail(const StepArgs& a, int pair, const Pai
 
 // ---------------------------------------------------------------------------
 // Split pairs.  The chunks of a pair are separate workgroups of the same
-// launch.  Each keeps its rows' logits on chip and publishes its merged
-// partial (weighted value sums, then max and sum per head) as exchange words.
+// launch.  Each keeps its rows' logits on chip; every wave publishes its own
+// max and sum per head as exchange words when its stream ends, and the chunk
+// then its weighted value sums.
 // Every chunk then waits, for a bounded time, until all chunks of its pair
 // have published their statistics, computes the step's global max and
 // normaliser per head itself (the same bits in every chunk), scores its own
