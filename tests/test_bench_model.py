@@ -1,7 +1,8 @@
 """The benchmark's byte model against the per-step sizes worked out by hand
 from the configurations (K and V read once, the incoming token read and
-written into its slot, q read and the output written), and its refusal of
-more than one GPU.  CPU only."""
+written into its slot, q read and the output written), its refusal of more
+than one GPU, and the code hash that ties committed counters to the kernel.
+CPU only."""
 from __future__ import annotations
 
 import importlib.util
@@ -49,3 +50,16 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_code_hash_follows_code_not_comments():
+    # The committed HBM counters stay attached to the kernel while only its
+    # comments change, and are dropped as soon as its code does.
+    src = "// header\n__global__ void k(float* x) {  // trailing\n  /* block\n     comment */\n  x[0] = 1.f;\n\n}\n"
+    reworded = "// other words\n__global__ void k(float* x) {\n  x[0] = 1.f;  /* another */\n}\n"
+    changed = "// header\n__global__ void k(float* x) {  // trailing\n  x[0] = 2.f;\n}\n"
+    b = _bench()
+    assert b.code_sha256(src) == b.code_sha256(reworded)
+    assert b.code_sha256(src) != b.code_sha256(changed)
+    path = os.path.join(ROOT, "kv_cache_eviction_lf_amd", "csrc", "lf_kernel.hip")
+    assert len(b.code_sha256(open(path).read())) == 64
