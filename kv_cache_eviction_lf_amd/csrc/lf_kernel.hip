@@ -596,7 +596,7 @@ __device__ __forceinline__ void block_argmin(float& best, int& besti, float* s_a
 // merge area holds the bitmap and the argmin candidates (Shape::kBitsOffset).
 template <class T, int D, int G>
 __device__ __forceinline__ void pair_tail(const StepArgs& a, int pair, const PairMeta& pm, const float* s_part, float* s_tail,
-                          const float* s_logit, int lmode, const float* s_pre) {
+                          const float* s_logit, int lmode, const float* s_pre, const float* s_snew) {
   using elem = typename T::elem;
   constexpr int kOut = (G * D + kThreads - 1) / kThreads;  // output elements per thread
   // float4 logit cells per head preloaded from the workspace (more when the
@@ -639,9 +639,17 @@ __device__ __forceinline__ void pair_tail(const StepArgs& a, int pair, const Pai
     }
   }
   QReg<T, G> q;
-  uint4 kn;
   float snew[G];
-  new_token_logits<T, D, G>(a, pair, s_pre, q, kn, snew);
+  if constexpr (T::kEpl == 8) {
+    // The incoming token's logits came from wave 0's stream (s_snew); q (the
+    // LDS copy) is only used to rescore candidate slots from their key rows.
+    load_q<T, G>(q, reinterpret_cast<const elem*>(s_pre) + (lane % LPR) * EPL, D, a.scale_log2);
+#pragma unroll
+    for (int h = 0; h < G; ++h) snew[h] = s_snew[h];
+  } else {
+    uint4 kn;
+    new_token_logits<T, D, G>(a, pair, s_pre, q, kn, snew);
+  }
   // ---- global max and normaliser: the chunk's merged partial and the
   // incoming token (every thread computes them itself).
   float M[G], invL[G], en[G], w0[G];
@@ -2068,11 +2076,11 @@ __device__ __forceinline__ void stream_mfma(const StepArgs& a, int pair, int sta
     xstore(xs, xword(m, pm.epoch));
     xstore(xs + 1, xword(lsum, pm.epoch));
   }
-  // The incoming token's logits, for a split pair's tail: one more row group
-  // of products with k_new as every row (from wave 0's LDS copy, complete once
+  // The incoming token's logits, for the pair's tail: one more row group of
+  // products with k_new as every row (from wave 0's LDS copy, complete once
   // any of its stream loads was waited for; without a row, waited for here),
   // so lane h of row group 0 holds q_h . k_new.
-  if (wave == 0 && pm.nchunk > 1) {
+  if (wave == 0) {
     if (Rend <= R0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     const uint16_t* kn = reinterpret_cast<const uint16_t*>(s_pre) + G * D + 8 * j;
     f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
@@ -2166,7 +2174,7 @@ void lf_step_kernel(StepArgs a) {
   __syncthreads();  // merged partial complete, bitmap cleared
   set_protect_bits<T, D, G>(a, pair, pm.budget, s_bits, s_pre);
   __syncthreads();
-  pair_tail<T, D, G>(a, pair, pm, s_part, s_work, s_logit, lmode, s_pre);
+  pair_tail<T, D, G>(a, pair, pm, s_part, s_work, s_logit, lmode, s_pre, s_stat);
 }
 
 template <class T, int D, int G>
