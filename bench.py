@@ -441,7 +441,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
-        "data": "synthetic (seeded N(0,1) q/k/v, bf16 round-to-nearest-even)",
+        "data": ("synthetic (seeded N(0,1) q/k/v, bf16 round-to-nearest-even)" if w.dtype == "bf16" else
+                 "synthetic (seeded N(0,1) q/k/v, float32)"),
         "config": {
             "workload": w.name,
             "batch": w.batch,
