@@ -397,28 +397,37 @@ def main():
         # The same read probe over the step's own byte count, one launch per
         # graph node and rotating buffers past the Infinity Cache like the
         # layer caches: what a kernel that only streams the step's bytes takes
-        # per launch at this size (ramp and launch included).
+        # per launch at this size (ramp and launch included).  Below a few
+        # hundred MB the fastest grid depends on the size, so several grids
+        # are timed and the fastest is the ceiling.
         del src, dst
         ns = (step_bytes + 15) // 16 * 16
         Lp = max(2, -(-(512 << 20) // ns))
         bufs = [torch.empty(ns, dtype=torch.uint8, device=dev) for _ in range(Lp)]
         nodes = max(8, min(512, (64 << 30) // (ns * 8)))
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=cs):
-            sh = torch.cuda.current_stream().cuda_stream
-            for k in range(nodes):
-                _lib.lf_probe_read(bufs[k % Lp].data_ptr(), ns, sink.data_ptr(), sh)
-        g.replay()
-        torch.cuda.synchronize()
-        a.record(cur)
-        for _ in range(3):
+        per_grid = {}
+        for grid in (256, 512, 1024, 2048):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cs):
+                sh = torch.cuda.current_stream().cuda_stream
+                for k in range(nodes):
+                    _lib.lf_probe_read_grid(bufs[k % Lp].data_ptr(), ns, grid, sink.data_ptr(), sh)
             g.replay()
-        b.record(cur)
-        torch.cuda.synchronize()
-        us = a.elapsed_time(b) * 1e3 / (3 * nodes)
+            torch.cuda.synchronize()
+            a.record(cur)
+            for _ in range(3):
+                g.replay()
+            b.record(cur)
+            torch.cuda.synchronize()
+            per_grid[grid] = a.elapsed_time(b) * 1e3 / (3 * nodes)
+            del g
+        best = min(per_grid, key=per_grid.get)
+        us = per_grid[best]
         res["read_step_bytes_us"] = round(us, 2)
         res["read_step_bytes_GBps"] = round(ns / us / 1e3, 1)
-        del bufs, g
+        res["read_step_bytes_grid"] = best
+        res["read_step_bytes_us_by_grid"] = {str(k): round(v, 2) for k, v in per_grid.items()}
+        del bufs
         probe = res
 
     base = base1 = None

@@ -29,6 +29,14 @@ lf_status lf_probe_copy(const void* src, void* dst, size_t bytes, void* stream);
 lf_status lf_probe_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
 int32_t lf_probe_read_sink_words(void);
 
+/* lf_probe_read over a grid of `n_blocks` workgroups (1 ... 
+ * lf_probe_read_sink_words()) instead of the default: below a few hundred MB
+ * per launch the fastest grid depends on the size (one workgroup per compute
+ * unit reads 32-64 MB faster than the default grid), so a size-matched ceiling
+ * takes the fastest of several.  sink receives n_blocks words.  Returns
+ * LF_ERR_ARG for a grid outside that range. */
+lf_status lf_probe_read_grid(const void* src, size_t bytes, int32_t n_blocks, uint32_t* sink, void* stream);
+
 /* Launch `n_blocks` (>= 1) workgroups of 256 threads that do nothing.  Timed
  * in a graph of many such nodes it gives the launch floor a decode step of the
  * same grid pays before moving any byte. */

@@ -73,6 +73,7 @@ PROTOTYPES = {
     "lf_probe_copy": (c_int32, [c_void_p, c_void_p, c_size_t, c_void_p]),
     "lf_probe_read": (c_int32, [c_void_p, c_size_t, c_void_p, c_void_p]),
     "lf_probe_read_sink_words": (c_int32, []),
+    "lf_probe_read_grid": (c_int32, [c_void_p, c_size_t, c_int32, c_void_p, c_void_p]),
     "lf_probe_empty": (c_int32, [c_int32, c_void_p]),
     "lf_prefill_work_bytes": (c_int32, [POINTER(lf_config), c_int32, POINTER(c_size_t)]),
     "lf_set_split_wait": (c_int32, [c_void_p, c_int32]),
@@ -280,6 +281,11 @@ def lf_probe_copy(src: int, dst: int, nbytes: int, stream: int = 0) -> None:
 def lf_probe_read(src: int, nbytes: int, sink: int, stream: int = 0) -> None:
     _check(load_library().lf_probe_read(c_void_p(src), c_size_t(nbytes), c_void_p(sink), c_void_p(stream)),
            "lf_probe_read")
+
+
+def lf_probe_read_grid(src: int, nbytes: int, n_blocks: int, sink: int, stream: int = 0) -> None:
+    _check(load_library().lf_probe_read_grid(c_void_p(src), c_size_t(nbytes), c_int32(n_blocks), c_void_p(sink),
+                                             c_void_p(stream)), "lf_probe_read_grid")
 
 
 def lf_probe_empty(n_blocks: int, stream: int = 0) -> None:

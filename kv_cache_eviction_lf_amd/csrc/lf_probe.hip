@@ -55,17 +55,33 @@ __global__ __launch_bounds__(kProbeThreads) void probe_read_kernel(const uint4* 
                                                                     uint32_t* __restrict__ sink) {
   size_t lo, hi;
   slice(n, lo, hi);
+  // A ring of kReadUnroll loads per lane kept in flight the whole time: each
+  // element is consumed and its register refilled with the element
+  // kReadUnroll rounds ahead, so a slice that is not a multiple of a round
+  // costs its remainder, not one more memory round trip.  The trip count is
+  // the same for every lane of the workgroup; lanes past the slice load its
+  // last element and do not use it.
   uint32_t x = 0;
-  for (size_t i = lo + threadIdx.x; i < hi; i += (size_t)kProbeThreads * kReadUnroll) {
+  if (lo < hi) {
+    const size_t rounds = (hi - lo + kProbeThreads - 1) / kProbeThreads;  // elements per lane, rounded up
+    const size_t last = hi - 1;
+    auto at = [&](size_t m) { return lo + threadIdx.x + m * kProbeThreads; };
     uint4 v[kReadUnroll];
 #pragma unroll
-    for (int k = 0; k < kReadUnroll; ++k) {
-      const size_t j = i + (size_t)k * kProbeThreads;
-      v[k] = load_nt(src + (j < hi ? j : hi - 1));
+    for (int k = 0; k < kReadUnroll; ++k) v[k] = load_nt(src + (at(k) < hi ? at(k) : last));
+    size_t m = 0;
+    for (; m + kReadUnroll < rounds; m += kReadUnroll) {
+#pragma unroll
+      for (int k = 0; k < kReadUnroll; ++k) {
+        if (at(m + k) < hi) x ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
+        const size_t j = at(m + k + kReadUnroll);
+        v[k] = load_nt(src + (j < hi ? j : last));
+        __builtin_amdgcn_sched_barrier(0);  // keep each refill right after its use
+      }
     }
 #pragma unroll
     for (int k = 0; k < kReadUnroll; ++k)
-      if (i + (size_t)k * kProbeThreads < hi) x ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
+      if (at(m + k) < hi) x ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) x ^= __shfl_xor(x, off);
@@ -101,6 +117,14 @@ lf_status lf_probe_read(const void* src, size_t bytes, uint32_t* sink, void* str
   if (!bytes) return LF_OK;
   hipLaunchKernelGGL(probe_read_kernel, dim3(kReadBlocks), dim3(kProbeThreads), 0,
                      static_cast<hipStream_t>(stream), static_cast<const uint4*>(src), bytes / 16, sink);
+  return hipGetLastError() == hipSuccess ? LF_OK : LF_ERR_HIP;
+}
+
+lf_status lf_probe_read_grid(const void* src, size_t bytes, int32_t n_blocks, uint32_t* sink, void* stream) {
+  if (bad(src) || !sink || bytes % 16 || n_blocks < 1 || n_blocks > kReadBlocks) return LF_ERR_ARG;
+  if (!bytes) return LF_OK;
+  hipLaunchKernelGGL(probe_read_kernel, dim3(n_blocks), dim3(kProbeThreads), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint4*>(src), bytes / 16, sink);
   return hipGetLastError() == hipSuccess ? LF_OK : LF_ERR_HIP;
 }
 

@@ -4,6 +4,7 @@ No call here reaches a kernel or the HIP runtime."""
 from __future__ import annotations
 
 import ctypes
+from ctypes import c_int32, c_size_t, c_void_p
 import os
 import re
 import subprocess
@@ -210,3 +211,12 @@ def test_layer_steps_reject_bad_handles_without_launching():
     with pytest.raises(LFError) as ei:
         _lib.lf_decode_step_layer_dbg(1, 1, 1, ctypes.addressof(fake), 0, 1, 1)
     assert ei.value.status == LF_ERR_STATE
+
+
+def test_probe_read_grid_rejects_bad_grids_before_launching():
+    # 16-byte aligned stand-in pointers: the argument checks return before any
+    # device call, so this runs without a GPU.
+    lib = _lib.load_library()
+    for grid in (0, -1, lib.lf_probe_read_sink_words() + 1):
+        assert lib.lf_probe_read_grid(c_void_p(4096), c_size_t(64), c_int32(grid), c_void_p(4096), None) == LF_ERR_ARG
+    assert lib.lf_probe_read_grid(c_void_p(4096), c_size_t(8), c_int32(1), c_void_p(4096), None) == LF_ERR_ARG

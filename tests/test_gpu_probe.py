@@ -41,3 +41,22 @@ def test_probe_empty_launch():
     torch.cuda.synchronize()
     with pytest.raises(_lib.LFError):
         _lib.lf_probe_empty(0, stream)
+
+
+@pytest.mark.parametrize("grid", [1, 256, 2048])
+def test_probe_read_grid(grid):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    nbytes = (1 << 20) + 32
+    g = torch.Generator().manual_seed(grid)
+    host = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, generator=g)
+    src = host.cuda()
+    sink = torch.zeros(grid, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    _lib.lf_probe_read_grid(src.data_ptr(), nbytes, grid, sink.data_ptr(), stream)
+    torch.cuda.synchronize()
+    want = np.bitwise_xor.reduce(host.numpy().view(np.uint32))
+    assert np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32)) == want
+    for bad in (0, _lib.lf_probe_read_sink_words() + 1):
+        with pytest.raises(_lib.LFError):
+            _lib.lf_probe_read_grid(src.data_ptr(), nbytes, bad, sink.data_ptr(), stream)
