@@ -318,12 +318,17 @@ lf_status prefill_impl(const lf_config* cfg, const int32_t* budgets, const int32
   char* w = static_cast<char*>(work);
   float* stats = reinterpret_cast<float*>(w + align_up(sizeof(float) * pairs * (size_t)max_prefill));
   int32_t* dlen = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(stats) + align_up(sizeof(float) * pairs * nck * 16));
-  float* logits = reinterpret_cast<float*>(reinterpret_cast<char*>(dlen) + align_up(sizeof(int32_t) * 2 * cfg->batch));
-  std::vector<int32_t> host(2 * cfg->batch);
+  float* logits = reinterpret_cast<float*>(reinterpret_cast<char*>(dlen) + align_up(sizeof(int32_t) * 3 * cfg->batch));
+  // prefill lengths, budgets, and the sequences by decreasing prefill length
+  // (the selection pass starts its longest pairs first)
+  std::vector<int32_t> host(3 * cfg->batch);
   for (int b = 0; b < cfg->batch; ++b) {
     host[b] = prefill[b];
     host[cfg->batch + b] = bud[b];
+    host[2 * cfg->batch + b] = b;
   }
+  std::stable_sort(host.begin() + 2 * cfg->batch, host.end(),
+                   [&](int32_t x, int32_t y) { return prefill[x] > prefill[y]; });
   char err[256];
   if (lf::upload_and_wait(dlen, host.data(), sizeof(int32_t) * host.size(), stream, err, sizeof(err)))
     return fail(LF_ERR_HIP, "%s", err);
@@ -341,6 +346,7 @@ lf_status prefill_impl(const lf_config* cfg, const int32_t* budgets, const int32
   a.n_copy = (cfg->max_budget + lf::kPrefillCopyRows - 1) / lf::kPrefillCopyRows;
   a.prefill = dlen;
   a.budget = dlen + cfg->batch;
+  a.order = dlen + 2 * cfg->batch;
   a.n_kv_heads = cfg->n_kv_heads;
   a.n_q_heads = cfg->n_q_heads;
   a.group = cfg->n_q_heads / cfg->n_kv_heads;
@@ -726,7 +732,7 @@ lf_status lf_prefill_work_bytes(const lf_config* cfg, int32_t max_prefill, size_
   const size_t nck = (max_prefill + lf::kPrefillChunk - 1) / lf::kPrefillChunk;
   const size_t group = cfg->n_q_heads / cfg->n_kv_heads;
   *bytes = align_up(sizeof(float) * pairs * (size_t)max_prefill) + align_up(sizeof(float) * pairs * nck * 16) +
-           align_up(sizeof(int32_t) * 2 * cfg->batch) + align_up(sizeof(float) * pairs * (size_t)max_prefill * group);
+           align_up(sizeof(int32_t) * 3 * cfg->batch) + align_up(sizeof(float) * pairs * (size_t)max_prefill * group);
   g_err[0] = 0;
   return LF_OK;
 }

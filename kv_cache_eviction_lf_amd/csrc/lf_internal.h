@@ -130,6 +130,7 @@ struct PrefillArgs {
   float* logits;       // [pairs][group][max_prefill]: log2-domain logits of the last query
   const int32_t* prefill;  // device [B]
   const int32_t* budget;   // device [B]
+  const int32_t* order;    // device [B]: sequences by decreasing prefill length
   int32_t n_chunks;    // score chunks per pair (max_prefill / 512, rounded up)
   int32_t n_copy;      // copy workgroups per pair (max_budget / 256, rounded up)
   int32_t n_kv_heads;

@@ -13,14 +13,18 @@
 //   prefill_stats_kernel       a workgroup per (pair, 512-row chunk): the
 //                              chunk's logits (stored head-major, [G][position])
 //                              and their per-head maximum and normaliser.
-//   prefill_select_kernel      a workgroup per pair: the pair's statistics
+//   prefill_select_kernel      a workgroup per pair, the pairs of the longest
+//                              prefills first: the pair's statistics
 //                              combined in chunk order, every position's
 //                              importance from its stored logits (no second
-//                              pass over K), then radix selection of the
-//                              threshold over 48-bit keys (importance, then the
-//                              complement of the position, so keys are unique
-//                              and the lower position ranks first on equal
-//                              importance) and position-ordered compaction.
+//                              pass over K; kept in LDS for prefills up to
+//                              kSelLdsMax positions), then radix selection of
+//                              the threshold over 48-bit keys (importance, then
+//                              the complement of the position, so keys are
+//                              unique and the lower position ranks first on
+//                              equal importance; passes stop once the bin at
+//                              the threshold is wanted whole) and
+//                              position-ordered compaction.
 //   prefill_copy_kernel        a workgroup per (pair, 256 kept rows): the
 //                              kept K/V rows copied in order.
 #include <hip/hip_runtime.h>
@@ -106,6 +110,11 @@ __device__ __forceinline__ void ml_merge(float& m, float& l, float m2, float l2)
 // batches still fill the device.
 constexpr int kChunkRows = kPrefillChunk;
 constexpr int kSel = 8;  // positions per thread whose loads the selection pass issues together
+// Longest prefill whose importances the selection pass keeps in LDS (60 KB
+// of the 64 KB a workgroup may hold, beside the histogram, scan and chunk
+// statistics arrays); longer prefills are selected from the copy in global
+// memory.
+constexpr int kSelLdsMax = 15360;
 
 template <class E, int D, int G>
 struct ScoreCore {
@@ -346,52 +355,78 @@ __device__ __forceinline__ uint64_t rank_key(float x, int pos) {
   return (static_cast<uint64_t>(__float_as_uint(fmaxf(x, 0.f))) << 16) | (0xFFFFu - static_cast<uint32_t>(pos));
 }
 
-template <int G>
+template <int G, bool kLds>
 __global__ __launch_bounds__(kPT) void prefill_select_kernel(PrefillArgs a) {
-  const int pair = blockIdx.x;
-  const int b = pair / a.n_kv_heads;
+  extern __shared__ float s_dyn[];  // kLds: the pair's importances, a.max_prefill floats
+  // Workgroups take the pairs of the longest prefills first, so the longest
+  // selections do not start in a late round of the grid.
+  const int rank = blockIdx.x / a.n_kv_heads;
+  const int b = a.order[rank];
+  const int pair = b * a.n_kv_heads + (blockIdx.x - rank * a.n_kv_heads);
   const int P = a.prefill[b], budget = a.budget[b];
   const int sink = a.sink, R = a.recent;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  float* imp = a.work + (size_t)pair * a.max_prefill;
+  float* imp_out = a.work + (size_t)pair * a.max_prefill;  // the call's importance output
+  const float* imp = kLds ? s_dyn : imp_out;               // what the selection reads
   int32_t* kept = a.kept + (size_t)pair * a.max_budget;
   const int nkeep = min(P, budget);
   __shared__ uint32_t s_hist[256];
-  __shared__ uint32_t s_digit, s_want;
+  __shared__ uint32_t s_digit, s_want, s_done;
   __shared__ uint32_t s_scan[kPT];
 
   // The pair's statistics combined in chunk order, then every position's
-  // importance from its stored logits (written out: the call's importance
-  // output, read back by the selection below from L2).
+  // importance from its stored logits (written out as the call's importance
+  // output and, with kLds, kept in LDS for the selection below; without it
+  // the selection reads the output back).
   {
+    // The chunks' (max, sum) of the G heads are loaded together into LDS (one
+    // memory round trip instead of one per chunk), merged in chunk order by
+    // thread h for head h, and read back by every thread.
+    constexpr int kMaxChunksSel = (kLds ? kSelLdsMax : kMaxPrefill) / kChunkRows;
+    __shared__ float s_st[kMaxChunksSel * G * 2];
+    __shared__ float s_mi[2 * G];
     const int nck = (P + kChunkRows - 1) / kChunkRows;
-    float M[G], invL[G];
     const float* st = a.stats + (size_t)pair * a.n_chunks * kMaxG * 2;
+    for (int i = tid; i < nck * G * 2; i += kPT) {
+      const int k = i / (2 * G), r = i - k * 2 * G;
+      s_st[i] = st[k * kMaxG * 2 + r];
+    }
+    __syncthreads();
+    if (tid < G) {
+      float mm = -INFINITY, ll = 0.f;
+      for (int k = 0; k < nck; ++k) ml_merge(mm, ll, s_st[k * 2 * G + 2 * tid], s_st[k * 2 * G + 2 * tid + 1]);
+      s_mi[tid] = mm;
+      s_mi[G + tid] = 1.0f / ll;
+    }
+    __syncthreads();
+    float M[G], invL[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float mm = -INFINITY, ll = 0.f;
-      for (int k = 0; k < nck; ++k) ml_merge(mm, ll, st[k * kMaxG * 2 + 2 * h], st[k * kMaxG * 2 + 2 * h + 1]);
-      M[h] = mm;
-      invL[h] = 1.0f / ll;
+      M[h] = s_mi[h];
+      invL[h] = s_mi[G + h];
     }
     // kSel positions per thread and pass, their logits loaded before any
     // store (the compiler cannot move a load above a store it cannot tell
     // apart), so a pass costs one memory round trip rather than kSel.
     const float* lg = a.logits + (size_t)pair * a.max_prefill * G;
-    for (int i0 = tid; i0 < P; i0 += kSel * kPT) {
-      float x[kSel][G];
+    constexpr int kImp = kLds ? 2 * kSel : kSel;  // positions per round trip (registers allow more with kLds)
+    for (int i0 = tid; i0 < P; i0 += kImp * kPT) {
+      float x[kImp][G];
 #pragma unroll
-      for (int u = 0; u < kSel; ++u) {
+      for (int u = 0; u < kImp; ++u) {
         const int i = min(i0 + u * kPT, P - 1);
 #pragma unroll
         for (int h = 0; h < G; ++h) x[u][h] = lg[(size_t)h * a.max_prefill + i];
       }
 #pragma unroll
-      for (int u = 0; u < kSel; ++u) {
+      for (int u = 0; u < kImp; ++u) {
         float y = 0.f;
 #pragma unroll
         for (int h = 0; h < G; ++h) y = fmaf(__builtin_amdgcn_exp2f(x[u][h] - M[h]), invL[h], y);
-        if (i0 + u * kPT < P) imp[i0 + u * kPT] = y;
+        if (i0 + u * kPT < P) {
+          imp_out[i0 + u * kPT] = y;
+          if constexpr (kLds) s_dyn[i0 + u * kPT] = y;
+        }
       }
     }
     __syncthreads();  // every position's importance written (same workgroup)
@@ -401,7 +436,10 @@ __global__ __launch_bounds__(kPT) void prefill_select_kernel(PrefillArgs a) {
   if (P > budget) {
     const int lo = sink, hi = P - R;
     uint64_t prefix = 0, mask = 0;
-    if (tid == 0) s_want = budget - sink - R;
+    if (tid == 0) {
+      s_want = budget - sink - R;
+      s_done = 0u;
+    }
     for (int pass = 0; pass < 6; ++pass) {
       const int shift = 40 - 8 * pass;
       for (int i = tid; i < 256; i += kPT) s_hist[i] = 0u;
@@ -414,7 +452,18 @@ __global__ __launch_bounds__(kPT) void prefill_select_kernel(PrefillArgs a) {
         for (int u = 0; u < kSel; ++u) {
           const int i = i0 + u * kPT;
           const uint64_t key = rank_key(v[u], i);
-          if (i < hi && (key & mask) == prefix) atomicAdd(&s_hist[(key >> shift) & 255u], 1u);
+          const bool in = i < hi && (key & mask) == prefix;
+          const uint32_t bin = static_cast<uint32_t>(key >> shift) & 255u;
+          // Importances of one pair often share their leading bits, so most
+          // lanes of a wave hit one bin: the bin of the wave's first counted
+          // lane is added once for every lane holding it, the others singly.
+          const uint64_t act = __builtin_amdgcn_ballot_w64(in);
+          if (act) {
+            const uint32_t lead = __builtin_amdgcn_readlane(bin, __builtin_ctzll(act));
+            const uint64_t same = __builtin_amdgcn_ballot_w64(in && bin == lead);
+            if (lane == __builtin_ctzll(act)) atomicAdd(&s_hist[lead], static_cast<uint32_t>(__builtin_popcountll(same)));
+            if (in && bin != lead) atomicAdd(&s_hist[bin], 1u);
+          }
         }
       }
       __syncthreads();
@@ -442,6 +491,9 @@ __global__ __launch_bounds__(kPT) void prefill_select_kernel(PrefillArgs a) {
             if (before < want && before + cnt[k] >= want) {
               s_digit = 255 - 4 * lane - k;
               s_want = want - before;
+              // the whole bin is wanted: every key at or above the bin's
+              // smallest key is kept, the lower bits need no further pass
+              s_done = before + cnt[k] == want ? 1u : 0u;
               before = want;  // found: no later digit qualifies
             } else {
               before += cnt[k];
@@ -452,7 +504,9 @@ __global__ __launch_bounds__(kPT) void prefill_select_kernel(PrefillArgs a) {
       __syncthreads();
       prefix |= static_cast<uint64_t>(s_digit) << shift;
       mask |= 0xFFull << shift;
-      __syncthreads();  // s_digit / s_want are rewritten next pass
+      const bool done = s_done != 0u;
+      __syncthreads();  // s_digit / s_want / s_done are rewritten next pass
+      if (done) break;
     }
     thr = prefix;  // keys are unique: exactly budget - sink - R middle keys are >= it
   }
@@ -518,7 +572,7 @@ __global__ __launch_bounds__(kPT) void prefill_copy_kernel(PrefillArgs a) {
   // non-temporal.
   const int n = r1 - r0;
   if (n <= 0) return;
-  constexpr int kU = 8;
+  constexpr int kU = 16;
   constexpr int kStep = kPW * kRowsPerWave * kU;  // rows per pass of the workgroup
   constexpr int kPasses = (kCopyRows + kStep - 1) / kStep;
   int pos[kPasses][kU];
@@ -555,7 +609,11 @@ void launch_scores(const PrefillArgs& a, int n_pairs, hipStream_t s) {
     hipLaunchKernelGGL((prefill_stats_mfma_kernel<D, G>), dim3(n_pairs * a.n_chunks), dim3(kPT), 0, s, a);
   else
     hipLaunchKernelGGL((prefill_stats_kernel<E, D, G>), dim3(n_pairs * a.n_chunks), dim3(kPT), 0, s, a);
-  hipLaunchKernelGGL((prefill_select_kernel<G>), dim3(n_pairs), dim3(kPT), 0, s, a);
+  if (a.max_prefill <= kSelLdsMax)
+    hipLaunchKernelGGL((prefill_select_kernel<G, true>), dim3(n_pairs), dim3(kPT), sizeof(float) * a.max_prefill, s,
+                       a);
+  else
+    hipLaunchKernelGGL((prefill_select_kernel<G, false>), dim3(n_pairs), dim3(kPT), 0, s, a);
 }
 
 template <class E, int D>

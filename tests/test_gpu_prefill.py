@@ -33,6 +33,9 @@ CASES = [
     # largest budgets with prefills up to twice the budget, so the decode leg
     # starts from the method's own compression at full size (split pairs).
     _case("pf_ragged_shape", 3, 40, 8, 128, "bf16", [1024, 4096, 8192], [2048, 4100, 16384], 4, 64, 16384, 25),
+    # The same shape with every prefill short enough for the selection to keep
+    # the importances on chip (the ragged batch's longest prefill is 14801).
+    _case("pf_ragged_lds", 2, 40, 8, 128, "bf16", [4096, 7168], [8000, 15000], 4, 64, 15360, 26),
 ]
 
 
@@ -103,3 +106,32 @@ def test_prefill_compress_matches_oracle(case):
                     slots[b, g] = ev_h[b, g]
         oc.commit(slots, ks, vs)
     cache.close()
+
+
+@pytest.mark.parametrize("max_prefill", [4096, 16384], ids=["lds", "global"])
+def test_prefill_equal_importances_keep_the_lowest_positions(max_prefill):
+    # Every prefill key of a pair equal: every middle position has the same
+    # importance, so the selection runs through its position bits and keeps
+    # the lowest middle positions (lower position first on equal importance).
+    from kv_cache_eviction_lf_amd import compress_prefill
+
+    B, Hq, Hkv, d, sink, recent = 2, 8, 2, 128, 4, 16
+    bud, pre = [300, 1000], [3000, max_prefill - 5]
+    print(f"[prefill] equal keys: max_prefill={max_prefill} budgets={bud} prefill={pre}", flush=True)
+    rng = np.random.default_rng(31)
+    dev = torch.device("cuda:0")
+    q = torch.from_numpy(rng.standard_normal((B, Hq, d)).astype(np.float32)).to(dev, torch.bfloat16)
+    row = torch.from_numpy(rng.standard_normal((B, Hkv, 1, d)).astype(np.float32)).to(dev, torch.bfloat16)
+    k = row.expand(B, Hkv, max_prefill, d).contiguous()
+    v = torch.from_numpy(rng.standard_normal((B, Hkv, max_prefill, d)).astype(np.float32)).to(dev, torch.bfloat16)
+    kc, vc, kept, imp = compress_prefill(q, k, v, pre, max(bud), sink, recent, budgets=bud)
+    torch.cuda.synchronize()
+    kept_h, imp_h = kept.cpu().numpy(), imp.cpu().numpy()
+    v_h = v.float().cpu().numpy()
+    for b in range(B):
+        P, nb = pre[b], bud[b]
+        want = np.array(list(range(nb - recent)) + list(range(P - recent, P)))
+        for g in range(Hkv):
+            assert np.all(imp_h[b, g, :P] == imp_h[b, g, 0]), (b, g)
+            assert np.array_equal(kept_h[b, g, :nb], want), (b, g, kept_h[b, g, :8], kept_h[b, g, nb - recent - 4:nb])
+            assert np.array_equal(vc[b, g, :nb].float().cpu().numpy(), v_h[b, g, want]), (b, g)
