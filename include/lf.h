@@ -310,7 +310,8 @@ lf_status lf_prefill_work_bytes(const lf_config* cfg, int32_t max_prefill, size_
  *   work         device scratch of work_bytes >= lf_prefill_work_bytes(); on
  *                return it holds the importance [B][Hkv][max_prefill] (float).
  * All device pointers 16-byte aligned; k_pre/v_pre must not overlap k_cache/v_cache.
- * Asynchronous on `stream` after a small synchronous upload of the lengths.
+ * Asynchronous on `stream`; batches of more than 128 sequences first upload
+ * their lengths with a small copy that waits for the stream.
  * Errors: LF_ERR_ARG, LF_ERR_UNSUPPORTED, LF_ERR_HIP.
  */
 lf_status lf_prefill_compress(const lf_config* cfg, const int32_t* budgets, const int32_t* prefill,

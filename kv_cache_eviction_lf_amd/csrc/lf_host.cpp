@@ -330,9 +330,13 @@ lf_status prefill_impl(const lf_config* cfg, const int32_t* budgets, const int32
   std::stable_sort(host.begin() + 2 * cfg->batch, host.end(),
                    [&](int32_t x, int32_t y) { return prefill[x] > prefill[y]; });
   char err[256];
-  if (lf::upload_and_wait(dlen, host.data(), sizeof(int32_t) * host.size(), stream, err, sizeof(err)))
-    return fail(LF_ERR_HIP, "%s", err);
   lf::PrefillArgs a{};
+  if (cfg->batch <= lf::kPrefillArgBatch) {
+    a.n_inline = cfg->batch;
+    std::copy(host.begin(), host.end(), a.lens);
+  } else if (lf::upload_and_wait(dlen, host.data(), sizeof(int32_t) * host.size(), stream, err, sizeof(err))) {
+    return fail(LF_ERR_HIP, "%s", err);
+  }
   a.q_last = q_last;
   a.k_pre = k_pre;
   a.v_pre = v_pre;

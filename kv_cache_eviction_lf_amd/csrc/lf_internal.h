@@ -19,6 +19,7 @@ constexpr int kTargetItems = 256;   // split pairs into chunks until about this 
 constexpr int kMaxPrefill = 65536;  // prefill compression: positions fit 16 bits of the selection key
 constexpr int kPrefillChunk = 512;  // rows per workgroup of the prefill score passes
 constexpr int kPrefillCopyRows = 256;  // kept rows per workgroup of the prefill copy
+constexpr int kPrefillArgBatch = 128;  // prefill compression: largest batch whose lengths travel as kernel arguments
 // Static device scratch of lf_prefill_compress_noalloc (one copy per GPU).
 constexpr size_t kPrefillScratchBytes = size_t(64) << 20;
 constexpr int kMaxDevices = 64;
@@ -128,7 +129,7 @@ struct PrefillArgs {
   float* work;         // [pairs][max_prefill]
   float* stats;        // [pairs][n_chunks][8][2]: per-chunk (max, sum) per head
   float* logits;       // [pairs][group][max_prefill]: log2-domain logits of the last query
-  const int32_t* prefill;  // device [B]
+  const int32_t* prefill;  // device [B] (batches above kPrefillArgBatch)
   const int32_t* budget;   // device [B]
   const int32_t* order;    // device [B]: sequences by decreasing prefill length
   int32_t n_chunks;    // score chunks per pair (max_prefill / 512, rounded up)
@@ -141,6 +142,11 @@ struct PrefillArgs {
   int32_t sink;
   int32_t recent;
   float scale_log2;
+  // Batches of up to kPrefillArgBatch sequences carry their prefill lengths,
+  // budgets and order in the kernel arguments (no upload, no wait: the call is
+  // then fully asynchronous); larger batches use the device arrays above.
+  int32_t n_inline;  // B when the lengths are inline, else 0
+  int32_t lens[3 * kPrefillArgBatch];
 };
 
 // Kernel launch and runtime helpers, implemented in lf_kernel.hip (step) and

@@ -106,6 +106,17 @@ __device__ __forceinline__ void ml_merge(float& m, float& l, float m2, float l2)
   m = mn;
 }
 
+// Per-sequence prefill length, budget and the sequence of rank r in order of
+// decreasing prefill length: from the kernel arguments for small batches,
+// else from the device arrays the host uploaded.
+__device__ __forceinline__ int prefill_of(const PrefillArgs& a, int b) { return a.n_inline ? a.lens[b] : a.prefill[b]; }
+__device__ __forceinline__ int budget_of(const PrefillArgs& a, int b) {
+  return a.n_inline ? a.lens[a.n_inline + b] : a.budget[b];
+}
+__device__ __forceinline__ int seq_of_rank(const PrefillArgs& a, int r) {
+  return a.n_inline ? a.lens[2 * a.n_inline + r] : a.order[r];
+}
+
 // Rows of one chunk of the score passes: pairs are split so that short
 // batches still fill the device.
 constexpr int kChunkRows = kPrefillChunk;
@@ -175,7 +186,7 @@ template <class E, int D, int G>
 __global__ __launch_bounds__(kPT) void prefill_stats_kernel(PrefillArgs a) {
   const int pair = blockIdx.x / a.n_chunks, chunk = blockIdx.x - pair * a.n_chunks;
   const int b = pair / a.n_kv_heads;
-  const int P = a.prefill[b];
+  const int P = prefill_of(a, b);
   if (chunk * kChunkRows >= P) return;  // past this prefill (the grid covers the longest)
   const int r0 = chunk * kChunkRows, r1 = min(P, r0 + kChunkRows);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -243,7 +254,7 @@ __global__ __launch_bounds__(kPT) void prefill_stats_mfma_kernel(PrefillArgs a) 
   constexpr int NS = 4;                        // 16-row groups in flight per wave (current one included)
   const int pair = blockIdx.x / a.n_chunks, chunk = blockIdx.x - pair * a.n_chunks;
   const int b = pair / a.n_kv_heads, g = pair - b * a.n_kv_heads;
-  const int P = a.prefill[b];
+  const int P = prefill_of(a, b);
   if (chunk * kChunkRows >= P) return;  // past this prefill (the grid covers the longest)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, n = lane & 15, j = lane >> 4;
   const int r0 = chunk * kChunkRows + wave * kWaveRows;
@@ -361,9 +372,9 @@ __global__ __launch_bounds__(kPT) void prefill_select_kernel(PrefillArgs a) {
   // Workgroups take the pairs of the longest prefills first, so the longest
   // selections do not start in a late round of the grid.
   const int rank = blockIdx.x / a.n_kv_heads;
-  const int b = a.order[rank];
+  const int b = seq_of_rank(a, rank);
   const int pair = b * a.n_kv_heads + (blockIdx.x - rank * a.n_kv_heads);
-  const int P = a.prefill[b], budget = a.budget[b];
+  const int P = prefill_of(a, b), budget = budget_of(a, b);
   const int sink = a.sink, R = a.recent;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   float* imp_out = a.work + (size_t)pair * a.max_prefill;  // the call's importance output
@@ -555,7 +566,7 @@ __global__ __launch_bounds__(kPT) void prefill_copy_kernel(PrefillArgs a) {
   using elem = typename E::elem;
   const int pair = blockIdx.x / a.n_copy, part = blockIdx.x - pair * a.n_copy;
   const int b = pair / a.n_kv_heads;
-  const int P = a.prefill[b], nkeep = min(P, a.budget[b]);
+  const int P = prefill_of(a, b), nkeep = min(P, budget_of(a, b));
   const int r0 = part * kCopyRows, r1 = min(nkeep, r0 + kCopyRows);
   const int32_t* kept = a.kept + (size_t)pair * a.max_budget;
   constexpr int kPieces = D * sizeof(elem) / 16;

@@ -135,3 +135,57 @@ def test_prefill_equal_importances_keep_the_lowest_positions(max_prefill):
             assert np.all(imp_h[b, g, :P] == imp_h[b, g, 0]), (b, g)
             assert np.array_equal(kept_h[b, g, :nb], want), (b, g, kept_h[b, g, :8], kept_h[b, g, nb - recent - 4:nb])
             assert np.array_equal(vc[b, g, :nb].float().cpu().numpy(), v_h[b, g, want]), (b, g)
+
+
+def _large_batch_case():
+    # More sequences than travel in the kernel arguments: the lengths, budgets
+    # and order are uploaded to the device instead.
+    B = 130
+    bud = [48 + 8 * (i % 5) for i in range(B)]
+    pre = [b + (7 * i) % (b + 1) for i, b in enumerate(bud)]
+    return _case("pf_large_batch", B, 4, 1, 64, "bf16", bud, pre, 2, 8, max(pre), 27)
+
+
+@pytest.mark.parametrize("case", [_large_batch_case()], ids=["pf_large_batch"])
+def test_prefill_compress_large_batch(case):
+    test_prefill_compress_matches_oracle(case)
+
+
+def test_prefill_compress_in_a_graph():
+    # Batches that fit the kernel arguments make only kernel launches: the call
+    # can be captured in a HIP graph; every replay (with eager work and
+    # synchronisations between them) must reproduce the eager result.
+    from kv_cache_eviction_lf_amd import _lib
+
+    w, bud, pre, max_prefill = CASES[0]
+    print(f"[prefill] graph capture: {w.name} budgets={bud} prefill={pre}", flush=True)
+    dev = torch.device("cuda:0")
+    q, k, v = (torch.from_numpy(x).to(dev, torch.bfloat16) for x in prefill_inputs(w, max_prefill))
+    max_budget = max(bud)
+    cfg = _lib.make_config(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, max_budget, w.sink, w.recent, _lib.LF_BF16)
+    wb = _lib.lf_prefill_work_bytes(cfg, max_prefill)
+    work = torch.zeros(wb, dtype=torch.uint8, device=dev)
+    shape = (w.batch, w.n_kv_heads, max_budget, w.head_dim)
+    kc, vc = torch.zeros(shape, dtype=torch.bfloat16, device=dev), torch.zeros(shape, dtype=torch.bfloat16, device=dev)
+    kept = torch.full((w.batch, w.n_kv_heads, max_budget), -1, dtype=torch.int32, device=dev)
+
+    def call(stream):
+        _lib.lf_prefill_compress(cfg, bud, pre, max_prefill, q.data_ptr(), k.data_ptr(), v.data_ptr(), kc.data_ptr(),
+                                 vc.data_ptr(), kept.data_ptr(), work.data_ptr(), wb, stream)
+
+    call(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    want = (kc.clone(), vc.clone(), kept.clone())
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=side):
+        call(torch.cuda.current_stream().cuda_stream)
+    for rep in range(3):
+        kc.zero_()
+        vc.zero_()
+        kept.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, exp, name in zip((kc, vc, kept), want, ("k_cache", "v_cache", "kept")):
+            assert torch.equal(got, exp), f"replay {rep}: {name} differs from the eager call"
