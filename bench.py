@@ -66,7 +66,8 @@ def fast_caches(w, bud, L, dev, torch):
     """L layer caches of workload w for timing only: K/V drawn N(0,1) on the
     device (the key outlier channels scaled), filled to each sequence's
     prefill length or budget, instead of the seeded host recipe (whose values
-    only parity runs need)."""
+    only parity runs need); prefills longer than the budgets (the ragged
+    batch) are drawn at full length and compressed to the budgets."""
     from workloads import prefill_lengths
     from workloads.generate import outlier_channels
 
@@ -76,6 +77,23 @@ def fast_caches(w, bud, L, dev, torch):
     S = int(bud.max())
     seq_len = prefill_lengths(w)
     out = []
+    if w.prefill == "ragged":
+        # Prefills longer than the budgets, compressed down to them at start by
+        # the method's own one-shot compression (lf_prefill_compress): the
+        # caches hold the kept tokens of N(0,1) prefills in position order.
+        from kv_cache_eviction_lf_amd import compress_prefill
+
+        P = int(seq_len.max())
+        for _ in range(L):
+            q = torch.randn((w.batch, w.n_q_heads, w.head_dim), generator=gen, device=dev).to(dt)
+            k_pre = torch.randn((w.batch, w.n_kv_heads, P, w.head_dim), generator=gen, device=dev).to(dt)
+            v_pre = torch.randn((w.batch, w.n_kv_heads, P, w.head_dim), generator=gen, device=dev).to(dt)
+            K, V, _, _ = compress_prefill(q, k_pre, v_pre, [int(x) for x in seq_len], S, w.sink, w.recent,
+                                          budgets=[int(x) for x in bud])
+            del k_pre, v_pre
+            out.append((K, V, seq_len))
+        torch.cuda.synchronize()
+        return out
     for _ in range(L):
         K = torch.randn((w.batch, w.n_kv_heads, S, w.head_dim), generator=gen, device=dev)
         if ch.numel():
@@ -226,9 +244,10 @@ def time_steps(args, w, bud, steps, warmup, torch, dev, lib, fast=False):
     # L independent layer caches (distinct seeds) and fresh inputs for every
     # step (a repeated input would fill the caches with copies of its tokens).
     caches = []
-    if fast:
+    if fast or w.prefill == "ragged":
         for K, V, seq_len in fast_caches(w, bud, L, dev, torch):
-            caches.append(LongFlowCache(K, V, w.n_q_heads, w.sink, w.recent, seq_len, budgets=bud))
+            caches.append(LongFlowCache(K, V, w.n_q_heads, w.sink, w.recent, seq_len, budgets=bud,
+                                        score=args.score, chunk_slots=args.chunk))
     else:
         for layer in range(L):
             wl = w.with_(seed=w.seed + 7919 * layer)
@@ -350,6 +369,8 @@ def main():
             others[name] = {"ms_per_step": round(mo, 6), "steps_per_s": round(1e3 / mo, 1), "kv_GBps": round(gb, 1),
                             "frac": round(gb / HBM_PEAK_GBPS, 4), "steps": args.other_steps, "layer_caches": Lo,
                             "bytes_per_launch": bo_bytes}
+            if wo.prefill == "ragged":
+                others[name]["initial_cache"] = "full-length prefills compressed to the budgets by lf_prefill_compress"
 
     cur = torch.cuda.current_stream()
     probe = None
@@ -465,6 +486,8 @@ def main():
             "layer_caches": L,
             "launch": "eager" if args.eager else "hip-graph",
             "chunk_slots": chunk_slots,
+            **({"initial_cache": "full-length prefills compressed to the budgets by lf_prefill_compress"}
+               if w.prefill == "ragged" else {}),
         },
         "kv_GBps": round(achieved, 1),
         "pct_hbm_peak": round(100 * achieved / HBM_PEAK_GBPS, 2),
