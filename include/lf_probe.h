@@ -29,7 +29,7 @@ lf_status lf_probe_copy(const void* src, void* dst, size_t bytes, void* stream);
 lf_status lf_probe_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
 int32_t lf_probe_read_sink_words(void);
 
-/* lf_probe_read over a grid of `n_blocks` workgroups (1 ... 
+/* lf_probe_read over a grid of `n_blocks` workgroups (1 to
  * lf_probe_read_sink_words()) instead of the default: below a few hundred MB
  * per launch the fastest grid depends on the size (one workgroup per compute
  * unit reads 32-64 MB faster than the default grid), so a size-matched ceiling
